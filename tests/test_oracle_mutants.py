@@ -1,0 +1,165 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and show that
+at least one pin fails for each: the pins are strong enough to catch them."""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.gptq as og
+from oracle_pins import ALL_CHECKS
+
+
+def _namespace(**overrides):
+    ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in oracle.__all__})
+    for k, v in overrides.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def _columns_factory(sign=1.0, divide_by_ujj=True, scale_from_original=False, rounding=np.round,
+                     update_row_of_u=True):
+    def gptq_columns(W, U, bits, g):
+        W0 = np.array(W, dtype=np.float64)
+        Wc = W0.copy()
+        U = np.asarray(U, dtype=np.float64)
+        out, n = Wc.shape
+        q = og.qmax(bits)
+        ng = (n + g - 1) // g
+        codes = np.zeros((out, n), dtype=np.int64)
+        scales = np.zeros((out, ng))
+        err = np.zeros((out, n))
+        for grp in range(ng):
+            g0, g1 = grp * g, min(n, (grp + 1) * g)
+            src = W0 if scale_from_original else Wc
+            scale = np.max(np.abs(src[:, g0:g1]), axis=1) / q
+            scales[:, grp] = scale
+            for j in range(g0, g1):
+                c = np.zeros(out)
+                live = scale != 0
+                c[live] = rounding(Wc[live, j] / scale[live])
+                c = np.clip(c, -q - 1, q)
+                codes[:, j] = c
+                e = Wc[:, j] - c * scale
+                if divide_by_ujj:
+                    e = e / U[j, j]
+                err[:, j] = e
+                row = U[j, j + 1:] if update_row_of_u else U[j + 1:, j]
+                Wc[:, j + 1:] -= sign * e[:, None] * row[None, :]
+        return codes, scales, err
+    return gptq_columns
+
+
+def _layer_with(columns=None, factor=None, damped=None, perm=None):
+    def gptq_layer(W, H0, d=None, bits=4, g=128, damp=0.01, act_order=False, U=None):
+        saved = (og.gptq_columns, og.inverse_upper_factor, og.damped, og.act_order_permutation)
+        try:
+            if columns is not None:
+                og.gptq_columns = columns
+            if factor is not None:
+                og.inverse_upper_factor = factor
+            if damped is not None:
+                og.damped = damped
+            if perm is not None:
+                og.act_order_permutation = perm
+            return saved_layer(W, H0, d, bits, g, damp, act_order, U)
+        finally:
+            og.gptq_columns, og.inverse_upper_factor, og.damped, og.act_order_permutation = saved
+    return gptq_layer
+
+
+saved_layer = og.gptq_layer
+
+
+def _lower_factor(H):
+    return np.linalg.cholesky(np.linalg.inv(H))          # forgot the transpose
+
+
+def _no_damp(H0, damp):
+    return np.asarray(H0, dtype=np.float64).copy(), 0.0
+
+
+def _damp_sum(H0, damp):
+    H0 = np.asarray(H0, dtype=np.float64)
+    lam = damp * float(np.sum(np.diag(H0)))              # sum instead of mean
+    return H0 + lam * np.eye(H0.shape[0]), lam
+
+
+def _ascending(d):
+    return np.argsort(np.asarray(d), kind="stable")      # increasing instead of decreasing
+
+
+def _ties_reversed(d):
+    n = len(d)
+    return np.lexsort((-np.arange(n), -np.asarray(d, dtype=np.float64)))   # ties: higher index first
+
+
+def _hessian_no_mirror(X, chunk_rows=2048):
+    X = np.asarray(X, dtype=np.float64)
+    H0 = X.T @ X
+    d = np.sum(X * X, axis=0)
+    return H0 + np.triu(H0, 1) * 1e-3, d                 # asymmetric junk in the upper part
+
+
+def _rtn_floor(W, bits, g):
+    W = np.asarray(W, dtype=np.float64)
+    out, n = W.shape
+    q = og.qmax(bits)
+    ng = (n + g - 1) // g
+    codes = np.zeros((out, n), dtype=np.int64)
+    scales = np.zeros((out, ng))
+    for grp in range(ng):
+        g0, g1 = grp * g, min(n, (grp + 1) * g)
+        s = np.max(np.abs(W[:, g0:g1]), axis=1) / q
+        scales[:, grp] = s
+        with np.errstate(invalid="ignore", divide="ignore"):
+            c = np.where(s[:, None] != 0, np.trunc(W[:, g0:g1] / s[:, None]), 0)
+        codes[:, g0:g1] = np.clip(c, -q - 1, q)
+    return codes, scales
+
+
+def _awq_channels_reversed(X):
+    return np.mean(np.abs(np.asarray(X, dtype=np.float64)), axis=0)[::-1]
+
+
+def _awq_rms(X):
+    X = np.asarray(X, dtype=np.float64)
+    return np.sqrt(np.mean(X * X, axis=0))                # root-mean-square instead of mean |x|
+
+
+MUTANTS = {
+    "feedback sign flipped": dict(gptq_layer=_layer_with(columns=_columns_factory(sign=-1.0))),
+    "error not divided by U_jj": dict(gptq_layer=_layer_with(columns=_columns_factory(divide_by_ujj=False))),
+    "scale from original W": dict(gptq_layer=_layer_with(columns=_columns_factory(scale_from_original=True))),
+    "floor instead of round": dict(gptq_layer=_layer_with(columns=_columns_factory(rounding=np.floor))),
+    "column of U instead of row": dict(gptq_layer=_layer_with(columns=_columns_factory(update_row_of_u=False))),
+    "lower factor (no transpose)": dict(gptq_layer=_layer_with(factor=_lower_factor),
+                                        inverse_upper_factor=_lower_factor),
+    "damping dropped": dict(gptq_layer=_layer_with(damped=_no_damp), damped=_no_damp),
+    "damping by sum not mean": dict(gptq_layer=_layer_with(damped=_damp_sum), damped=_damp_sum),
+    "act-order ascending": dict(gptq_layer=_layer_with(perm=_ascending), act_order_permutation=_ascending),
+    "hessian not symmetric": dict(proxy_hessian=_hessian_no_mirror),
+    "rtn truncates": dict(rtn=_rtn_floor),
+    "act-order ties reversed": dict(gptq_layer=_layer_with(perm=_ties_reversed),
+                                    act_order_permutation=_ties_reversed),
+    "awq channels reversed": dict(channel_mean_abs=_awq_channels_reversed),
+    "awq rms instead of mean abs": dict(channel_mean_abs=_awq_rms),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    impl = _namespace(**MUTANTS[name])
+    failures = []
+    for check in ALL_CHECKS:
+        try:
+            check(impl)
+        except (AssertionError, np.linalg.LinAlgError, ValueError, FloatingPointError):
+            failures.append(check.__name__)
+    assert failures, f"no pin caught the planted mistake: {name}"
+
+
+def test_real_oracle_passes_every_pin():
+    impl = _namespace()
+    for check in ALL_CHECKS:
+        check(impl)
