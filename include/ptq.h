@@ -1,0 +1,195 @@
+/*
+ * ptq.h — C ABI of libptq.so: GPTQ / AWQ layer quantization on MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *  [OBJ]  "GPTQ versus AWQ objectives" (inferenceinterviews.com):
+ *         "A strong answer" (objective ||X W^T - X What^T||^2, proxy Hessian
+ *         X^T X, 1% mean-diagonal damping, upper Cholesky factor of H^-1, the
+ *         column loop, lazy batching over column blocks, Hessian sizing, AWQ's
+ *         s_j = mean|x_j|^alpha with a per-layer grid search over alpha);
+ *         "What interviewers probe next" (act-order, group index per column,
+ *         damping).
+ *  [PTQ]  "A Comprehensive Analysis of Post-Training Quantization Strategies
+ *         for Large Language Models: GPTQ, AWQ and GGUF" (uplatz.com),
+ *         sections 2.1-2.2 (layer-wise objective, group size, act-order) and
+ *         3.2 (AWQ's equivalent per-channel scaling).
+ *
+ * Conventions shared by every entry point:
+ *  - W is [out, in] row-major with row stride ldw (elements); X is [rows, in]
+ *    row-major with row stride ldx; H and U are [in, in] row-major, dense.
+ *  - Every array argument is a DEVICE pointer owned by the caller, unless
+ *    marked "host". The library allocates nothing: scratch memory comes from
+ *    the caller's workspace, whose size the matching *_workspace_bytes query
+ *    returns (256-byte aligned; NULL with size 0 is allowed where the query
+ *    returns 0).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *    Entry points that return host values (stats, alpha) synchronise that
+ *    stream before returning; the others are asynchronous.
+ *  - Arguments are validated before any HIP call; a bad argument returns
+ *    PTQ_EINVAL and touches no memory. ptq_last_error() then holds a
+ *    thread-local message naming the argument.
+ *  - Device pointers must be 16-byte aligned; ldw/ldx must keep every row
+ *    16-byte aligned.
+ *  - Integer codes are unpacked int8 in [-qmax-1, qmax], qmax = 2^(bits-1)-1.
+ *    Scales are fp32, one per (row, group); group k is the k-th run of g
+ *    columns in processing order, so scales[r][g_idx[c]] dequantizes column c.
+ */
+#ifndef PTQ_H
+#define PTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    PTQ_OK = 0,
+    PTQ_EINVAL = 1,       /* bad argument (nothing was launched)                  */
+    PTQ_ENOTPD = 2,       /* H + lambda I is not positive definite (a pivot <= 0) */
+    PTQ_ENONFINITE = 3,   /* NaN/Inf met in the inputs or a derived quantity       */
+    PTQ_EWORKSPACE = 4,   /* workspace NULL or smaller than the query's answer     */
+    PTQ_EHIP = 5          /* a HIP runtime call failed                             */
+};
+
+/* Element types of W and X. */
+enum { PTQ_BF16 = 0, PTQ_F32 = 1 };
+
+/* Thread-local message for the last non-OK status of this thread. */
+const char* ptq_last_error(void);
+/* Static name of a status code. */
+const char* ptq_status_string(int status);
+/* ABI version (incremented on any signature change). */
+int ptq_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing. With bit k of kernel_mask set, every later launch of kernel
+ * class k is bracketed by two hipEvents recorded on its launch stream:
+ *   0 X^T X bf16 MFMA tiles        1 fp32 GEMMs of the U recursion
+ *   2 diagonal-block factor/inverse 3 GPTQ in-block column loop
+ *   4 GPTQ trailing fp32 GEMM       5 AWQ error GEMM
+ * Enabling (any mask, 0 included) discards earlier records. ptq_profile_read
+ * waits for the recorded events of class `kernel` and returns the sum of
+ * their elapsed times (ms) and the number of launches. Process-wide; calls
+ * that overlap from several threads share the records.
+ * ---------------------------------------------------------------------- */
+int ptq_profile_enable(unsigned kernel_mask);
+int ptq_profile_read(int kernel, double* total_ms, int64_t* launches);
+
+/* ------------------------------------------------------------------------
+ * Stage 1 — proxy Hessian.  [OBJ] "A strong answer": H = X^T X over the
+ * calibration inputs (the page's 2 X^T X differs by a constant that the
+ * relative damping makes irrelevant).
+ *
+ * H[in, in] fp32 (+)= X^T X, accumulated on MFMA from bf16 (or fp32) X with
+ * fp32 accumulation; the result is written as a full symmetric matrix
+ * (H[i][j] and H[j][i] receive the same value). d[in] fp64 (+)= column sums
+ * of squares sum_i x_ij^2 (the act-order key and the damping base), which may
+ * be NULL. The call is additive: zero H and d before the first chunk, then
+ * call once per chunk of calibration rows (large chunks are faster: each call
+ * re-reads and re-writes H once). rows may be 0 (no-op).
+ * Workspace: hessian_workspace_bytes(in, rows) (0 is always acceptable; more
+ * lets small `in` use split-K partial sums for parallelism).
+ * Errors: EINVAL (in < 1, rows < 0, ldx < in, bad dtype, NULL H or X with
+ * rows > 0, misalignment), EHIP.
+ * ---------------------------------------------------------------------- */
+size_t hessian_workspace_bytes(int64_t in, int64_t rows);
+int hessian_accumulate(float* H, double* d, int64_t in,
+                       const void* X, int x_dtype, int64_t rows, int64_t ldx,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 2 — damping, act-order and the upper factor of the inverse.
+ * [OBJ] "A strong answer": H += damp * mean(diag H) * I; U upper triangular
+ * with U^T U = H^-1. [OBJ] "What interviewers probe next": act-order
+ * processes columns in decreasing Hessian diagonal.
+ *
+ * lambda = damp * mean(d) (d from hessian_accumulate; NULL: diag(H) in fp32
+ * is used instead). With act_order, perm = stable sort of columns by
+ * decreasing d (ties: lower index first); otherwise perm = identity.
+ * U[in, in] (output, dense; strictly lower part set to 0) is the upper factor
+ * of (P (H + lambda I) P^T)^-1 in the PROCESSING basis, computed as H = R R^T
+ * (R upper, reversed-order Cholesky) and U = R^-1. perm (int32[in], may be
+ * NULL when act_order == 0) receives perm[k] = original column processed
+ * k-th. lambda_out (host, may be NULL). Synchronous (reads the pivot flag).
+ * Errors: EINVAL (damp < 0 or not finite, in < 1), ENOTPD, ENONFINITE,
+ * EWORKSPACE, EHIP.
+ * ---------------------------------------------------------------------- */
+size_t gptq_factor_workspace_bytes(int64_t in);
+int gptq_inverse_factor(const float* H, const double* d, int64_t in, double damp, int act_order,
+                        float* U, int32_t* perm, double* lambda_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 3 — the column loop in lazy blocks.  [OBJ] "A strong answer": per
+ * group start j (j % g == 0, processing order) scale = max |W_cur| over the
+ * group's columns / qmax, from the error-updated weights; code =
+ * clip(round_half_even(w / scale), -qmax-1, qmax) (scale 0 gives code 0);
+ * err = (w - code*scale) / U_jj is subtracted from the later columns through
+ * row j of U. Updates are batched over blocks of `block_size` columns (the
+ * page's lazy batch): in-block updates in registers, then one fp32 MFMA GEMM
+ * W_cur[:, b1:] -= E U[b0:b1, b1:] per block; the arithmetic is the same.
+ *
+ * W (not modified) in ORIGINAL column order; U from gptq_inverse_factor (in
+ * the processing basis); perm as returned there (NULL = identity).
+ * Outputs: codes int8[out, in] in ORIGINAL column order (row stride in);
+ * scales fp32[out, ceil(in/g)] (row stride ceil(in/g)); g_idx int32[in]
+ * (g_idx[c] = position of column c in processing order / g; may be NULL).
+ * stats (host, may be NULL) double[4]: [0] sum of err^2 (= tr(dW H dW^T) for
+ * the damped H), [1] untouched, [2] ||W - What||_F^2, [3] untouched.
+ * Requires block_size % g == 0 or g % block_size == 0; block_size in
+ * {32, 64, 128}; bits in [2, 8]; g >= 1. Synchronous when stats != NULL.
+ * Errors: EINVAL, ENONFINITE (a non-finite error term), EWORKSPACE, EHIP.
+ * ---------------------------------------------------------------------- */
+size_t gptq_columns_workspace_bytes(int64_t out, int64_t in, int block_size);
+int gptq_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                          const float* U, const int32_t* perm,
+                          int bits, int group_size, int block_size,
+                          int8_t* codes, float* scales, int32_t* g_idx, double* stats,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stages 2 + 3 in one call: gptq_inverse_factor then gptq_quantize_columns.
+ * H is the UNDAMPED X^T X from hessian_accumulate (not modified), d its fp64
+ * column sums of squares (may be NULL). perm may be NULL when act_order == 0.
+ * stats (host, may be NULL) double[4]: [0] sum err^2, [1] lambda,
+ * [2] ||dW||_F^2, [3] calibration objective ||X dW^T||^2 =
+ * stats[0] - lambda * stats[2] (an identity of the loop; see DESIGN).
+ * Synchronous. Errors: union of the two stages.
+ * ---------------------------------------------------------------------- */
+size_t gptq_workspace_bytes(int64_t out, int64_t in, int block_size);
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                        const float* H, const double* d,
+                        int bits, int group_size, double damp, int act_order, int block_size,
+                        int8_t* codes, float* scales, int32_t* g_idx, int32_t* perm, double* stats,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 4 — AWQ's per-layer alpha grid search.  [OBJ] "A strong answer",
+ * AWQ: s_j = mean|x_j|^alpha; scale W's column j by s_j, round to nearest
+ * (symmetric groups of g), and pick the alpha with the least calibration
+ * output error ||X (W - What)^T||^2, What = Q(W diag s) diag(s)^-1.
+ * [PTQ] 3.2: the scaled weights are quantized uniformly; 1/s is folded into
+ * the previous operator by the caller.
+ *
+ * mean|x_j| is floored at 1e-12 * max_j mean|x_j|. alphas (host, n_alpha
+ * values, n_alpha in [1, 64]). Outputs: alpha_best (host), err_per_alpha
+ * (host, n_alpha doubles, may be NULL), s fp32[in] at alpha_best (device),
+ * codes int8[out, in] and scales fp32[out, ceil(in/g)] of W diag(s) (device).
+ * Ties go to the first alpha of the grid. Synchronous.
+ * Errors: EINVAL, EWORKSPACE, EHIP.
+ * ---------------------------------------------------------------------- */
+size_t awq_workspace_bytes(int64_t out, int64_t in, int64_t rows, int n_alpha);
+int awq_search_alpha(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                     const void* X, int x_dtype, int64_t rows, int64_t ldx,
+                     const float* alphas, int n_alpha, int bits, int group_size,
+                     float* alpha_best, double* err_per_alpha, float* s,
+                     int8_t* codes, float* scales,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PTQ_H */

@@ -1,0 +1,34 @@
+/*
+ * ptq_testing.h — test hook of libptq.so (not part of the product API).
+ *
+ * Exposes the fp32 MFMA GEMM used inside stages 2 and 3 so its operand
+ * layouts and triangle modes can be checked against a reference on their own:
+ *
+ *   C = alpha * op(A) op(B) + beta * C,   beta = beta_one ? 1 : 0
+ *
+ * layout_a: 0 = A row-major [M, K] (row stride lda), 1 = A stored [K, M].
+ * layout_b: 0 = B row-major [K, N] (row stride ldb), 1 = B stored [N, K].
+ * tri: 0 none; 1 A upper triangular (A[i][k] = 0 for k < i: those k are
+ * skipped per row tile); 2 B upper (layout 0, B[k][j] = 0 for k > j);
+ * 3 B upper stored [N][K] (entries with k < j are zero). upper_only: only
+ * 128 x 128 output tiles on or above the diagonal are written.
+ * Device pointers; lda, ldb multiples of 4; asynchronous on `stream`.
+ * Returns PTQ_OK, PTQ_EINVAL or PTQ_EHIP.
+ */
+#ifndef PTQ_TESTING_H
+#define PTQ_TESTING_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int ptq_test_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int layout_a, const float* B,
+                      int64_t ldb, int layout_b, float* C, int64_t ldc, float alpha, int beta_one, int tri,
+                      int upper_only, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PTQ_TESTING_H */

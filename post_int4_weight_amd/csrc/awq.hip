@@ -1,0 +1,313 @@
+// Stage 4: AWQ's per-layer alpha grid search on the calibration output error.
+//
+// "GPTQ versus AWQ objectives", "A strong answer", AWQ paragraph: scale input
+// channel j of W up by s_j = mean|x_j|^alpha (the activation is scaled down by
+// the same factor in the previous operator), round to nearest, and grid-search
+// the single exponent alpha per layer on the calibration output error; no
+// reconstruction and no backprop. "A Comprehensive Analysis of Post-Training
+// Quantization Strategies for LLMs: GPTQ, AWQ and GGUF", section 3.2: the
+// equivalent transform y = (W s)(X / s), then uniform quantization of the
+// scaled matrix.
+//
+// All alphas are evaluated in one batch: awq_quant_kernel writes, per alpha,
+// dW = W - Q(W diag s) diag(s)^-1 as a bf16 high part plus a bf16 residual;
+// the bf16 MFMA GEMM of gemm_bf16.hip then forms X dW^T tile by tile and keeps
+// only each tile's sum of squares (E is never written). fp32 calibration
+// inputs take an fp32 path (E through the fp32 MFMA GEMM, then a reduction).
+#include "common.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+namespace ptq {
+
+int launch_awq_error_gemm(const uint16_t* X, int64_t ldx, int64_t rows, int64_t n, const uint16_t* hi,
+                          const uint16_t* lo, int64_t ldw, int64_t out, int64_t batch_stride, int nbatch,
+                          double* partial, int64_t* ntiles_out, hipStream_t st);
+
+namespace {
+
+constexpr double MEAN_ABS_FLOOR = 1e-12;
+
+// m_j (+)= sum over a slab of rows of |x_ij| (fp64); slabs reduced later.
+template <typename T>
+__global__ void col_abs_sum_kernel(const T* __restrict__ X, int64_t ldx, int64_t rows, int64_t n,
+                                   int64_t slab_rows, double* __restrict__ part) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    const int64_t r0 = (int64_t)blockIdx.y * slab_rows, r1 = std::min<int64_t>(rows, r0 + slab_rows);
+    double s = 0.0;
+    for (int64_t r = r0; r < r1; ++r) s += fabs((double)load_as_float<T>(X, r * ldx + c));
+    part[(int64_t)blockIdx.y * n + c] = s;
+}
+
+// m = mean|x| with the floor; one workgroup computes the max for the floor.
+__global__ void mean_abs_finish_kernel(const double* part, int nslab, int64_t n, int64_t rows, double* m) {
+    __shared__ double red[256];
+    double mx = 0.0;
+    for (int64_t c = threadIdx.x; c < n; c += 256) {
+        double s = 0.0;
+        for (int q = 0; q < nslab; ++q) s += part[(int64_t)q * n + c];
+        s /= (double)rows;
+        m[c] = s;
+        mx = fmax(mx, s);
+    }
+    red[threadIdx.x] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    const double floor_v = MEAN_ABS_FLOOR * red[0];
+    for (int64_t c = threadIdx.x; c < n; c += 256) m[c] = fmax(m[c], floor_v);
+}
+
+// s[a][j] = m_j ^ alpha_a (fp64 pow, stored fp32)
+__global__ void scales_kernel(const double* m, int64_t n, const float* alphas, int na, float* s) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int a = blockIdx.y;
+    if (c < n && a < na) s[(int64_t)a * n + c] = (float)pow(m[c], (double)alphas[a]);
+}
+
+// One thread per (alpha, row, group): RTN of the scaled group, then either the
+// hi/lo split of dW (search) or the codes/scales of W diag(s) (final).
+template <typename T>
+__global__ void awq_quant_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n, int g, float qmax,
+                                 const float* __restrict__ s_all, int na, uint16_t* __restrict__ hi,
+                                 uint16_t* __restrict__ lo, int8_t* __restrict__ codes, float* __restrict__ scales,
+                                 int64_t ngroups) {
+    const int64_t per_a = out * ngroups;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= per_a * na) return;
+    const int a = (int)(id / per_a);
+    const int64_t rem = id % per_a;
+    const int64_t r = rem / ngroups, grp = rem % ngroups;
+    const float* s = s_all + (int64_t)a * n;
+    const int64_t c0 = grp * g, c1 = std::min<int64_t>(n, c0 + g);
+    float mx = 0.f;
+    for (int64_t c = c0; c < c1; ++c) mx = fmaxf(mx, fabsf(load_as_float<T>(W, r * ldw + c) * s[c]));
+    const float scale = mx / qmax;
+    if (scales) scales[r * ngroups + grp] = scale;
+    for (int64_t c = c0; c < c1; ++c) {
+        const float w = load_as_float<T>(W, r * ldw + c);
+        const float ws = w * s[c];
+        float q = 0.f;
+        if (scale > 0.f) q = fminf(fmaxf(rintf(ws / scale), -qmax - 1.f), qmax);
+        if (codes) {
+            codes[r * n + c] = (int8_t)(int)q;
+        } else {
+            const float dw = w - (q * scale) / s[c];
+            const uint16_t h = float_to_bf16_bits(dw);
+            const float l = dw - bf16_bits_to_float(h);
+            const int64_t o = (int64_t)a * out * n + r * n + c;
+            hi[o] = h;
+            lo[o] = float_to_bf16_bits(l);
+        }
+    }
+}
+
+// fp32 path: dW as fp32 for one alpha (no split)
+template <typename T>
+__global__ void awq_dw_f32_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n, int g, float qmax,
+                                  const float* __restrict__ s, float* __restrict__ dW, int64_t ngroups) {
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= out * ngroups) return;
+    const int64_t r = id / ngroups, grp = id % ngroups;
+    const int64_t c0 = grp * g, c1 = std::min<int64_t>(n, c0 + g);
+    float mx = 0.f;
+    for (int64_t c = c0; c < c1; ++c) mx = fmaxf(mx, fabsf(load_as_float<T>(W, r * ldw + c) * s[c]));
+    const float scale = mx / qmax;
+    for (int64_t c = c0; c < c1; ++c) {
+        const float w = load_as_float<T>(W, r * ldw + c);
+        float q = 0.f;
+        if (scale > 0.f) q = fminf(fmaxf(rintf((w * s[c]) / scale), -qmax - 1.f), qmax);
+        dW[r * n + c] = w - (q * scale) / s[c];
+    }
+}
+
+// sum of squares of a dense buffer (fp64, one workgroup per slice, fixed order)
+__global__ void sumsq_slices_kernel(const float* E, int64_t count, int64_t slice, double* part) {
+    __shared__ double red[256];
+    const int64_t b = (int64_t)blockIdx.x * slice, e = std::min<int64_t>(count, b + slice);
+    double s = 0.0;
+    for (int64_t i = b + threadIdx.x; i < e; i += 256) s += (double)E[i] * (double)E[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// err[a] = sum over tiles of partial[a][tile], fixed order
+__global__ void reduce_err_kernel(const double* partial, int64_t ntiles, double* err) {
+    __shared__ double red[256];
+    const int a = blockIdx.x;
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < ntiles; i += 256) s += partial[(int64_t)a * ntiles + i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) err[a] = red[0];
+}
+
+constexpr int64_t SLAB = 1024;
+constexpr int64_t F32_SLICE = 1 << 16;
+
+struct AwqLayout {
+    int64_t nslab, ntiles;
+};
+
+AwqLayout awq_layout(int64_t out, int64_t n, int64_t rows) {
+    AwqLayout l;
+    l.nslab = std::max<int64_t>(1, cdiv(rows, SLAB));
+    l.ntiles = cdiv(rows, 256) * cdiv(out, 256);
+    return l;
+}
+
+}  // namespace
+
+size_t awq_ws_bytes(int64_t out, int64_t n, int64_t rows, int n_alpha) {
+    AwqLayout l = awq_layout(out, n, rows);
+    Sizer z;
+    z.take<double>((size_t)l.nslab * n);        // column |x| partials
+    z.take<double>((size_t)n);                  // m
+    z.take<float>((size_t)n_alpha * n);         // s per alpha
+    z.take<float>((size_t)n_alpha);             // alphas (device copy)
+    z.take<double>((size_t)n_alpha);            // err
+    // bf16 path: hi + lo for every alpha, one partial per tile and alpha
+    Sizer b = z;
+    b.take<uint16_t>((size_t)n_alpha * out * n);
+    b.take<uint16_t>((size_t)n_alpha * out * n);
+    b.take<double>((size_t)n_alpha * l.ntiles);
+    // fp32 path: dW and E for one alpha, slice partials
+    Sizer f = z;
+    f.take<float>((size_t)out * n);
+    f.take<float>((size_t)rows * out);
+    f.take<double>((size_t)cdiv(rows * out, F32_SLICE) + 1);
+    return std::max(b.bytes(), f.bytes());
+}
+
+int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, const void* X, int x_dtype,
+            int64_t rows, int64_t ldx, const float* alphas, int n_alpha, int bits, int g, float* alpha_best,
+            double* err_per_alpha, float* s_out, int8_t* codes, float* scales, void* ws, size_t ws_bytes,
+            hipStream_t st) {
+    AwqLayout l = awq_layout(out, n, rows);
+    Arena ar(ws, ws_bytes);
+    double* cpart = ar.take<double>((size_t)l.nslab * n);
+    double* m = ar.take<double>((size_t)n);
+    float* s_all = ar.take<float>((size_t)n_alpha * n);
+    float* al_dev = ar.take<float>((size_t)n_alpha);
+    double* err = ar.take<double>((size_t)n_alpha);
+    const int64_t ngroups = cdiv(n, g);
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    const bool bf = (x_dtype == PTQ_BF16);
+    uint16_t *hi = nullptr, *lo = nullptr;
+    double* partial = nullptr;
+    float *dW = nullptr, *E = nullptr;
+    if (bf) {
+        hi = ar.take<uint16_t>((size_t)n_alpha * out * n);
+        lo = ar.take<uint16_t>((size_t)n_alpha * out * n);
+        partial = ar.take<double>((size_t)n_alpha * l.ntiles);
+    } else {
+        dW = ar.take<float>((size_t)out * n);
+        E = ar.take<float>((size_t)rows * out);
+        partial = ar.take<double>((size_t)cdiv(rows * out, F32_SLICE) + 1);
+    }
+    if (!cpart || !m || !s_all || !al_dev || !err || !partial || (bf && (!hi || !lo)) || (!bf && (!dW || !E))) {
+        set_error("awq_search_alpha: workspace of %zu bytes, %zu needed", ws_bytes,
+                  awq_ws_bytes(out, n, rows, n_alpha));
+        return PTQ_EWORKSPACE;
+    }
+    PTQ_HIP(hipMemcpyAsync(al_dev, alphas, sizeof(float) * n_alpha, hipMemcpyHostToDevice, st));
+
+    // m_j = mean |x_j|
+    {
+        dim3 grid((unsigned)cdiv(n, 256), (unsigned)l.nslab);
+        if (bf)
+            hipLaunchKernelGGL(col_abs_sum_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)X, ldx, rows, n,
+                               SLAB, cpart);
+        else
+            hipLaunchKernelGGL(col_abs_sum_kernel<float>, grid, dim3(256), 0, st, (const float*)X, ldx, rows, n, SLAB,
+                               cpart);
+        PTQ_LAUNCH_CHECK();
+        hipLaunchKernelGGL(mean_abs_finish_kernel, dim3(1), dim3(256), 0, st, cpart, (int)l.nslab, n, rows, m);
+        PTQ_LAUNCH_CHECK();
+        hipLaunchKernelGGL(scales_kernel, dim3((unsigned)cdiv(n, 256), (unsigned)n_alpha), dim3(256), 0, st, m, n,
+                           al_dev, n_alpha, s_all);
+        PTQ_LAUNCH_CHECK();
+    }
+
+    if (bf) {
+        const int64_t nth = out * ngroups * n_alpha;
+        if (w_dtype == PTQ_BF16)
+            hipLaunchKernelGGL(awq_quant_kernel<uint16_t>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st,
+                               (const uint16_t*)W, ldw, out, n, g, qmax, s_all, n_alpha, hi, lo, (int8_t*)nullptr,
+                               (float*)nullptr, ngroups);
+        else
+            hipLaunchKernelGGL(awq_quant_kernel<float>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st,
+                               (const float*)W, ldw, out, n, g, qmax, s_all, n_alpha, hi, lo, (int8_t*)nullptr,
+                               (float*)nullptr, ngroups);
+        PTQ_LAUNCH_CHECK();
+        int64_t ntiles = 0;
+        PTQ_TRY(launch_awq_error_gemm((const uint16_t*)X, ldx, rows, n, hi, lo, n, out, out * n, n_alpha, partial,
+                                      &ntiles, st));
+        hipLaunchKernelGGL(reduce_err_kernel, dim3((unsigned)n_alpha), dim3(256), 0, st, partial, ntiles, err);
+        PTQ_LAUNCH_CHECK();
+    } else {
+        const int64_t nslice = cdiv(rows * out, F32_SLICE);
+        for (int a = 0; a < n_alpha; ++a) {
+            if (w_dtype == PTQ_BF16)
+                hipLaunchKernelGGL(awq_dw_f32_kernel<uint16_t>, dim3((unsigned)cdiv(out * ngroups, 256)), dim3(256), 0,
+                                   st, (const uint16_t*)W, ldw, out, n, g, qmax, s_all + (int64_t)a * n, dW, ngroups);
+            else
+                hipLaunchKernelGGL(awq_dw_f32_kernel<float>, dim3((unsigned)cdiv(out * ngroups, 256)), dim3(256), 0, st,
+                                   (const float*)W, ldw, out, n, g, qmax, s_all + (int64_t)a * n, dW, ngroups);
+            PTQ_LAUNCH_CHECK();
+            // E = X dW^T  [rows, out]
+            GemmArgs ga{};
+            ga.M = rows; ga.N = out; ga.K = n;
+            ga.A = (const float*)X; ga.lda = ldx; ga.layout_a = A_MK;
+            ga.B = dW; ga.ldb = n; ga.layout_b = B_NK;
+            ga.C = E; ga.ldc = out; ga.alpha = 1.f; ga.beta_one = 0; ga.tri = TRI_NONE; ga.upper_only = 0;
+            PTQ_TRY(launch_gemm_f32(ga, st));
+            hipLaunchKernelGGL(sumsq_slices_kernel, dim3((unsigned)nslice), dim3(256), 0, st, E, rows * out, F32_SLICE,
+                               partial);
+            PTQ_LAUNCH_CHECK();
+            hipLaunchKernelGGL(reduce_err_kernel, dim3(1), dim3(256), 0, st, partial, nslice, err + a);
+            PTQ_LAUNCH_CHECK();
+        }
+    }
+
+    std::vector<double> eh(n_alpha);
+    PTQ_HIP(hipMemcpyAsync(eh.data(), err, sizeof(double) * n_alpha, hipMemcpyDeviceToHost, st));
+    PTQ_HIP(hipStreamSynchronize(st));
+    int best = 0;
+    for (int a = 1; a < n_alpha; ++a)
+        if (eh[a] < eh[best]) best = a;
+    if (err_per_alpha)
+        for (int a = 0; a < n_alpha; ++a) err_per_alpha[a] = eh[a];
+    if (alpha_best) *alpha_best = alphas[best];
+
+    // final codes / scales of W diag(s) at alpha*
+    const float* sb = s_all + (int64_t)best * n;
+    if (s_out) PTQ_HIP(hipMemcpyAsync(s_out, sb, sizeof(float) * n, hipMemcpyDeviceToDevice, st));
+    const int64_t nth = out * ngroups;
+    if (w_dtype == PTQ_BF16)
+        hipLaunchKernelGGL(awq_quant_kernel<uint16_t>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st,
+                           (const uint16_t*)W, ldw, out, n, g, qmax, sb, 1, (uint16_t*)nullptr, (uint16_t*)nullptr,
+                           codes, scales, ngroups);
+    else
+        hipLaunchKernelGGL(awq_quant_kernel<float>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st, (const float*)W,
+                           ldw, out, n, g, qmax, sb, 1, (uint16_t*)nullptr, (uint16_t*)nullptr, codes, scales, ngroups);
+    PTQ_LAUNCH_CHECK();
+    PTQ_HIP(hipStreamSynchronize(st));
+    return PTQ_OK;
+}
+
+}  // namespace ptq

@@ -1,0 +1,290 @@
+// Stage 2: damping, act-order permutation and U, the upper factor of H^-1.
+//
+// "GPTQ versus AWQ objectives", "A strong answer": H += damp * mean(diag H) I,
+// then U upper triangular with U^T U = H^-1 (the page forms it as the
+// Cholesky factor of inv(H), transposed). "What interviewers probe next":
+// act-order processes columns in decreasing Hessian diagonal.
+//
+// U is unique (positive diagonal), so it is computed here by a cheaper route
+// that never forms H^-1: the reversed-order Cholesky H = R R^T with R upper
+// triangular, then U = R^-1 (U^T U = R^-T R^-1 = (R R^T)^-1). Both factors are
+// produced together by one recursion on the 2 x 2 block split
+//
+//   H = [H11 H12; H12^T H22]:  (R22, U22) from H22 (recursively),
+//                              R12 = H12 U22^T,
+//                              H11 <- H11 - R12 R12^T,
+//                              (R11, U11) from H11 (recursively),
+//                              U12 = -U11 R12 U22,
+//
+// so 2n^3/3 flops run as large fp32 MFMA GEMMs (gemm_f32.hip) and only
+// 64 x 64 diagonal blocks are factored and inverted inside one workgroup's
+// LDS. A non-positive (or NaN) pivot raises a device flag read once at the end.
+#include "common.hpp"
+
+#include <algorithm>
+#include <cmath>
+
+namespace ptq {
+namespace {
+
+constexpr int BASE = 64;
+
+// lambda = damp * mean(key); key = d (fp64) or diag(H). One workgroup, fixed order.
+__global__ void damping_kernel(const float* H, const double* d, int64_t n, double damp, double* lam) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 256) s += d ? d[i] : (double)H[i * n + i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *lam = damp * (red[0] / (double)n);
+}
+
+// Act-order key of column j; a NaN key sorts last (so the ranks stay a
+// permutation; the NaN itself is reported by the factorization).
+__device__ __forceinline__ double order_key(const float* H, const double* d, int64_t n, int64_t j) {
+    const double v = d ? d[j] : (double)H[j * n + j];
+    return (v != v) ? -HUGE_VAL : v;
+}
+
+// perm[rank(j)] = j with rank(j) = #{k : key_k > key_j or (key_k == key_j and k < j)}:
+// the stable sort of columns by decreasing key.
+__global__ void act_order_rank_kernel(const float* H, const double* d, int64_t n, int32_t* perm) {
+    __shared__ double tile[256];
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const double kj = (j < n) ? order_key(H, d, n, j) : 0.0;
+    int64_t rank = 0;
+    for (int64_t b = 0; b < n; b += 256) {
+        const int64_t k = b + threadIdx.x;
+        tile[threadIdx.x] = (k < n) ? order_key(H, d, n, k) : 0.0;
+        __syncthreads();
+        const int lim = (int)std::min<int64_t>(256, n - b);
+        for (int q = 0; q < lim; ++q) {
+            const double kk = tile[q];
+            rank += (kk > kj || (kk == kj && b + q < j)) ? 1 : 0;
+        }
+        __syncthreads();
+    }
+    if (j < n) perm[rank] = (int32_t)j;
+}
+
+__global__ void identity_perm_kernel(int32_t* perm, int64_t n) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) perm[j] = (int32_t)j;
+}
+
+// A[i][j] = H[p_i][p_j] + lambda [i == j]  (p = perm or identity)
+__global__ void build_damped_kernel(const float* __restrict__ H, const int32_t* __restrict__ perm, int64_t n,
+                                    const double* lam, float* __restrict__ A) {
+    const int64_t i = blockIdx.y;
+    const int64_t pi = perm ? perm[i] : i;
+    const float l = (float)*lam;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t pj = perm ? perm[j] : j;
+        float v = H[pi * n + pj];
+        if (i == j) v = (float)((double)v + (double)l);
+        A[i * n + j] = v;
+    }
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t count) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
+         e += (int64_t)gridDim.x * blockDim.x)
+        p[e] = 0.f;
+}
+
+__global__ void fill_int_kernel(int* p, int v) { *p = v; }
+
+// Base case on an m x m diagonal block (m <= BASE): reversed Cholesky of the
+// block's upper triangle, A = R R^T, then U = R^-1, both in LDS; U is written
+// to the block (zeros below its diagonal). Bit 0 of *flag: non-positive pivot;
+// bit 1: NaN pivot.
+__global__ __launch_bounds__(256) void chol_inv_base_kernel(const float* __restrict__ A, float* __restrict__ U,
+                                                             int m, int64_t ld, int* flag) {
+    __shared__ float a[BASE][BASE + 1];
+    __shared__ float u[BASE][BASE + 1];
+    const int t = threadIdx.x;
+    for (int e = t; e < m * m; e += 256) {
+        const int i = e / m, j = e % m;
+        a[i][j] = (i <= j) ? A[(int64_t)i * ld + j] : 0.f;
+        u[i][j] = 0.f;
+    }
+    __syncthreads();
+    // reversed-order Cholesky: column j from the last to the first
+    for (int j = m - 1; j >= 0; --j) {
+        float piv = a[j][j];
+        if (!(piv > 0.f)) {
+            if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
+            piv = 1.f;
+        }
+        const float rjj = sqrtf(piv);
+        __syncthreads();
+        for (int i = t; i < j; i += 256) a[i][j] = a[i][j] / rjj;
+        if (t == 0) a[j][j] = rjj;
+        __syncthreads();
+        // A[i][k] -= R[i][j] R[k][j] for 0 <= i <= k < j
+        const int cnt = j * j;
+        for (int e = t; e < cnt; e += 256) {
+            const int i = e / j, k = e % j;
+            if (i <= k) a[i][k] -= a[i][j] * a[k][j];
+        }
+        __syncthreads();
+    }
+    // U = R^-1, row by row from the bottom: U[i][i] = 1/R[i][i],
+    // U[i][c] = -(sum_{k=i+1..c} R[i][k] U[k][c]) / R[i][i]
+    // 4 threads per column c, each summing a strided quarter of k.
+    const int c = t >> 2, part = t & 3;
+    for (int i = m - 1; i >= 0; --i) {
+        float s = 0.f;
+        if (c < m && c > i)
+            for (int k = i + 1 + part; k <= c; k += 4) s += a[i][k] * u[k][c];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (c < m && part == 0) {
+            if (c == i) u[i][i] = 1.f / a[i][i];
+            else if (c > i) u[i][c] = -s / a[i][i];
+        }
+        __syncthreads();
+    }
+    for (int e = t; e < m * m; e += 256) {
+        const int i = e / m, j = e % m;
+        U[(int64_t)i * ld + j] = (i <= j) ? u[i][j] : 0.f;
+    }
+}
+
+struct Ctx {
+    float* A;      // damped (permuted) H, destroyed
+    float* U;      // output
+    float* T;      // scratch, >= (n/2)^2 + slack
+    int64_t n;
+    int* flag;
+    hipStream_t st;
+};
+
+int gemm(Ctx& c, int64_t M, int64_t N, int64_t K, const float* A, int la, const float* B, int lb,
+         int64_t ldb, float* C, int64_t ldc, float alpha, int beta_one, int tri, int upper_only) {
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = c.n; g.layout_a = la;
+    g.B = B; g.ldb = ldb; g.layout_b = lb;
+    g.C = C; g.ldc = ldc;
+    g.alpha = alpha; g.beta_one = beta_one; g.tri = tri; g.upper_only = upper_only;
+    prof_begin(PROF_FACTOR_GEMM, c.st);
+    const int s = launch_gemm_f32(g, c.st);
+    prof_end(PROF_FACTOR_GEMM, c.st);
+    return s;
+}
+
+// Factor the diagonal block [o, o+m) of A into U (see the recursion above).
+int recurse(Ctx& c, int64_t o, int64_t m) {
+    const int64_t n = c.n;
+    if (m <= BASE) {
+        prof_begin(PROF_FACTOR_BASE, c.st);
+        hipLaunchKernelGGL(chol_inv_base_kernel, dim3(1), dim3(256), 0, c.st, c.A + o * n + o, c.U + o * n + o,
+                           (int)m, n, c.flag);
+        prof_end(PROF_FACTOR_BASE, c.st);
+        PTQ_LAUNCH_CHECK();
+        return PTQ_OK;
+    }
+    // split so the trailing part is a multiple of BASE (keeps blocks aligned)
+    const int64_t n2 = cdiv(m / 2, BASE) * BASE;
+    const int64_t n1 = m - n2;
+    float* A12 = c.A + o * n + (o + n1);
+    float* A11 = c.A + o * n + o;
+    float* U11 = c.U + o * n + o;
+    float* U12 = c.U + o * n + (o + n1);   // holds R12 until U12 replaces it
+    float* U22 = c.U + (o + n1) * n + (o + n1);
+    PTQ_TRY(recurse(c, o + n1, n2));
+    // R12 = H12 U22^T  (U22 stored [N][K], upper: entries with k < j are zero)
+    PTQ_TRY(gemm(c, n1, n2, n2, A12, A_MK, U22, B_NK, n, U12, n, 1.f, 0, TRI_B_UPPER_NK, 0));
+    // H11 -= R12 R12^T (upper tiles only)
+    PTQ_TRY(gemm(c, n1, n1, n2, U12, A_MK, U12, B_NK, n, A11, n, -1.f, 1, TRI_NONE, 1));
+    PTQ_TRY(recurse(c, o, n1));
+    // T = R12 U22 (U22 upper: B[k][j] = 0 for k > j), T is [n1, n2] with row stride n2
+    PTQ_TRY(gemm(c, n1, n2, n2, U12, A_MK, U22, B_KN, n, c.T, n2, 1.f, 0, TRI_B_UPPER_KN, 0));
+    // U12 = -U11 T (U11 upper: A[i][k] = 0 for k < i)
+    {
+        GemmArgs g{};
+        g.M = n1; g.N = n2; g.K = n1;
+        g.A = U11; g.lda = n; g.layout_a = A_MK;
+        g.B = c.T; g.ldb = n2; g.layout_b = B_KN;
+        g.C = U12; g.ldc = n;
+        g.alpha = -1.f; g.beta_one = 0; g.tri = TRI_A_UPPER; g.upper_only = 0;
+        prof_begin(PROF_FACTOR_GEMM, c.st);
+        const int s = launch_gemm_f32(g, c.st);
+        prof_end(PROF_FACTOR_GEMM, c.st);
+        PTQ_TRY(s);
+    }
+    return PTQ_OK;
+}
+
+}  // namespace
+
+size_t factor_workspace_bytes(int64_t n) {
+    Sizer z;
+    z.take<float>((size_t)n * n);                          // A
+    const int64_t half = cdiv(n / 2, BASE) * BASE;
+    z.take<float>((size_t)half * half + 1024);             // T
+    z.take<double>(1);                                     // lambda
+    z.take<int>(1);                                        // flag
+    z.take<int32_t>((size_t)n);                            // perm (when the caller passes none)
+    return z.bytes();
+}
+
+int run_inverse_factor(const float* H, const double* d, int64_t n, double damp, int act_order, float* U,
+                       int32_t* perm, double* lambda_host, void* ws, size_t ws_bytes, hipStream_t st) {
+    Arena ar(ws, ws_bytes);
+    Ctx c{};
+    c.n = n;
+    c.st = st;
+    c.A = ar.take<float>((size_t)n * n);
+    const int64_t half = cdiv(n / 2, BASE) * BASE;
+    c.T = ar.take<float>((size_t)half * half + 1024);
+    double* lam = ar.take<double>(1);
+    c.flag = ar.take<int>(1);
+    int32_t* ptmp = ar.take<int32_t>((size_t)n);
+    if (!c.A || !c.T || !lam || !c.flag || !ptmp) {
+        set_error("gptq_inverse_factor: workspace of %zu bytes, %zu needed", ws_bytes, factor_workspace_bytes(n));
+        return PTQ_EWORKSPACE;
+    }
+    c.U = U;
+    int32_t* p = perm ? perm : ptmp;
+
+    hipLaunchKernelGGL(fill_int_kernel, dim3(1), dim3(1), 0, st, c.flag, 0);
+    PTQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(damping_kernel, dim3(1), dim3(256), 0, st, H, d, n, damp, lam);
+    PTQ_LAUNCH_CHECK();
+    if (act_order) {
+        hipLaunchKernelGGL(act_order_rank_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, H, d, n, p);
+    } else {
+        hipLaunchKernelGGL(identity_perm_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, p, n);
+    }
+    PTQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(build_damped_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)n),
+                       dim3(256), 0, st, H, act_order ? p : nullptr, n, lam, c.A);
+    PTQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, st, U, n * n);
+    PTQ_LAUNCH_CHECK();
+    PTQ_TRY(recurse(c, 0, n));
+
+    int flag = 0;
+    double lh = 0.0;
+    PTQ_HIP(hipMemcpyAsync(&flag, c.flag, sizeof(int), hipMemcpyDeviceToHost, st));
+    PTQ_HIP(hipMemcpyAsync(&lh, lam, sizeof(double), hipMemcpyDeviceToHost, st));
+    PTQ_HIP(hipStreamSynchronize(st));
+    if (lambda_host) *lambda_host = lh;
+    if (flag & 2) {
+        set_error("gptq_inverse_factor: NaN pivot (non-finite H or d)");
+        return PTQ_ENONFINITE;
+    }
+    if (flag & 1) {
+        set_error("gptq_inverse_factor: H + lambda I is not positive definite (lambda = %g)", lh);
+        return PTQ_ENOTPD;
+    }
+    return PTQ_OK;
+}
+
+}  // namespace ptq

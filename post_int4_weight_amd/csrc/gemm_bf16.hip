@@ -1,0 +1,473 @@
+// bf16 "NT" GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16):
+//
+//   C[i][j] = sum_k A[i][k] B[j][k]      A [M, K], B [N, K], both K-contiguous
+//
+// Two uses, selected by the epilogue:
+//  * the proxy Hessian H (+)= X^T X ("GPTQ versus AWQ objectives", "A strong
+//    answer"), run on a transposed chunk of the calibration rows, Xt [in,
+//    rows], with A = B = Xt: only tiles on or above the diagonal are
+//    computed; the tile is added into H (fp32) and, on request, mirrored;
+//  * AWQ's calibration output error ||X dW^T||^2 (same page, AWQ paragraph),
+//    with A = X [rows, in] and B = dW [out, in] split into a bf16 high part and
+//    a bf16 residual (dW = hi + lo to ~16 significant bits): the K loop runs
+//    over both halves with the same A, and the epilogue reduces the tile's
+//    sum of squares to one fp64 partial per workgroup (E is never written).
+//
+// Tile 256 x 256 (or 128 x 128) per workgroup of 256 threads, 4 wave64s in
+// 2 x 2, each wave a (BM/2)^2 block of 32x32 MFMA accumulators. K is staged
+// 32 at a time through LDS, double buffered: 16-byte chunks go straight from
+// global memory into 64-byte LDS rows whose chunk index is XOR-swizzled by
+// (row >> 2) & 3, so both the staging writes and the ds_read_b128 operand
+// fetches (32 rows x 2 chunks per wave) are free of bank conflicts.
+//
+// Workgroup order is XCD-aware: blockIdx b runs on XCD b % 8, so logical work
+// items are handed out in contiguous runs per XCD; Hessian tiles are ordered
+// in bands of 4 tile-rows so the ~32 tiles one XCD holds at a time reuse a
+// dozen panels from its L2.
+#include "common.hpp"
+
+#include <algorithm>
+
+namespace ptq {
+namespace {
+
+constexpr int KT = 32;
+constexpr int NTH = 256;
+constexpr int BAND = 4;
+constexpr int NXCD = 8;
+
+enum { EPI_HESSIAN = 0, EPI_SUMSQ = 1 };
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+
+// Upper-triangle tile at position L of the band order (T tile-rows).
+__device__ __forceinline__ void band_tile(int64_t L, int T, int& ti, int& tj) {
+    int r0 = 0;
+    while (true) {
+        const int h = min(BAND, T - r0);
+        const int64_t tri = (int64_t)h * (h + 1) / 2;
+        const int64_t cnt = tri + (int64_t)(T - r0 - h) * h;
+        if (L < cnt) {
+            if (L < tri) {
+                int c = 0;
+                while ((int64_t)(c + 1) * (c + 2) / 2 <= L) ++c;
+                tj = r0 + c;
+                ti = r0 + (int)(L - (int64_t)c * (c + 1) / 2);
+            } else {
+                const int64_t q = L - tri;
+                tj = r0 + h + (int)(q / h);
+                ti = r0 + (int)(q % h);
+            }
+            return;
+        }
+        L -= cnt;
+        r0 += h;
+    }
+}
+
+struct Bf16GemmArgs {
+    // operand segments: k in [0, K1) uses (A1, B1); k in [K1, K1 + K2) uses (A2, B2) at k - K1
+    const uint16_t* A1; const uint16_t* B1;
+    const uint16_t* A2; const uint16_t* B2;
+    int64_t K1, K2;
+    int64_t lda, ldb;
+    int64_t M, N;
+    int64_t b_batch_stride;    // EPI_SUMSQ: B offset per blockIdx.y
+    // EPI_HESSIAN
+    float* H; int64_t ldh; int mirror; int T; int store_not_add;
+    // EPI_SUMSQ
+    double* partial;           // [gridDim.y][tiles]
+    int64_t tiles_n, ntiles;
+};
+
+template <int BMX>
+struct Smem {
+    alignas(16) unsigned char a[2][BMX * 64];
+    alignas(16) unsigned char b[2][BMX * 64];
+};
+
+template <int BMX>
+struct Stg {
+    uint4 a[BMX / 64];
+    uint4 b[BMX / 64];
+};
+
+// Load this thread's share of a K-slab of one operand panel (rows x0.., k0..k0+31).
+template <int BMX>
+__device__ __forceinline__ void load_panel(uint4 (&v)[BMX / 64], const uint16_t* P, int64_t ld,
+                                           int64_t x0, int64_t X, int64_t k0, int64_t K, int t) {
+#pragma unroll
+    for (int q = 0; q < BMX / 64; ++q) {
+        const int idx = t + NTH * q;          // BMX rows x 4 chunks
+        const int r = idx >> 2, c = idx & 3;
+        const int64_t row = x0 + r, k = k0 + 8 * c;
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (row < X) {
+            const uint16_t* p = P + row * ld + k;
+            if (k + 8 <= K) {
+                val = *(const uint4*)p;
+            } else if (k < K) {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                for (int e = 0; e < 8; ++e)
+                    if (k + e < K) w[e >> 1] |= ((uint32_t)p[e]) << (16 * (e & 1));
+                val = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        v[q] = val;
+    }
+}
+
+template <int BMX>
+__device__ __forceinline__ void store_panel(unsigned char* S, const uint4 (&v)[BMX / 64], int t) {
+#pragma unroll
+    for (int q = 0; q < BMX / 64; ++q) {
+        const int idx = t + NTH * q;
+        const int r = idx >> 2, c = idx & 3;
+        *(uint4*)(S + swz(r, c)) = v[q];
+    }
+}
+
+template <int BMX, int EPI>
+__global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, int64_t nwork) {
+    constexpr int WT = BMX / 64;
+    const int64_t per = (nwork + NXCD - 1) / NXCD;
+    const int64_t L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
+    if (L >= nwork) return;
+
+    int64_t i0, j0;
+    bool diag = false;
+    if (EPI == EPI_HESSIAN) {
+        int ti, tj;
+        band_tile(L, g.T, ti, tj);
+        i0 = (int64_t)ti * BMX;
+        j0 = (int64_t)tj * BMX;
+        diag = (ti == tj);
+    } else {
+        i0 = (L / g.tiles_n) * BMX;
+        j0 = (L % g.tiles_n) * BMX;
+    }
+    const uint16_t* B1 = g.B1 + (int64_t)blockIdx.y * g.b_batch_stride;
+    const uint16_t* B2 = g.B2 ? g.B2 + (int64_t)blockIdx.y * g.b_batch_stride : nullptr;
+
+    __shared__ Smem<BMX> sm;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 1) * (BMX / 2), wn = (wave & 1) * (BMX / 2);
+    const int li = lane & 31, lh = lane >> 5;
+
+    f32x16 acc[WT][WT];
+#pragma unroll
+    for (int a = 0; a < WT; ++a)
+#pragma unroll
+        for (int b = 0; b < WT; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    const int64_t n1 = cdiv(g.K1, KT), n2 = cdiv(g.K2, KT);
+    const int64_t nst = n1 + n2;
+    Stg<BMX> rg;
+    auto gload = [&](int64_t s) {
+        if (s < n1) {
+            load_panel<BMX>(rg.a, g.A1, g.lda, i0, g.M, s * KT, g.K1, t);
+            load_panel<BMX>(rg.b, B1, g.ldb, j0, g.N, s * KT, g.K1, t);
+        } else {
+            load_panel<BMX>(rg.a, g.A2, g.lda, i0, g.M, (s - n1) * KT, g.K2, t);
+            load_panel<BMX>(rg.b, B2, g.ldb, j0, g.N, (s - n1) * KT, g.K2, t);
+        }
+    };
+
+    if (nst > 0) {
+        gload(0);
+        store_panel<BMX>(sm.a[0], rg.a, t);
+        store_panel<BMX>(sm.b[0], rg.b, t);
+    }
+    __syncthreads();
+    for (int64_t s = 0; s < nst; ++s) {
+        const int cur = (int)(s & 1);
+        const bool more = s + 1 < nst;
+        if (more) gload(s + 1);
+        const unsigned char* As = sm.a[cur];
+        const unsigned char* Bs = sm.b[cur];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 av[WT], bv[WT];
+#pragma unroll
+            for (int a = 0; a < WT; ++a) av[a] = *(const bf16x8*)(As + swz(wm + 32 * a + li, 2 * kk + lh));
+#pragma unroll
+            for (int b = 0; b < WT; ++b) bv[b] = *(const bf16x8*)(Bs + swz(wn + 32 * b + li, 2 * kk + lh));
+#pragma unroll
+            for (int a = 0; a < WT; ++a)
+#pragma unroll
+                for (int b = 0; b < WT; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+        if (more) {
+            store_panel<BMX>(sm.a[cur ^ 1], rg.a, t);
+            store_panel<BMX>(sm.b[cur ^ 1], rg.b, t);
+        }
+        __syncthreads();
+    }
+
+    // 32x32 accumulator layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    if (EPI == EPI_HESSIAN) {
+#pragma unroll
+        for (int a = 0; a < WT; ++a)
+#pragma unroll
+            for (int b = 0; b < WT; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t i = i0 + wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int64_t j = j0 + wn + 32 * b + li;
+                    if (i < g.M && j < g.N) {
+                        float* p = g.H + i * g.ldh + j;
+                        const float v = g.store_not_add ? acc[a][b][r] : (*p + acc[a][b][r]);
+                        *p = v;
+                        if (g.mirror && !diag) g.H[j * g.ldh + i] = v;
+                    }
+                }
+    } else {
+        double s = 0.0;
+#pragma unroll
+        for (int a = 0; a < WT; ++a)
+#pragma unroll
+            for (int b = 0; b < WT; ++b) {
+                float part = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t i = i0 + wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int64_t j = j0 + wn + 32 * b + li;
+                    const float v = (i < g.M && j < g.N) ? acc[a][b][r] : 0.f;
+                    part = fmaf(v, v, part);
+                }
+                s += (double)part;
+            }
+        // wave reduction (fixed order), then across the 4 waves through LDS
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+        __shared__ double red[4];
+        if (lane == 0) red[wave] = s;
+        __syncthreads();
+        if (t == 0)
+            g.partial[(int64_t)blockIdx.y * g.ntiles + L] = ((red[0] + red[1]) + (red[2] + red[3]));
+    }
+}
+
+// Xt[c][r] = X[r0 + r][c] for r < nr; rows nr..ldt-1 of Xt are zeroed.
+__global__ void transpose_rows_kernel(const uint16_t* __restrict__ X, int64_t ldx, int64_t n, int64_t r0,
+                                      int64_t nr, uint16_t* __restrict__ Xt, int64_t ldt) {
+    __shared__ uint16_t tile[64][66];
+    const int64_t cb = (int64_t)blockIdx.x * 64, rb = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 256 threads: 64 x 4
+    for (int y = ty; y < 64; y += 4) {
+        const int64_t r = rb + y, c = cb + tx;
+        tile[y][tx] = (r < nr && c < n) ? X[(r0 + r) * ldx + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int y = ty; y < 64; y += 4) {
+        const int64_t c = cb + y, r = rb + tx;
+        if (c < n && r < ldt) Xt[c * ldt + r] = tile[tx][y];
+    }
+}
+
+__global__ void mirror_diag_blocks_kernel(float* H, int64_t n, int bm) {
+    const int64_t base = (int64_t)blockIdx.y * bm;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < (int64_t)bm * bm;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = base + e / bm, j = base + e % bm;
+        if (i < n && j < n && i > j) H[i * n + j] = H[j * n + i];
+    }
+}
+
+// H[i][j] += sum_s part[s][i][j] over the upper triangle, mirrored.
+__global__ void reduce_partials_kernel(float* H, const float* part, int nsplit, int64_t n) {
+    const int64_t nn = n * n;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = e / n, j = e % n;
+        if (i > j) continue;
+        float v = H[e];
+        for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * nn + e];
+        H[e] = v;
+        if (i != j) H[j * n + i] = v;
+    }
+}
+
+// fp64 column sums of squares over one slab of rows; 2 columns per thread.
+template <typename T>
+__global__ void colsumsq_kernel(const T* __restrict__ X, int64_t ldx, int64_t rows, int64_t n,
+                                int64_t slab_rows, double* __restrict__ out, int direct) {
+    const int64_t c = 2 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+    if (c >= n) return;
+    const int64_t r0 = (int64_t)blockIdx.y * slab_rows;
+    const int64_t r1 = min(rows, r0 + slab_rows);
+    double s0 = 0.0, s1 = 0.0;
+    for (int64_t r = r0; r < r1; ++r) {
+        const T* p = X + r * ldx + c;
+        const float x0 = load_as_float<T>(p, 0);
+        const float x1 = (c + 1 < n) ? load_as_float<T>(p, 1) : 0.f;
+        s0 += (double)x0 * (double)x0;
+        s1 += (double)x1 * (double)x1;
+    }
+    if (direct) {
+        out[c] += s0;
+        if (c + 1 < n) out[c + 1] += s1;
+    } else {
+        double* o = out + (int64_t)blockIdx.y * n;
+        o[c] = s0;
+        if (c + 1 < n) o[c + 1] = s1;
+    }
+}
+
+__global__ void reduce_slabs_kernel(double* d, const double* part, int nslab, int64_t n) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    double v = d[c];
+    for (int s = 0; s < nslab; ++s) v += part[(int64_t)s * n + c];
+    d[c] = v;
+}
+
+constexpr int64_t SLAB_ROWS = 2048;
+constexpr int MAX_SLABS = 256;
+constexpr int64_t CHUNK_ROWS_MAX = 65536;   // calibration rows per transposed chunk
+
+struct XtxPlan {
+    int bm, T, nsplit;
+    int64_t chunk;        // rows per transposed chunk (multiple of 64)
+    int nslab;
+    int64_t slab_rows;
+};
+
+size_t plan_bytes(const XtxPlan& p, int64_t n) {
+    Sizer z;
+    if (p.nslab > 1) z.take<double>((size_t)p.nslab * n);
+    z.take<uint16_t>((size_t)n * p.chunk);
+    if (p.nsplit > 1) z.take<float>((size_t)p.nsplit * n * n);
+    return z.bytes();
+}
+
+XtxPlan plan_xtx(int64_t n, int64_t rows) {
+    XtxPlan p;
+    p.bm = (n >= 2048) ? 256 : 128;
+    p.T = (int)cdiv(n, p.bm);
+    p.chunk = std::min<int64_t>(CHUNK_ROWS_MAX, cdiv(std::max<int64_t>(rows, 1), 64) * 64);
+    const int64_t ntiles = (int64_t)p.T * (p.T + 1) / 2;
+    int s = 1;
+    while (ntiles * s < 1024 && p.chunk / (2 * s) >= 4096 && s < 16) s *= 2;
+    p.nsplit = s;
+    p.slab_rows = std::max<int64_t>(SLAB_ROWS, cdiv(cdiv(rows, MAX_SLABS), 64) * 64);
+    p.nslab = (int)std::max<int64_t>(1, cdiv(rows, p.slab_rows));
+    return p;
+}
+
+}  // namespace
+
+size_t xtx_workspace_bytes(int64_t n, int64_t rows) { return plan_bytes(plan_xtx(n, rows), n); }
+
+int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64_t rows,
+               int64_t ldx, void* ws, size_t ws_bytes, hipStream_t st) {
+    if (rows == 0) return PTQ_OK;
+    XtxPlan p = plan_xtx(n, rows);
+    if (x_dtype == PTQ_BF16 && plan_bytes(p, n) > ws_bytes) {
+        set_error("hessian_accumulate: workspace of %zu bytes, %zu needed", ws_bytes, plan_bytes(p, n));
+        return PTQ_EWORKSPACE;
+    }
+    Arena ar(ws, ws_bytes);
+    double* dpart = (p.nslab > 1 && ws) ? ar.take<double>((size_t)p.nslab * n) : nullptr;
+    if (!dpart) { p.nslab = 1; p.slab_rows = rows; }
+
+    if (d) {
+        dim3 grid((unsigned)cdiv(cdiv(n, 2), 256), (unsigned)p.nslab);
+        if (x_dtype == PTQ_BF16)
+            hipLaunchKernelGGL(colsumsq_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)X, ldx,
+                               rows, n, p.slab_rows, p.nslab > 1 ? dpart : d, p.nslab > 1 ? 0 : 1);
+        else
+            hipLaunchKernelGGL(colsumsq_kernel<float>, grid, dim3(256), 0, st, (const float*)X, ldx, rows,
+                               n, p.slab_rows, p.nslab > 1 ? dpart : d, p.nslab > 1 ? 0 : 1);
+        PTQ_LAUNCH_CHECK();
+        if (p.nslab > 1) {
+            hipLaunchKernelGGL(reduce_slabs_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, d, dpart,
+                               p.nslab, n);
+            PTQ_LAUNCH_CHECK();
+        }
+    }
+
+    if (x_dtype == PTQ_F32) {
+        // fp32 calibration inputs: fp32 MFMA GEMM on the upper tiles, then mirror
+        GemmArgs g{};
+        g.M = n; g.N = n; g.K = rows;
+        g.A = (const float*)X; g.lda = ldx; g.layout_a = A_KM;
+        g.B = (const float*)X; g.ldb = ldx; g.layout_b = B_KN;
+        g.C = H; g.ldc = n; g.alpha = 1.f; g.beta_one = 1; g.tri = TRI_NONE; g.upper_only = 1;
+        PTQ_TRY(launch_gemm_f32(g, st));
+        hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(1024, 1), dim3(256), 0, st, H, n, (int)n);
+        PTQ_LAUNCH_CHECK();
+        return PTQ_OK;
+    }
+
+    uint16_t* Xt = ar.take<uint16_t>((size_t)n * p.chunk);
+    float* hpart = (p.nsplit > 1) ? ar.take<float>((size_t)p.nsplit * n * n) : nullptr;
+    const int64_t ntiles = (int64_t)p.T * (p.T + 1) / 2;
+    for (int64_t r0 = 0; r0 < rows; r0 += p.chunk) {
+        const int64_t nr = std::min<int64_t>(p.chunk, rows - r0);
+        const int64_t ldt = cdiv(nr, 64) * 64;
+        hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)(ldt / 64)),
+                           dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt);
+        PTQ_LAUNCH_CHECK();
+        const bool last = r0 + p.chunk >= rows;
+        const int ns = (p.nsplit > 1 && nr >= p.nsplit * 4096) ? p.nsplit : 1;
+        const int64_t kper = cdiv(cdiv(ldt, ns), KT) * KT;
+        for (int s = 0; s < ns; ++s) {
+            const int64_t kb = s * kper, ke = std::min<int64_t>(ldt, kb + kper);
+            Bf16GemmArgs g{};
+            g.A1 = Xt + kb; g.B1 = Xt + kb; g.A2 = nullptr; g.B2 = nullptr;
+            g.K1 = std::max<int64_t>(0, ke - kb); g.K2 = 0;
+            g.lda = ldt; g.ldb = ldt; g.M = n; g.N = n; g.b_batch_stride = 0;
+            g.H = (ns > 1) ? hpart + (int64_t)s * n * n : H;
+            g.ldh = n; g.mirror = (ns == 1 && last) ? 1 : 0; g.T = p.T; g.store_not_add = (ns > 1) ? 1 : 0;
+            const unsigned grid = (unsigned)(cdiv(ntiles, NXCD) * NXCD);
+            prof_begin(PROF_XTX_GEMM, st);
+            if (p.bm == 256)
+                hipLaunchKernelGGL((gemm_bf16_nt_kernel<256, EPI_HESSIAN>), dim3(grid), dim3(NTH), 0, st, g, ntiles);
+            else
+                hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, EPI_HESSIAN>), dim3(grid), dim3(NTH), 0, st, g, ntiles);
+            prof_end(PROF_XTX_GEMM, st);
+            PTQ_LAUNCH_CHECK();
+        }
+        if (ns > 1) {
+            // reduce the split partials into H (upper triangle, mirrored)
+            hipLaunchKernelGGL(reduce_partials_kernel, dim3(2048), dim3(256), 0, st, H, hpart, ns, n);
+            PTQ_LAUNCH_CHECK();
+        } else if (last) {
+            hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(64, (unsigned)p.T), dim3(256), 0, st, H, n, p.bm);
+            PTQ_LAUNCH_CHECK();
+        }
+    }
+    if (p.nsplit > 1) {
+        // chunks that ran without splitting left only their upper triangle: mirror all
+        hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(1024, 1), dim3(256), 0, st, H, n, (int)n);
+        PTQ_LAUNCH_CHECK();
+    }
+    return PTQ_OK;
+}
+
+// AWQ error GEMM: partial[z][tile] = sum over the tile of (X (hi_z + lo_z)^T)^2
+int launch_awq_error_gemm(const uint16_t* X, int64_t ldx, int64_t rows, int64_t n, const uint16_t* hi,
+                          const uint16_t* lo, int64_t ldw, int64_t out, int64_t batch_stride, int nbatch,
+                          double* partial, int64_t* ntiles_out, hipStream_t st) {
+    Bf16GemmArgs g{};
+    g.A1 = X; g.B1 = hi; g.A2 = X; g.B2 = lo;
+    g.K1 = n; g.K2 = n; g.lda = ldx; g.ldb = ldw; g.M = rows; g.N = out;
+    g.b_batch_stride = batch_stride;
+    g.tiles_n = cdiv(out, 256);
+    g.ntiles = cdiv(rows, 256) * g.tiles_n;
+    *ntiles_out = g.ntiles;
+    g.partial = partial;
+    const unsigned grid = (unsigned)(cdiv(g.ntiles, NXCD) * NXCD);
+    prof_begin(PROF_AWQ_GEMM, st);
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<256, EPI_SUMSQ>), dim3(grid, (unsigned)nbatch), dim3(NTH), 0, st, g,
+                       g.ntiles);
+    prof_end(PROF_AWQ_GEMM, st);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
+}  // namespace ptq

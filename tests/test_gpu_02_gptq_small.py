@@ -1,0 +1,168 @@
+"""GPU parity of stages 2-3 against the fp64 oracle at sizes the oracle finishes
+in seconds: the tiny layer, ragged shapes, every bit width / group / block
+combination, act-order, and the degenerate cases.
+
+Tolerances (fixed before measuring): U relative Frobenius error <= 1e-4;
+>= 99% of integer codes identical; relative output error within 1% of the
+oracle's; lambda to 1e-12 relative (both sides sum d in fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+from gpu_util import announce, code_match, rel_fro, relative_output_error, to64, zeros_h
+
+pytestmark = pytest.mark.gpu
+
+
+def _hessian(api, Xd, n, gpu):
+    H, d = zeros_h(n, gpu)
+    api.hessian_accumulate(H, d, Xd)
+    return H, d
+
+
+def test_tiny_layer_all_stages(gpu):
+    from post_int4_weight_amd import api
+    cfg = inputs.CONFIGS["tiny"]
+    announce("tiny layer 256x512, fp32, 4-bit g=128")
+    W, X, _ = inputs.layer(cfg, device="cpu")
+    Wd, Xd = W.to(gpu), X.to(gpu)
+    H, d = _hessian(api, Xd, cfg.inp, gpu)
+    res = api.gptq_quantize_layer(Wd, H, d, bits=4, group_size=128, damp=0.01)
+    U, _, lam = api.gptq_inverse_factor(H, d, damp=0.01)
+    torch.cuda.synchronize()
+
+    H0, d0 = oracle.proxy_hessian(to64(X))
+    ref = oracle.gptq_layer(to64(W), H0, d0, bits=4, g=128, damp=0.01)
+    assert rel_fro(H.cpu().double().numpy(), H0) <= 1e-5
+    assert abs(lam - ref["lambda"]) <= 1e-12 * ref["lambda"]
+    assert abs(res["stats"]["lambda"] - ref["lambda"]) <= 1e-12 * ref["lambda"]
+    assert rel_fro(U.cpu().double().numpy(), ref["U"]) <= 1e-4
+    codes = res["codes"].cpu().numpy()
+    assert code_match(codes, ref["codes"]) >= 0.99
+    assert codes.min() >= -8 and codes.max() <= 7
+    scales = res["scales"].cpu().double().numpy()
+    assert np.allclose(scales[:, 0], ref["scales"][:, 0], rtol=1e-6)      # first group: untouched W
+    assert rel_fro(scales, ref["scales"]) <= 1e-4
+    g_idx = res["g_idx"].cpu().numpy()
+    assert np.array_equal(g_idx, ref["g_idx"])
+    What = oracle.dequantize(codes, scales, g_idx)
+    e_gpu = relative_output_error(H0, to64(W), What)
+    e_ref = relative_output_error(H0, to64(W), ref["What"])
+    assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
+    # stats: sum err^2 = tr(dW H dW^T) (damped H) and the free objective
+    Hd, _ = oracle.damped(H0, 0.01)
+    dW = to64(W) - What
+    assert abs(res["stats"]["sum_err2"] - float(np.sum((dW @ Hd) * dW))) <= 1e-3 * res["stats"]["sum_err2"]
+    assert abs(res["stats"]["dW_fro2"] - float(np.sum(dW * dW))) <= 1e-6 * res["stats"]["dW_fro2"]
+    obj = float(np.sum((dW @ H0) * dW))
+    assert abs(res["stats"]["objective"] - obj) <= 1e-3 * obj
+
+
+def test_columns_stage_alone_with_oracle_U(gpu):
+    """Stage 3 given the oracle's own U (fp32-rounded): isolates the loop."""
+    from post_int4_weight_amd import api
+    announce("column loop with oracle U, 300x1024, g=64 block=128")
+    W, X = inputs.custom(300, 1024, 4096, seed=21, dtype="f32")
+    H0, d0 = oracle.proxy_hessian(to64(X))
+    ref = oracle.gptq_layer(to64(W), H0, d0, bits=4, g=64, damp=0.01)
+    Ud = torch.tensor(ref["U"], dtype=torch.float32, device=gpu)
+    codes, scales, g_idx, stats = api.gptq_quantize_columns(W.to(gpu), Ud, None, bits=4, group_size=64,
+                                                            block_size=128)
+    torch.cuda.synchronize()
+    assert code_match(codes.cpu().numpy(), ref["codes"]) >= 0.999
+    assert rel_fro(scales.cpu().double().numpy(), ref["scales"]) <= 1e-5
+    assert abs(stats[0] - ref["sum_err2"]) <= 1e-4 * ref["sum_err2"]
+
+
+@pytest.mark.parametrize("out,n,rows,bits,g,block,act,dtype", [
+    (100, 520, 1000, 4, 128, 128, False, "bf16"),     # ragged last block and group
+    (100, 520, 1000, 4, 128, 128, True, "bf16"),
+    (64, 384, 800, 3, 64, 128, False, "f32"),         # two groups per block
+    (64, 384, 800, 2, 32, 64, True, "f32"),
+    (33, 640, 1500, 8, 256, 128, False, "bf16"),      # groups spanning two blocks
+    (33, 640, 1500, 4, 256, 64, True, "bf16"),
+    (17, 256, 512, 4, 32, 32, False, "f32"),
+    (5, 1040, 3000, 3, 128, 128, True, "bf16"),       # several U recursion levels, ragged
+])
+def test_layer_shapes(gpu, out, n, rows, bits, g, block, act, dtype):
+    from post_int4_weight_amd import api
+    announce(f"layer out={out} n={n} rows={rows} bits={bits} g={g} block={block} act={act} {dtype}")
+    W, X = inputs.custom(out, n, rows, seed=out + n + bits, dtype=dtype)
+    Wd, Xd = W.to(gpu), X.to(gpu)
+    H, d = _hessian(api, Xd, n, gpu)
+    res = api.gptq_quantize_layer(Wd, H, d, bits=bits, group_size=g, damp=0.01, act_order=act, block_size=block)
+    U, perm, _ = api.gptq_inverse_factor(H, d, damp=0.01, act_order=act)
+    torch.cuda.synchronize()
+    H0, d0 = oracle.proxy_hessian(to64(X))
+    ref = oracle.gptq_layer(to64(W), H0, d0, bits=bits, g=g, damp=0.01, act_order=act)
+    if act:
+        assert np.array_equal(res["perm"].cpu().numpy(), ref["perm"])
+        assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    assert rel_fro(U.cpu().double().numpy(), ref["U"]) <= 1e-4
+    codes = res["codes"].cpu().numpy()
+    q = 2 ** (bits - 1) - 1
+    assert codes.min() >= -q - 1 and codes.max() <= q
+    assert code_match(codes, ref["codes"]) >= 0.99
+    assert np.array_equal(res["g_idx"].cpu().numpy(), ref["g_idx"])
+    What = oracle.dequantize(codes, res["scales"].cpu().double().numpy(), ref["g_idx"])
+    e_gpu = relative_output_error(H0, to64(W), What)
+    e_ref = relative_output_error(H0, to64(W), ref["What"])
+    assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
+
+
+def test_identity_hessian_is_rtn(gpu):
+    """H a multiple of I: U is diagonal, no feedback, GPTQ = RTN exactly."""
+    from post_int4_weight_amd import api
+    announce("H = c I reduces to RTN")
+    out, n = 64, 512
+    W, _ = inputs.custom(out, n, 8, seed=5, dtype="f32")
+    H = torch.eye(n, device=gpu) * 3.7
+    res = api.gptq_quantize_layer(W.to(gpu), H, None, bits=4, group_size=128, damp=0.01)
+    torch.cuda.synchronize()
+    codes, scales = oracle.rtn(to64(W), 4, 128)
+    assert np.array_equal(res["codes"].cpu().numpy(), codes)
+    assert np.allclose(res["scales"].cpu().double().numpy(), scales, rtol=1e-6)
+
+
+def test_empty_out_and_zero_rows(gpu):
+    from post_int4_weight_amd import api
+    announce("out = 0")
+    n = 256
+    _, X = inputs.custom(4, n, 600, seed=1, dtype="f32")
+    H, d = _hessian(api, X.to(gpu), n, gpu)
+    W = torch.zeros(0, n, device=gpu)
+    res = api.gptq_quantize_layer(W, H, d)
+    torch.cuda.synchronize()
+    assert res["stats"]["sum_err2"] == 0.0
+    assert np.array_equal(res["g_idx"].cpu().numpy(), np.arange(n) // 128)
+    # a zero weight row: scale 0, codes 0, no error
+    W = torch.zeros(3, n, device=gpu)
+    W[1] = 1.0
+    res = api.gptq_quantize_layer(W, H, d)
+    torch.cuda.synchronize()
+    c = res["codes"].cpu().numpy()
+    assert np.all(c[0] == 0) and np.all(c[2] == 0)
+    assert np.all(res["scales"].cpu().numpy()[0] == 0)
+
+
+def test_not_positive_definite_and_nonfinite(gpu):
+    from post_int4_weight_amd import api
+    announce("ENOTPD / ENONFINITE")
+    n = 128
+    _, X = inputs.custom(4, n, 600, seed=2, dtype="f32")
+    X[:, 17] = 0.0                                         # a dead channel
+    H, d = _hessian(api, X.to(gpu), n, gpu)
+    with pytest.raises(api.PTQError) as ei:
+        api.gptq_inverse_factor(H, d, damp=0.0)
+    assert ei.value.name == "PTQ_ENOTPD"
+    U, _, lam = api.gptq_inverse_factor(H, d, damp=0.01)  # damping fixes it
+    torch.cuda.synchronize()
+    assert lam > 0 and torch.isfinite(U).all()
+    H2 = H.clone()
+    H2[5, 5] = float("nan")
+    with pytest.raises(api.PTQError) as ei:
+        api.gptq_inverse_factor(H2, None, damp=0.01)
+    assert ei.value.name in ("PTQ_ENONFINITE", "PTQ_ENOTPD")

@@ -1,0 +1,125 @@
+"""GPU checks at full size on the Llama-70B-shaped down_proj — W [8192, 28672]
+bf16, X [262144, 28672] bf16 (60% zeros), 4- and 3-bit, g = 128, damp = 0.01,
+block 128: the workload and launch configuration that bench.py times.
+
+The fp64 oracle cannot factor a 28672^2 Hessian in seconds, so it is checked
+on what it can compute exactly:
+  * H on diagonal and off-diagonal blocks from the matching columns of X;
+  * lambda from all of X (sum of squares streamed in fp64);
+  * U's trailing 512 x 512 block, which depends only on H's trailing block
+    (H = R R^T with R upper: the trailing block of R, hence of U = R^-1,
+    is the reversed Cholesky of H's trailing block);
+  * the first group's scales (the loop has not touched those columns yet);
+and on properties that hold at any size, evaluated in fp64 on the device:
+  * U H_d U^T = I on sampled rows;
+  * the loop identity sum err^2 = tr(dW H_d dW^T) over all rows;
+  * every code on the grid; calibration error below RTN's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+from gpu_util import announce, rel_fro, to64, zeros_h
+
+pytestmark = pytest.mark.gpu
+
+TRAIL = 512
+
+
+@pytest.fixture(scope="module")
+def down_proj(gpu):
+    from post_int4_weight_amd import api
+    cfg = inputs.CONFIGS["llama70b_down_proj"]
+    announce("down_proj 8192x28672: generate X (15 GB) + hessian")
+    W, X, _ = inputs.layer(cfg, device=gpu)
+    H, d = zeros_h(cfg.inp, gpu)
+    api.hessian_accumulate(H, d, X)
+    torch.cuda.synchronize()
+    # oracle lambda: fp64 sum of squares of every entry of X, streamed
+    d0 = np.zeros(cfg.inp)
+    for r0 in range(0, cfg.rows, 8192):
+        xc = X[r0:r0 + 8192].cpu().float().numpy().astype(np.float64)
+        d0 += np.sum(xc * xc, axis=0)
+    return cfg, W, X, H, d, d0
+
+
+def test_hessian_blocks(down_proj):
+    cfg, W, X, H, d, d0 = down_proj
+    n = cfg.inp
+    announce("down_proj hessian blocks")
+    assert np.max(np.abs(d.cpu().numpy() - d0) / np.maximum(d0, 1e-300)) <= 1e-12
+    for c0 in (0, 14336 - 256, n - TRAIL):
+        cols = list(range(c0, c0 + TRAIL))
+        H0b, _ = oracle.proxy_hessian(to64(X[:, cols].cpu()), chunk_rows=16384)
+        Hb = H[c0:c0 + TRAIL, c0:c0 + TRAIL].cpu().double().numpy()
+        assert rel_fro(Hb, H0b) <= 1e-5
+    # an off-diagonal block, error measured against sqrt(H_ii H_jj)
+    ci = list(range(1000, 1256))
+    cj = list(range(n - 3000, n - 2744))
+    xi = to64(X[:, ci].cpu())
+    xj = to64(X[:, cj].cpu())
+    ref = xi.T @ xj
+    got = H[ci][:, cj].cpu().double().numpy()
+    scale = np.sqrt(np.outer(d0[ci], d0[cj]))
+    assert np.max(np.abs(got - ref) / scale) <= 1e-5
+    Hg_sym = H[:2048, :2048]
+    assert torch.equal(Hg_sym, Hg_sym.T)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_gptq_fullsize(down_proj, bits):
+    from post_int4_weight_amd import api
+    cfg, W, X, H, d, d0 = down_proj
+    n, out = cfg.inp, cfg.out
+    announce(f"down_proj gptq bits={bits}")
+    res = api.gptq_quantize_layer(W, H, d, bits=bits, group_size=128, damp=0.01, act_order=False, block_size=128)
+    U, _, lam = api.gptq_inverse_factor(H, d, damp=0.01)
+    torch.cuda.synchronize()
+    lam0 = 0.01 * float(np.mean(d0))
+    assert abs(lam - lam0) <= 1e-12 * lam0
+    assert abs(res["stats"]["lambda"] - lam0) <= 1e-12 * lam0
+
+    # U's trailing block against the oracle
+    cols = list(range(n - TRAIL, n))
+    H0t, _ = oracle.proxy_hessian(to64(X[:, cols].cpu()), chunk_rows=16384)
+    Ut = oracle.inverse_upper_factor(H0t + lam0 * np.eye(TRAIL))
+    assert rel_fro(U[n - TRAIL:, n - TRAIL:].cpu().double().numpy(), Ut) <= 1e-4
+
+    # U H_d U^T = I on sampled rows (fp64 on the device)
+    Hd = H.double()
+    Hd.diagonal().add_(lam)
+    U64 = U.double()
+    assert torch.equal(U64, torch.triu(U64))
+    for i in (0, 1, 4097, 14000, n - 129, n - 1):
+        w = U64 @ (Hd @ U64[i])
+        e = torch.zeros_like(w)
+        e[i] = 1.0
+        assert float((w - e).abs().max()) <= 1e-3, i
+    del U64
+
+    codes = res["codes"]
+    q = 2 ** (bits - 1) - 1
+    assert int(codes.min()) >= -q - 1 and int(codes.max()) <= q
+    scales = res["scales"]
+    Wf = W.float()
+    first = (Wf[:, :128].abs().amax(1).double() / q)
+    assert torch.allclose(scales[:, 0].double(), first, rtol=1e-6, atol=0)
+
+    # loop identity: sum err^2 = tr(dW H_d dW^T), and the objective identity
+    g_idx = res["g_idx"].long()
+    What = codes.double() * scales.double()[:, g_idx]
+    dW = W.double() - What
+    del What
+    quad_d = float(((dW @ Hd) * dW).sum())
+    assert abs(res["stats"]["sum_err2"] - quad_d) <= 1e-3 * quad_d
+    Hd.diagonal().sub_(lam)
+    obj = float(((dW @ Hd) * dW).sum())
+    assert abs(res["stats"]["objective"] - obj) <= 2e-3 * obj
+    # calibration error below plain RTN's (the loop's purpose)
+    Wrtn_codes, Wrtn_scales = oracle.rtn(to64(W.cpu()), bits, 128)
+    Wrtn = torch.tensor(oracle.dequantize(Wrtn_codes, Wrtn_scales, np.arange(n) // 128), device=W.device)
+    dR = W.double() - Wrtn
+    obj_rtn = float(((dR @ Hd) * dR).sum())
+    assert obj < obj_rtn, (obj, obj_rtn)

@@ -1,0 +1,53 @@
+"""GPU parity of AWQ's alpha grid search against the fp64 oracle.
+
+Criteria: the same alpha is chosen (or, if not, the oracle's own error at the
+GPU's alpha is within 1e-4 relative of its minimum: a near-tie), every
+per-alpha error within 1e-4 relative of the oracle's, and >= 99% of the codes
+of W diag(s) identical at the chosen alpha.
+"""
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+from gpu_util import announce, code_match, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(res, ref, alphas):
+    errs = np.array(res["errors"])
+    assert np.all(np.abs(errs - ref["errors"]) <= 1e-4 * ref["errors"]), (errs, ref["errors"])
+    ia = alphas.index(res["alpha"]) if res["alpha"] in alphas else int(np.argmin(np.abs(np.array(alphas) - res["alpha"])))
+    assert ia == ref["index"] or ref["errors"][ia] <= (1 + 1e-4) * ref["errors"][ref["index"]]
+    if ia == ref["index"]:
+        assert code_match(res["codes"].cpu().numpy(), ref["codes"]) >= 0.99
+        assert np.allclose(res["s"].cpu().double().numpy(), ref["s"], rtol=1e-6)
+
+
+@pytest.mark.parametrize("dtype,out,n,rows", [("f32", 256, 512, 2048), ("bf16", 300, 1024, 1000),
+                                              ("bf16", 128, 520, 700)])
+def test_awq_small(gpu, dtype, out, n, rows):
+    from post_int4_weight_amd import api
+    announce(f"awq {dtype} out={out} n={n} rows={rows}")
+    W, X = inputs.custom(out, n, rows, seed=out + rows, dtype=dtype)
+    alphas = list(inputs.AWQ_ALPHAS)
+    res = api.awq_search_alpha(W.to(gpu), X.to(gpu), alphas, bits=4, group_size=128)
+    torch.cuda.synchronize()
+    ref = oracle.awq_search(to64(W), to64(X), alphas, bits=4, g=128)
+    _compare(res, ref, alphas)
+
+
+def test_awq_llama70b_q_proj(gpu):
+    """The pages-shaped AWQ case: config llama70b_qkv_proj's W and its first
+    4096 calibration rows, 20 alphas in {0, 0.05, ..., 0.95}."""
+    from post_int4_weight_amd import api
+    cfg = inputs.CONFIGS["llama70b_qkv_proj"]
+    announce("awq llama70b q_proj 8192x8192, 4096 rows, 20 alphas")
+    W, X, _ = inputs.layer(cfg, device=gpu, rows=inputs.AWQ_CAL_ROWS)
+    alphas = list(inputs.AWQ_ALPHAS)
+    res = api.awq_search_alpha(W, X, alphas, bits=4, group_size=128)
+    torch.cuda.synchronize()
+    ref = oracle.awq_search(to64(W.cpu()), to64(X.cpu()), alphas, bits=4, g=128)
+    _compare(res, ref, alphas)
