@@ -63,18 +63,42 @@ __global__ void mean_abs_finish_kernel(const double* part, int nslab, int64_t n,
     for (int64_t c = threadIdx.x; c < n; c += 256) m[c] = fmax(m[c], floor_v);
 }
 
-// s[a][j] = m_j ^ alpha_a (fp64 pow, stored fp32)
-__global__ void scales_kernel(const double* m, int64_t n, const float* alphas, int na, float* s) {
+// s[a][j] = m_j ^ alpha_a in fp64 (the rounding decisions below are taken in
+// fp64, the precision of the pages' NumPy reference)
+__global__ void scales_kernel(const double* m, int64_t n, const float* alphas, int na, double* s) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int a = blockIdx.y;
-    if (c < n && a < na) s[(int64_t)a * n + c] = (float)pow(m[c], (double)alphas[a]);
+    if (c < n && a < na) s[(int64_t)a * n + c] = pow(m[c], (double)alphas[a]);
+}
+
+__global__ void s_to_f32_kernel(const double* s64, int64_t n, float* s) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c < n) s[c] = (float)s64[c];
+}
+
+// RTN of one group of W diag(s), decided in fp64. Returns the fp64 scale;
+// emit(c, w, q) is called per column with the fp64 code.
+template <typename T, typename F>
+__device__ __forceinline__ double awq_group(const T* W, int64_t row_off, int64_t c0, int64_t c1, const double* s,
+                                            double qmax, F emit) {
+    double mx = 0.0;
+    for (int64_t c = c0; c < c1; ++c) mx = fmax(mx, fabs((double)load_as_float<T>(W, row_off + c) * s[c]));
+    const double scale = mx / qmax;
+    for (int64_t c = c0; c < c1; ++c) {
+        const double w = (double)load_as_float<T>(W, row_off + c);
+        double q = 0.0;
+        if (scale > 0.0) q = fmin(fmax(rint((w * s[c]) / scale), -qmax - 1.0), qmax);
+        emit(c, w, q, scale);
+    }
+    return scale;
 }
 
 // One thread per (alpha, row, group): RTN of the scaled group, then either the
-// hi/lo split of dW (search) or the codes/scales of W diag(s) (final).
+// hi/lo split of dW = W - Q(W diag s) diag(s)^-1 (search) or the codes and
+// scales of W diag(s) (final).
 template <typename T>
 __global__ void awq_quant_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n, int g, float qmax,
-                                 const float* __restrict__ s_all, int na, uint16_t* __restrict__ hi,
+                                 const double* __restrict__ s_all, int na, uint16_t* __restrict__ hi,
                                  uint16_t* __restrict__ lo, int8_t* __restrict__ codes, float* __restrict__ scales,
                                  int64_t ngroups) {
     const int64_t per_a = out * ngroups;
@@ -83,47 +107,35 @@ __global__ void awq_quant_kernel(const T* __restrict__ W, int64_t ldw, int64_t o
     const int a = (int)(id / per_a);
     const int64_t rem = id % per_a;
     const int64_t r = rem / ngroups, grp = rem % ngroups;
-    const float* s = s_all + (int64_t)a * n;
+    const double* s = s_all + (int64_t)a * n;
     const int64_t c0 = grp * g, c1 = std::min<int64_t>(n, c0 + g);
-    float mx = 0.f;
-    for (int64_t c = c0; c < c1; ++c) mx = fmaxf(mx, fabsf(load_as_float<T>(W, r * ldw + c) * s[c]));
-    const float scale = mx / qmax;
-    if (scales) scales[r * ngroups + grp] = scale;
-    for (int64_t c = c0; c < c1; ++c) {
-        const float w = load_as_float<T>(W, r * ldw + c);
-        const float ws = w * s[c];
-        float q = 0.f;
-        if (scale > 0.f) q = fminf(fmaxf(rintf(ws / scale), -qmax - 1.f), qmax);
+    const double scale = awq_group<T>(W, r * ldw, c0, c1, s, (double)qmax, [&](int64_t c, double w, double q,
+                                                                                 double sc) {
         if (codes) {
             codes[r * n + c] = (int8_t)(int)q;
         } else {
-            const float dw = w - (q * scale) / s[c];
+            const float dw = (float)(w - (q * sc) / s[c]);
             const uint16_t h = float_to_bf16_bits(dw);
             const float l = dw - bf16_bits_to_float(h);
             const int64_t o = (int64_t)a * out * n + r * n + c;
             hi[o] = h;
             lo[o] = float_to_bf16_bits(l);
         }
-    }
+    });
+    if (scales) scales[r * ngroups + grp] = (float)scale;
 }
 
 // fp32 path: dW as fp32 for one alpha (no split)
 template <typename T>
 __global__ void awq_dw_f32_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n, int g, float qmax,
-                                  const float* __restrict__ s, float* __restrict__ dW, int64_t ngroups) {
+                                  const double* __restrict__ s, float* __restrict__ dW, int64_t ngroups) {
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= out * ngroups) return;
     const int64_t r = id / ngroups, grp = id % ngroups;
     const int64_t c0 = grp * g, c1 = std::min<int64_t>(n, c0 + g);
-    float mx = 0.f;
-    for (int64_t c = c0; c < c1; ++c) mx = fmaxf(mx, fabsf(load_as_float<T>(W, r * ldw + c) * s[c]));
-    const float scale = mx / qmax;
-    for (int64_t c = c0; c < c1; ++c) {
-        const float w = load_as_float<T>(W, r * ldw + c);
-        float q = 0.f;
-        if (scale > 0.f) q = fminf(fmaxf(rintf((w * s[c]) / scale), -qmax - 1.f), qmax);
-        dW[r * n + c] = w - (q * scale) / s[c];
-    }
+    awq_group<T>(W, r * ldw, c0, c1, s, (double)qmax, [&](int64_t c, double w, double q, double sc) {
+        dW[r * n + c] = (float)(w - (q * sc) / s[c]);
+    });
 }
 
 // sum of squares of a dense buffer (fp64, one workgroup per slice, fixed order)
@@ -177,7 +189,7 @@ size_t awq_ws_bytes(int64_t out, int64_t n, int64_t rows, int n_alpha) {
     Sizer z;
     z.take<double>((size_t)l.nslab * n);        // column |x| partials
     z.take<double>((size_t)n);                  // m
-    z.take<float>((size_t)n_alpha * n);         // s per alpha
+    z.take<double>((size_t)n_alpha * n);        // s per alpha (fp64)
     z.take<float>((size_t)n_alpha);             // alphas (device copy)
     z.take<double>((size_t)n_alpha);            // err
     // bf16 path: hi + lo for every alpha, one partial per tile and alpha
@@ -201,7 +213,7 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
     Arena ar(ws, ws_bytes);
     double* cpart = ar.take<double>((size_t)l.nslab * n);
     double* m = ar.take<double>((size_t)n);
-    float* s_all = ar.take<float>((size_t)n_alpha * n);
+    double* s_all = ar.take<double>((size_t)n_alpha * n);
     float* al_dev = ar.take<float>((size_t)n_alpha);
     double* err = ar.take<double>((size_t)n_alpha);
     const int64_t ngroups = cdiv(n, g);
@@ -295,8 +307,11 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
     if (alpha_best) *alpha_best = alphas[best];
 
     // final codes / scales of W diag(s) at alpha*
-    const float* sb = s_all + (int64_t)best * n;
-    if (s_out) PTQ_HIP(hipMemcpyAsync(s_out, sb, sizeof(float) * n, hipMemcpyDeviceToDevice, st));
+    const double* sb = s_all + (int64_t)best * n;
+    if (s_out) {
+        hipLaunchKernelGGL(s_to_f32_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, sb, n, s_out);
+        PTQ_LAUNCH_CHECK();
+    }
     const int64_t nth = out * ngroups;
     if (w_dtype == PTQ_BF16)
         hipLaunchKernelGGL(awq_quant_kernel<uint16_t>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st,

@@ -15,10 +15,12 @@
 //
 // Tile 256 x 256 (or 128 x 128) per workgroup of 256 threads, 4 wave64s in
 // 2 x 2, each wave a (BM/2)^2 block of 32x32 MFMA accumulators. K is staged
-// 32 at a time through LDS, double buffered: 16-byte chunks go straight from
-// global memory into 64-byte LDS rows whose chunk index is XOR-swizzled by
-// (row >> 2) & 3, so both the staging writes and the ds_read_b128 operand
-// fetches (32 rows x 2 chunks per wave) are free of bank conflicts.
+// 64 at a time through LDS (dynamic, double buffered): 16-byte chunks go
+// from global memory through registers into 128-byte LDS rows whose chunk
+// index is XOR-swizzled by (row >> 1) & 7, so both the staging writes (2 rows
+// x 8 chunks per 16 lanes) and the ds_read_b128 operand fetches (16 rows x 1
+// chunk) are free of bank conflicts. A stage is 64 MFMAs per wave, long enough
+// to cover the latency of the next stage's global loads.
 //
 // Workgroup order is XCD-aware: blockIdx b runs on XCD b % 8, so logical work
 // items are handed out in contiguous runs per XCD; Hessian tiles are ordered
@@ -31,14 +33,19 @@
 namespace ptq {
 namespace {
 
-constexpr int KT = 32;
+constexpr int KT = 64;              // contraction depth per LDS stage
+constexpr int ROWB = KT * 2;        // bytes per staged row
+constexpr int CPR = ROWB / 16;      // 16-byte chunks per staged row
 constexpr int NTH = 256;
 constexpr int BAND = 4;
 constexpr int NXCD = 8;
 
 enum { EPI_HESSIAN = 0, EPI_SUMSQ = 1 };
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + 16 * (c ^ ((r >> 1) & 7)); }
+
+template <int BMX>
+constexpr int smem_bytes() { return 4 * BMX * ROWB; }   // A and B, two stages each
 
 // Upper-triangle tile at position L of the band order (T tile-rows).
 __device__ __forceinline__ void band_tile(int64_t L, int T, int& ti, int& tj) {
@@ -81,25 +88,30 @@ struct Bf16GemmArgs {
 };
 
 template <int BMX>
-struct Smem {
-    alignas(16) unsigned char a[2][BMX * 64];
-    alignas(16) unsigned char b[2][BMX * 64];
-};
-
-template <int BMX>
 struct Stg {
-    uint4 a[BMX / 64];
-    uint4 b[BMX / 64];
+    uint4 a[BMX * CPR / NTH];
+    uint4 b[BMX * CPR / NTH];
 };
 
-// Load this thread's share of a K-slab of one operand panel (rows x0.., k0..k0+31).
-template <int BMX>
-__device__ __forceinline__ void load_panel(uint4 (&v)[BMX / 64], const uint16_t* P, int64_t ld,
+// Load this thread's share of a K-slab of one operand panel (rows x0.., k0..k0+KT-1).
+// GUARD = false: the whole slab is inside the matrix (no bounds checks).
+template <int BMX, bool GUARD>
+__device__ __forceinline__ void load_panel(uint4 (&v)[BMX * CPR / NTH], const uint16_t* P, int64_t ld,
                                            int64_t x0, int64_t X, int64_t k0, int64_t K, int t) {
+    if (!GUARD) {
+        const uint16_t* base = P + x0 * ld + k0;
 #pragma unroll
-    for (int q = 0; q < BMX / 64; ++q) {
-        const int idx = t + NTH * q;          // BMX rows x 4 chunks
-        const int r = idx >> 2, c = idx & 3;
+        for (int q = 0; q < BMX * CPR / NTH; ++q) {
+            const int idx = t + NTH * q;
+            const int r = idx / CPR, c = idx % CPR;
+            v[q] = *(const uint4*)(base + (int64_t)r * ld + 8 * c);
+        }
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < BMX * CPR / NTH; ++q) {
+        const int idx = t + NTH * q;          // BMX rows x CPR chunks
+        const int r = idx / CPR, c = idx % CPR;
         const int64_t row = x0 + r, k = k0 + 8 * c;
         uint4 val = make_uint4(0u, 0u, 0u, 0u);
         if (row < X) {
@@ -118,15 +130,20 @@ __device__ __forceinline__ void load_panel(uint4 (&v)[BMX / 64], const uint16_t*
 }
 
 template <int BMX>
-__device__ __forceinline__ void store_panel(unsigned char* S, const uint4 (&v)[BMX / 64], int t) {
+__device__ __forceinline__ void store_panel(unsigned char* S, const uint4 (&v)[BMX * CPR / NTH], int t) {
 #pragma unroll
-    for (int q = 0; q < BMX / 64; ++q) {
+    for (int q = 0; q < BMX * CPR / NTH; ++q) {
         const int idx = t + NTH * q;
-        const int r = idx >> 2, c = idx & 3;
+        const int r = idx / CPR, c = idx % CPR;
         *(uint4*)(S + swz(r, c)) = v[q];
     }
 }
 
+template <int BMX, int EPI>
+__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[BMX / 64][BMX / 64], int64_t i0,
+                                           int64_t j0, bool diag, int64_t L, unsigned char* smem);
+
+// Register-staged variant: any shape (bounds-checked loads, zero fill).
 template <int BMX, int EPI>
 __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, int64_t nwork) {
     constexpr int WT = BMX / 64;
@@ -149,7 +166,9 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
     const uint16_t* B1 = g.B1 + (int64_t)blockIdx.y * g.b_batch_stride;
     const uint16_t* B2 = g.B2 ? g.B2 + (int64_t)blockIdx.y * g.b_batch_stride : nullptr;
 
-    __shared__ Smem<BMX> sm;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    auto smA = [&](int buf) { return smem + buf * (BMX * ROWB); };
+    auto smB = [&](int buf) { return smem + (2 + buf) * (BMX * ROWB); };
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = (wave >> 1) * (BMX / 2), wn = (wave & 1) * (BMX / 2);
@@ -166,89 +185,292 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
     const int64_t n1 = cdiv(g.K1, KT), n2 = cdiv(g.K2, KT);
     const int64_t nst = n1 + n2;
     Stg<BMX> rg;
+    const bool rows_full = (i0 + BMX <= g.M) && (j0 + BMX <= g.N);
     auto gload = [&](int64_t s) {
-        if (s < n1) {
-            load_panel<BMX>(rg.a, g.A1, g.lda, i0, g.M, s * KT, g.K1, t);
-            load_panel<BMX>(rg.b, B1, g.ldb, j0, g.N, s * KT, g.K1, t);
+        const bool seg1 = s < n1;
+        const uint16_t* A = seg1 ? g.A1 : g.A2;
+        const uint16_t* B = seg1 ? B1 : B2;
+        const int64_t K = seg1 ? g.K1 : g.K2;
+        const int64_t k0 = (seg1 ? s : s - n1) * KT;
+        if (rows_full && k0 + KT <= K) {
+            load_panel<BMX, false>(rg.a, A, g.lda, i0, g.M, k0, K, t);
+            load_panel<BMX, false>(rg.b, B, g.ldb, j0, g.N, k0, K, t);
         } else {
-            load_panel<BMX>(rg.a, g.A2, g.lda, i0, g.M, (s - n1) * KT, g.K2, t);
-            load_panel<BMX>(rg.b, B2, g.ldb, j0, g.N, (s - n1) * KT, g.K2, t);
+            load_panel<BMX, true>(rg.a, A, g.lda, i0, g.M, k0, K, t);
+            load_panel<BMX, true>(rg.b, B, g.ldb, j0, g.N, k0, K, t);
         }
     };
 
     if (nst > 0) {
         gload(0);
-        store_panel<BMX>(sm.a[0], rg.a, t);
-        store_panel<BMX>(sm.b[0], rg.b, t);
+        store_panel<BMX>(smA(0), rg.a, t);
+        store_panel<BMX>(smB(0), rg.b, t);
     }
     __syncthreads();
     for (int64_t s = 0; s < nst; ++s) {
         const int cur = (int)(s & 1);
         const bool more = s + 1 < nst;
         if (more) gload(s + 1);
-        const unsigned char* As = sm.a[cur];
-        const unsigned char* Bs = sm.b[cur];
+        const unsigned char* As = smA(cur);
+        const unsigned char* Bs = smB(cur);
+        // operand fragments double-buffered in registers: the LDS reads for
+        // sub-step kk+1 are in flight while the MFMAs of sub-step kk run
+        bf16x8 av[2][WT], bv[2][WT];
+        auto frags = [&](int kk, int slot) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 av[WT], bv[WT];
+            for (int a = 0; a < WT; ++a) av[slot][a] = *(const bf16x8*)(As + swz(wm + 32 * a + li, 2 * kk + lh));
 #pragma unroll
-            for (int a = 0; a < WT; ++a) av[a] = *(const bf16x8*)(As + swz(wm + 32 * a + li, 2 * kk + lh));
+            for (int b = 0; b < WT; ++b) bv[slot][b] = *(const bf16x8*)(Bs + swz(wn + 32 * b + li, 2 * kk + lh));
+        };
+        frags(0, 0);
 #pragma unroll
-            for (int b = 0; b < WT; ++b) bv[b] = *(const bf16x8*)(Bs + swz(wn + 32 * b + li, 2 * kk + lh));
+        for (int kk = 0; kk < KT / 16; ++kk) {
+            const int slot = kk & 1;
+            if (kk + 1 < KT / 16) frags(kk + 1, slot ^ 1);
 #pragma unroll
             for (int a = 0; a < WT; ++a)
 #pragma unroll
                 for (int b = 0; b < WT; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[slot][a], bv[slot][b], acc[a][b], 0, 0, 0);
         }
         if (more) {
-            store_panel<BMX>(sm.a[cur ^ 1], rg.a, t);
-            store_panel<BMX>(sm.b[cur ^ 1], rg.b, t);
+            store_panel<BMX>(smA(cur ^ 1), rg.a, t);
+            store_panel<BMX>(smB(cur ^ 1), rg.b, t);
         }
         __syncthreads();
     }
 
-    // 32x32 accumulator layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    store_tile<BMX, EPI>(g, acc, i0, j0, diag, L, smem);
+}
+
+// Tile epilogue. 32x32 accumulator layout: lane l, register r -> row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32. `smem` is free scratch by now.
+template <int BMX, int EPI>
+__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[BMX / 64][BMX / 64], int64_t i0,
+                                           int64_t j0, bool diag, int64_t L, unsigned char* smem) {
+    constexpr int WT = BMX / 64;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 1) * (BMX / 2), wn = (wave & 1) * (BMX / 2);
+    const int li = lane & 31, lh = lane >> 5;
     if (EPI == EPI_HESSIAN) {
+        const int mi = (int)std::min<int64_t>(BMX, g.M - i0);   // valid rows / columns of this tile
+        const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
+        float* Ht = g.H + i0 * g.ldh + j0;                      // tile origin
+        float* Hm = g.H + j0 * g.ldh + i0;                      // mirror origin
+        const int ld = (int)g.ldh;
 #pragma unroll
         for (int a = 0; a < WT; ++a)
 #pragma unroll
-            for (int b = 0; b < WT; ++b)
+            for (int b = 0; b < WT; ++b) {
+                const int jj = wn + 32 * b + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t i = i0 + wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const int64_t j = j0 + wn + 32 * b + li;
-                    if (i < g.M && j < g.N) {
-                        float* p = g.H + i * g.ldh + j;
+                    const int ii = wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (ii < mi && jj < nj) {
+                        float* p = Ht + (int64_t)ii * ld + jj;
                         const float v = g.store_not_add ? acc[a][b][r] : (*p + acc[a][b][r]);
                         *p = v;
-                        if (g.mirror && !diag) g.H[j * g.ldh + i] = v;
+                        if (g.mirror && !diag) Hm[(int64_t)jj * ld + ii] = v;
                     }
                 }
+            }
     } else {
+        const int mi = (int)std::min<int64_t>(BMX, g.M - i0);
+        const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
         double s = 0.0;
 #pragma unroll
         for (int a = 0; a < WT; ++a)
 #pragma unroll
             for (int b = 0; b < WT; ++b) {
                 float part = 0.f;
+                const int jj = wn + 32 * b + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t i = i0 + wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const int64_t j = j0 + wn + 32 * b + li;
-                    const float v = (i < g.M && j < g.N) ? acc[a][b][r] : 0.f;
+                    const int ii = wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const float v = (ii < mi && jj < nj) ? acc[a][b][r] : 0.f;
                     part = fmaf(v, v, part);
                 }
                 s += (double)part;
             }
         // wave reduction (fixed order), then across the 4 waves through LDS
+        // (the staging buffers are free after the last barrier)
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-        __shared__ double red[4];
+        double* red = (double*)smem;
         if (lane == 0) red[wave] = s;
         __syncthreads();
         if (t == 0)
             g.partial[(int64_t)blockIdx.y * g.ntiles + L] = ((red[0] + red[1]) + (red[2] + red[3]));
     }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant (K1 and K2 multiples of 32). global_load_lds_dwordx4
+// moves each lane's 16 bytes straight into LDS at base + 16 * lane, so no
+// staging registers and no ds_write are spent; the XOR swizzle is applied on
+// the global side by choosing which chunk each lane fetches. A ring of four
+// 32-deep stages keeps three stages of loads in flight behind the MFMAs.
+// Rows past M (or N) read a clamped valid row: they only feed output rows
+// (columns) that the epilogue discards.
+constexpr int DK = 32;                 // contraction depth per stage
+constexpr int DROWB = DK * 2;          // bytes per staged row
+constexpr int NSTAGE = 4;
+
+template <int BMX>
+constexpr int dsmem_bytes() { return NSTAGE * 2 * BMX * DROWB; }
+
+__device__ __forceinline__ int dswz(int r, int c) { return r * DROWB + 16 * (c ^ ((r >> 2) & 3)); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt at their maxima
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BMX, int EPI>
+__global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g, int64_t nwork) {
+    constexpr int WT = BMX / 64;
+    constexpr int PER = BMX / 64;      // load instructions per wave per panel per stage (BMX*4 chunks / 64 / 4 waves)
+    const int64_t per = (nwork + NXCD - 1) / NXCD;
+    const int64_t L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
+    if (L >= nwork) return;
+
+    int64_t i0, j0;
+    bool diag = false;
+    if (EPI == EPI_HESSIAN) {
+        int ti, tj;
+        band_tile(L, g.T, ti, tj);
+        i0 = (int64_t)ti * BMX;
+        j0 = (int64_t)tj * BMX;
+        diag = (ti == tj);
+    } else {
+        i0 = (L / g.tiles_n) * BMX;
+        j0 = (L % g.tiles_n) * BMX;
+    }
+    const uint16_t* B1 = g.B1 + (int64_t)blockIdx.y * g.b_batch_stride;
+    const uint16_t* B2 = g.B2 ? g.B2 + (int64_t)blockIdx.y * g.b_batch_stride : nullptr;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 1) * (BMX / 2), wn = (wave & 1) * (BMX / 2);
+    const int li = lane & 31, lh = lane >> 5;
+
+    // element offsets (from the operand base) of the chunks this lane moves
+    int64_t offA[PER], offB[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int p = (wave * PER + q) * 64 + lane;      // 16-byte granule of the panel slab
+        const int r = p >> 2;
+        const int c = (p & 3) ^ ((r >> 2) & 3);
+        const int64_t ra = std::min<int64_t>(i0 + r, g.M - 1);
+        const int64_t rb = std::min<int64_t>(j0 + r, g.N - 1);
+        offA[q] = ra * g.lda + 8 * c;
+        offB[q] = rb * g.ldb + 8 * c;
+    }
+    const int64_t n1 = g.K1 / DK, n2 = g.K2 / DK;
+    const int64_t nst = n1 + n2;
+
+    auto issue = [&](int64_t s, int buf) {
+        const bool seg1 = s < n1;
+        const uint16_t* A = (seg1 ? g.A1 : g.A2) + (seg1 ? s : s - n1) * DK;
+        const uint16_t* B = (seg1 ? B1 : B2) + (seg1 ? s : s - n1) * DK;
+        unsigned char* sa = smem + buf * (2 * BMX * DROWB);
+        unsigned char* sb = sa + BMX * DROWB;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(A + offA[q]), (lds_ptr_t)(sa + (wave * PER + q) * 1024),
+                                             16, 0, 0);
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(B + offB[q]), (lds_ptr_t)(sb + (wave * PER + q) * 1024),
+                                             16, 0, 0);
+    };
+
+    f32x16 acc[WT][WT];
+#pragma unroll
+    for (int a = 0; a < WT; ++a)
+#pragma unroll
+        for (int b = 0; b < WT; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // fragment addresses: the swizzle term only depends on the lane
+    const int fsw = (li >> 2) & 3;
+    for (int64_t s = 0; s < NSTAGE - 1 && s < nst; ++s) issue(s, (int)s);
+    for (int64_t s = 0; s < nst; ++s) {
+        // this wave's copies of stage s have landed once at most the two
+        // younger stages' loads are outstanding (loads retire in order); the
+        // barrier (no memory fence: a fence would drain every prefetch) then
+        // makes all waves' copies visible. Every ds_read of the buffer that
+        // the next issue overwrites completed before the previous MFMAs.
+        if (s + 2 < nst) wait_vmcnt<4 * PER>();
+        else if (s + 1 < nst) wait_vmcnt<2 * PER>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (s + NSTAGE - 1 < nst) issue(s + NSTAGE - 1, (int)((s + NSTAGE - 1) % NSTAGE));
+        const unsigned char* As = smem + (s % NSTAGE) * (2 * BMX * DROWB);
+        const unsigned char* Bs = As + BMX * DROWB;
+        bf16x8 av[2][WT], bv[2][WT];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = (2 * kk + lh) ^ fsw;
+#pragma unroll
+            for (int a = 0; a < WT; ++a) av[kk][a] = *(const bf16x8*)(As + (wm + 32 * a + li) * DROWB + 16 * c);
+#pragma unroll
+            for (int b = 0; b < WT; ++b) bv[kk][b] = *(const bf16x8*)(Bs + (wn + 32 * b + li) * DROWB + 16 * c);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int a = 0; a < WT; ++a)
+#pragma unroll
+                for (int b = 0; b < WT; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][a], bv[kk][b], acc[a][b], 0, 0, 0);
+        // keep every fragment read of the stage ahead of its MFMAs (the
+        // scheduler would otherwise sink them and expose the LDS latency
+        // once per four MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * WT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * WT * WT, 0);
+    }
+    __syncthreads();
+    store_tile<BMX, EPI>(g, acc, i0, j0, diag, L, smem);
+}
+
+// Opt a kernel into more than 64 KB of dynamic LDS (once per instantiation).
+template <int BMX, int EPI, bool DIRECT>
+int prepare_kernel() {
+    static bool done = false;
+    if (!done) {
+        if (DIRECT)
+            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_direct_kernel<BMX, EPI>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, dsmem_bytes<BMX>()));
+        else
+            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_kernel<BMX, EPI>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem_bytes<BMX>()));
+        done = true;
+    }
+    return PTQ_OK;
+}
+
+// Launch either variant: the direct one when both K segments are multiples of DK.
+template <int BMX, int EPI>
+int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t st) {
+    const unsigned grid = (unsigned)(cdiv(nwork, NXCD) * NXCD);
+    if (g.K1 % DK == 0 && g.K2 % DK == 0 && g.M > 0 && g.N > 0) {
+        PTQ_TRY((prepare_kernel<BMX, EPI, true>()));
+        hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI>), dim3(grid, grid_y), dim3(NTH),
+                           dsmem_bytes<BMX>(), st, g, nwork);
+    } else {
+        PTQ_TRY((prepare_kernel<BMX, EPI, false>()));
+        hipLaunchKernelGGL((gemm_bf16_nt_kernel<BMX, EPI>), dim3(grid, grid_y), dim3(NTH), smem_bytes<BMX>(), st,
+                           g, nwork);
+    }
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
 }
 
 // Xt[c][r] = X[r0 + r][c] for r < nr; rows nr..ldt-1 of Xt are zeroed.
@@ -423,14 +645,11 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
             g.lda = ldt; g.ldb = ldt; g.M = n; g.N = n; g.b_batch_stride = 0;
             g.H = (ns > 1) ? hpart + (int64_t)s * n * n : H;
             g.ldh = n; g.mirror = (ns == 1 && last) ? 1 : 0; g.T = p.T; g.store_not_add = (ns > 1) ? 1 : 0;
-            const unsigned grid = (unsigned)(cdiv(ntiles, NXCD) * NXCD);
             prof_begin(PROF_XTX_GEMM, st);
-            if (p.bm == 256)
-                hipLaunchKernelGGL((gemm_bf16_nt_kernel<256, EPI_HESSIAN>), dim3(grid), dim3(NTH), 0, st, g, ntiles);
-            else
-                hipLaunchKernelGGL((gemm_bf16_nt_kernel<128, EPI_HESSIAN>), dim3(grid), dim3(NTH), 0, st, g, ntiles);
+            const int rc = (p.bm == 256) ? launch_nt<256, EPI_HESSIAN>(g, ntiles, 1, st)
+                                         : launch_nt<128, EPI_HESSIAN>(g, ntiles, 1, st);
             prof_end(PROF_XTX_GEMM, st);
-            PTQ_LAUNCH_CHECK();
+            PTQ_TRY(rc);
         }
         if (ns > 1) {
             // reduce the split partials into H (upper triangle, mirrored)
@@ -461,13 +680,10 @@ int launch_awq_error_gemm(const uint16_t* X, int64_t ldx, int64_t rows, int64_t 
     g.ntiles = cdiv(rows, 256) * g.tiles_n;
     *ntiles_out = g.ntiles;
     g.partial = partial;
-    const unsigned grid = (unsigned)(cdiv(g.ntiles, NXCD) * NXCD);
     prof_begin(PROF_AWQ_GEMM, st);
-    hipLaunchKernelGGL((gemm_bf16_nt_kernel<256, EPI_SUMSQ>), dim3(grid, (unsigned)nbatch), dim3(NTH), 0, st, g,
-                       g.ntiles);
+    const int rc = launch_nt<256, EPI_SUMSQ>(g, g.ntiles, (unsigned)nbatch, st);
     prof_end(PROF_AWQ_GEMM, st);
-    PTQ_LAUNCH_CHECK();
-    return PTQ_OK;
+    return rc;
 }
 
 }  // namespace ptq

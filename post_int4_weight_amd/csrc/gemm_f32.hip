@@ -9,36 +9,34 @@
 // Cholesky / triangular inverse that produce U.
 //
 // Tile: 128 x 128 per workgroup of 256 threads (4 wave64s in 2 x 2), each
-// wave 64 x 64 = 2 x 2 MFMA 32x32 blocks; K staged through LDS 16 at a time,
-// double buffered. LDS tiles are k-major (As[k][m], Bs[k][n]) so an MFMA
-// operand fetch is one conflict-free ds_read_b32 per lane whatever the
-// global layout; K-contiguous global layouts are transposed while staging.
-// Within a 16-deep K tile, MFMA step s (k = 2 per step) takes k = s from
-// lanes 0-31 and k = s + 8 from lanes 32-63 (the contraction is order-free);
-// with a 132-float LDS row this puts the two half-waves on disjoint banks.
+// wave 64 x 64 = 2 x 2 MFMA 32x32 blocks; K staged through LDS 32 at a time,
+// double buffered through registers. LDS tiles are k-major (As[k][m],
+// Bs[k][n]) so an MFMA operand fetch is one conflict-free ds_read_b32 per
+// lane whatever the global layout; K-contiguous global layouts are
+// transposed while staging. Within a 32-deep K tile, each MFMA step (k = 2
+// per step) takes one k-row from lanes 0-31 and the row 8 further from lanes
+// 32-63 (the contraction is order-free); with a 132-float LDS row the two
+// half-waves read disjoint banks. Operand layouts are template parameters and interior
+// tiles take an unguarded load path, so the main loop has no divergent
+// branches; every operand read of a stage is issued before its MFMAs.
 #include "common.hpp"
 
 namespace ptq {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LDS_ROW = 132;  // floats per k-row of a staged tile
 constexpr int NT = 256;
+constexpr int PER = BK * BM / 4 / NT;   // float4 per thread per operand per stage (4)
 
 struct Stage {
     float a[BK * LDS_ROW];
     float b[BK * LDS_ROW];
 };
 
-// Per-thread staging registers: 2 float4 of A and 2 of B per K tile.
-struct Regs {
-    float4 a[2];
-    float4 b[2];
-};
-
-__device__ __forceinline__ float4 load4_guarded(const float* base, int64_t ld, int64_t r, int64_t c,
-                                                int64_t R, int64_t Cn) {
-    // element (r, c..c+3) of a row-major [R, Cn] matrix, zero outside
+// element (r, c..c+3) of a row-major [R, Cn] matrix, zero outside
+__device__ __forceinline__ float4 load4_guarded(const float* base, int64_t ld, int64_t r, int64_t c, int64_t R,
+                                                int64_t Cn) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < R) {
         const float* p = base + r * ld + c;
@@ -54,31 +52,35 @@ __device__ __forceinline__ float4 load4_guarded(const float* base, int64_t ld, i
 }
 
 // Stage an operand tile [BK x 128] (k-major in LDS) from global memory.
-// kmajor_global: the global matrix is stored [K][X] (X = the M or N index).
-__device__ __forceinline__ void gload(float4 (&v)[2], const float* P, int64_t ld, bool kmajor_global,
-                                      int64_t k0, int64_t x0, int64_t K, int64_t X, int t) {
+// KMAJOR: the global matrix is stored [K][X] (X = the M or N index).
+template <bool KMAJOR, bool GUARD>
+__device__ __forceinline__ void gload(float4 (&v)[PER], const float* P, int64_t ld, int64_t k0, int64_t x0,
+                                      int64_t K, int64_t X, int t) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        int idx = t + NT * r;
-        if (kmajor_global) {
-            int k = idx >> 5, x4 = idx & 31;           // 16 rows x 32 float4
-            v[r] = load4_guarded(P, ld, k0 + k, x0 + 4 * x4, K, X);
+    for (int r = 0; r < PER; ++r) {
+        const int idx = t + NT * r;
+        if (KMAJOR) {
+            const int k = idx >> 5, x4 = idx & 31;           // BK rows x 32 float4
+            v[r] = GUARD ? load4_guarded(P, ld, k0 + k, x0 + 4 * x4, K, X)
+                         : *(const float4*)(P + (k0 + k) * ld + x0 + 4 * x4);
         } else {
-            int x = idx >> 2, kq = idx & 3;            // 128 rows x 4 float4 along k
-            v[r] = load4_guarded(P, ld, x0 + x, k0 + 4 * kq, X, K);
+            const int x = idx >> 3, kq = idx & 7;            // 128 rows x 8 float4 along k
+            v[r] = GUARD ? load4_guarded(P, ld, x0 + x, k0 + 4 * kq, X, K)
+                         : *(const float4*)(P + (x0 + x) * ld + k0 + 4 * kq);
         }
     }
 }
 
-__device__ __forceinline__ void sstore(float* S, const float4 (&v)[2], bool kmajor_global, int t) {
+template <bool KMAJOR>
+__device__ __forceinline__ void sstore(float* S, const float4 (&v)[PER], int t) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        int idx = t + NT * r;
-        if (kmajor_global) {
-            int k = idx >> 5, x4 = idx & 31;
+    for (int r = 0; r < PER; ++r) {
+        const int idx = t + NT * r;
+        if (KMAJOR) {
+            const int k = idx >> 5, x4 = idx & 31;
             *(float4*)(S + k * LDS_ROW + 4 * x4) = v[r];
         } else {
-            int x = idx >> 2, kq = idx & 3;
+            const int x = idx >> 3, kq = idx & 7;
             S[(4 * kq + 0) * LDS_ROW + x] = v[r].x;
             S[(4 * kq + 1) * LDS_ROW + x] = v[r].y;
             S[(4 * kq + 2) * LDS_ROW + x] = v[r].z;
@@ -87,6 +89,57 @@ __device__ __forceinline__ void sstore(float* S, const float4 (&v)[2], bool kmaj
     }
 }
 
+template <bool A_KMAJOR, bool B_KMAJOR, bool GUARD>
+__device__ __forceinline__ void main_loop(const GemmArgs& g, Stage (&st)[2], f32x16 (&acc)[2][2], int64_t kb,
+                                          int64_t nk, int64_t m0, int64_t n0) {
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int li = lane & 31, lh = lane >> 5;
+    float4 ra[PER], rb[PER];
+    gload<A_KMAJOR, GUARD>(ra, g.A, g.lda, kb, m0, g.K, g.M, t);
+    gload<B_KMAJOR, GUARD>(rb, g.B, g.ldb, kb, n0, g.K, g.N, t);
+    sstore<A_KMAJOR>(st[0].a, ra, t);
+    sstore<B_KMAJOR>(st[0].b, rb, t);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int64_t k1 = kb + (kt + 1) * BK;
+            gload<A_KMAJOR, GUARD>(ra, g.A, g.lda, k1, m0, g.K, g.M, t);
+            gload<B_KMAJOR, GUARD>(rb, g.B, g.ldb, k1, n0, g.K, g.N, t);
+        }
+        const float* As = st[cur].a;
+        const float* Bs = st[cur].b;
+        float av[BK / 2][2], bv[BK / 2][2];
+#pragma unroll
+        for (int s = 0; s < BK / 2; ++s) {
+            const int kr = (s & 7) + 16 * (s >> 3) + 8 * lh;   // half-waves 8 rows apart: disjoint banks
+            av[s][0] = As[kr * LDS_ROW + wm + li];
+            av[s][1] = As[kr * LDS_ROW + wm + 32 + li];
+            bv[s][0] = Bs[kr * LDS_ROW + wn + li];
+            bv[s][1] = Bs[kr * LDS_ROW + wn + 32 + li];
+        }
+#pragma unroll
+        for (int s = 0; s < BK / 2; ++s) {
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s][0], bv[s][0], acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s][0], bv[s][1], acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s][1], bv[s][0], acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s][1], bv[s][1], acc[1][1], 0, 0, 0);
+        }
+        // operand reads first, then the MFMAs (latency exposed once per stage)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * BK, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * BK, 0);
+        if (more) {
+            sstore<A_KMAJOR>(st[cur ^ 1].a, ra, t);
+            sstore<B_KMAJOR>(st[cur ^ 1].b, rb, t);
+        }
+        __syncthreads();
+    }
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR>
 __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmArgs g) {
     const int64_t tiles_n = cdiv(g.N, BN);
     const int64_t tile = blockIdx.x;
@@ -96,17 +149,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmArgs g) {
 
     // K range this tile needs (structural zeros of a triangular operand skipped)
     int64_t kb = 0, ke = g.K;
-    if (g.tri == TRI_A_UPPER) kb = m0;                       // A[i][k] = 0 for k < i
-    else if (g.tri == TRI_B_UPPER_NK) kb = n0;               // B[j][k] = 0 for k < j
+    if (g.tri == TRI_A_UPPER) kb = m0;                        // A[i][k] = 0 for k < i
+    else if (g.tri == TRI_B_UPPER_NK) kb = n0;                // B[j][k] = 0 for k < j
     else if (g.tri == TRI_B_UPPER_KN) ke = min(g.K, n0 + BN); // B[k][j] = 0 for k > j
     kb = (kb / BK) * BK;
 
     __shared__ Stage st[2];
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    const int li = lane & 31, lh = lane >> 5;
-
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -115,74 +163,52 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const bool a_km = g.layout_a == A_KM;
-    const bool b_kn = g.layout_b == B_KN;
     const int64_t nk = (ke > kb) ? cdiv(ke - kb, BK) : 0;
-
-    Regs rg;
     if (nk > 0) {
-        gload(rg.a, g.A, g.lda, a_km, kb, m0, g.K, g.M, t);
-        gload(rg.b, g.B, g.ldb, b_kn, kb, n0, g.K, g.N, t);
-        sstore(st[0].a, rg.a, a_km, t);
-        sstore(st[0].b, rg.b, b_kn, t);
-    }
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            int64_t k1 = kb + (kt + 1) * BK;
-            gload(rg.a, g.A, g.lda, a_km, k1, m0, g.K, g.M, t);
-            gload(rg.b, g.B, g.ldb, b_kn, k1, n0, g.K, g.N, t);
-        }
-        const float* As = st[cur].a;
-        const float* Bs = st[cur].b;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int kr = s + 8 * lh;
-            float av0 = As[kr * LDS_ROW + wm + li];
-            float av1 = As[kr * LDS_ROW + wm + 32 + li];
-            float bv0 = Bs[kr * LDS_ROW + wn + li];
-            float bv1 = Bs[kr * LDS_ROW + wn + 32 + li];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av0, bv0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av0, bv1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av1, bv0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av1, bv1, acc[1][1], 0, 0, 0);
-        }
-        if (more) {
-            sstore(st[cur ^ 1].a, rg.a, a_km, t);
-            sstore(st[cur ^ 1].b, rg.b, b_kn, t);
-        }
-        __syncthreads();
+        const bool interior = (m0 + BM <= g.M) && (n0 + BN <= g.N) && (kb + nk * BK <= g.K) &&
+                              (g.lda % 4 == 0) && (g.ldb % 4 == 0);
+        if (interior)
+            main_loop<A_KMAJOR, B_KMAJOR, false>(g, st, acc, kb, nk, m0, n0);
+        else
+            main_loop<A_KMAJOR, B_KMAJOR, true>(g, st, acc, kb, nk, m0, n0);
     }
 
     // Epilogue. 32x32 accumulator layout: lane l, register r holds
     // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int li = lane & 31, lh = lane >> 5;
+    const int mi = (int)min((int64_t)BM, g.M - m0), nj = (int)min((int64_t)BN, g.N - n0);
+    float* Ct = g.C + m0 * g.ldc + n0;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+            const int jj = wn + 32 * j + li;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-                int64_t col = n0 + wn + 32 * j + li;
-                if (row < g.M && col < g.N) {
-                    float* c = g.C + row * g.ldc + col;
-                    float v = g.alpha * acc[i][j][r];
+                const int ii = wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (ii < mi && jj < nj) {
+                    float* c = Ct + (int64_t)ii * g.ldc + jj;
+                    const float v = g.alpha * acc[i][j][r];
                     *c = g.beta_one ? (*c + v) : v;
                 }
             }
+        }
 }
 
 }  // namespace
 
 int launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
     if (a.M <= 0 || a.N <= 0) return PTQ_OK;
-    if (a.K <= 0) {
-        if (a.beta_one) return PTQ_OK;  // C += 0
-    }
-    int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)tiles), dim3(NT), 0, st, a);
+    if (a.K <= 0 && a.beta_one) return PTQ_OK;  // C += 0
+    const unsigned tiles = (unsigned)(cdiv(a.M, BM) * cdiv(a.N, BN));
+    const bool akm = a.layout_a == A_KM, bkn = a.layout_b == B_KN;
+    if (akm && bkn) hipLaunchKernelGGL((gemm_f32_kernel<true, true>), dim3(tiles), dim3(NT), 0, st, a);
+    else if (akm) hipLaunchKernelGGL((gemm_f32_kernel<true, false>), dim3(tiles), dim3(NT), 0, st, a);
+    else if (bkn) hipLaunchKernelGGL((gemm_f32_kernel<false, true>), dim3(tiles), dim3(NT), 0, st, a);
+    else hipLaunchKernelGGL((gemm_f32_kernel<false, false>), dim3(tiles), dim3(NT), 0, st, a);
     PTQ_LAUNCH_CHECK();
     return PTQ_OK;
 }

@@ -29,6 +29,10 @@ namespace {
 
 constexpr int CPL = 8;     // columns per lane
 constexpr int NTH = 256;
+// |w/scale| <= 128.5 for bits <= 8, where one fp32 ulp is <= 2^-16: a band of
+// 2^-15 around each half-integer holds every fp32 quotient whose rounding
+// could differ from the fp64 one.
+constexpr float TIE_BAND = 1.0f / 32768.0f;
 
 // Wc[r][k] = W[r][perm[k]] as fp32
 template <typename T>
@@ -46,7 +50,8 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
                                                           const float* __restrict__ U, int64_t b0, int bc,
                                                           int g, float qmax, const int32_t* __restrict__ perm,
                                                           int8_t* __restrict__ codes, float* __restrict__ scales,
-                                                          int64_t ngroups, float* __restrict__ E,
+                                                          int64_t ngroups, float* __restrict__ gmaxes,
+                                                          float* __restrict__ E,
                                                           float* __restrict__ err2, int64_t nblocks,
                                                           int* __restrict__ flag) {
     constexpr int LPR = B / CPL;          // lanes per row
@@ -82,6 +87,7 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
     const int lane = t & 63;
     const int row_lane0 = lane - lr;              // first lane of this row in the wave
     float scale = 0.f;
+    float gmax = 0.f;       // the group's max |w| (scale = gmax / qmax)
     float e2 = 0.f;
 
     if (g > B) {
@@ -95,10 +101,15 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
                 for (int64_t k = b0 + lr; k < j1; k += LPR) mx = fmaxf(mx, fabsf(Wc[r * n + k]));
 #pragma unroll
             for (int off = 1; off < LPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            gmax = mx;
             scale = mx / qmax;
-            if (live && lr == 0) scales[r * ngroups + b0 / g] = scale;
+            if (live && lr == 0) {
+                scales[r * ngroups + b0 / g] = scale;
+                gmaxes[r * ngroups + b0 / g] = mx;
+            }
         } else if (live) {
             scale = scales[r * ngroups + b0 / g];  // written by an earlier block
+            gmax = gmaxes[r * ngroups + b0 / g];
         }
     }
 
@@ -115,13 +126,22 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
                 }
 #pragma unroll
                 for (int off = 1; off < LPR; off <<= 1) loc = fmaxf(loc, __shfl_xor(loc, off, 64));
+                gmax = loc;
                 scale = loc / qmax;
                 if (live && lr == 0) scales[r * ngroups + (b0 + j) / g] = scale;
             }
-            // round this lane's copy of column j (the owner's copy is the real one)
+            // round this lane's copy of column j (the owner's copy is the real one).
+            // The rounding decision is the fp64 one, x / (gmax / qmax) in double:
+            // the fp32 quotient is within 2 ulp of it, so only quotients that
+            // close to a half-integer are recomputed in fp64.
             const float x = w[j % CPL];
             float q = 0.f;
-            if (scale > 0.f) q = fminf(fmaxf(rintf(x / scale), -qmax - 1.f), qmax);
+            if (scale > 0.f) {
+                const float t = x / scale;
+                float rq = rintf(t);
+                if (fabsf(fabsf(t - rq) - 0.5f) < TIE_BAND) rq = (float)rint((double)x / ((double)gmax / (double)qmax));
+                q = fminf(fmaxf(rq, -qmax - 1.f), qmax);
+            }
             const float e = (x - q * scale) / diag[j];
             const int owner = j / CPL;
             const float eb = __shfl(e, row_lane0 + owner, 64);
@@ -231,15 +251,15 @@ __global__ void zero_int_kernel(int* p) { *p = 0; }
 
 template <int B>
 int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float qmax, const int32_t* perm,
-               int8_t* codes, float* scales, int64_t ngroups, float* E, float* err2, int64_t nblocks, int* flag,
-               hipStream_t st) {
+               int8_t* codes, float* scales, int64_t ngroups, float* gmaxes, float* E, float* err2, int64_t nblocks,
+               int* flag, hipStream_t st) {
     constexpr int RPW = NTH / (B / CPL);
     const unsigned grid = (unsigned)cdiv(out, RPW);
     for (int64_t b0 = 0; b0 < n; b0 += B) {
         const int bc = (int)std::min<int64_t>(B, n - b0);
         prof_begin(PROF_BLOCK_LOOP, st);
         hipLaunchKernelGGL(gptq_block_kernel<B>, dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc, g, qmax, perm,
-                           codes, scales, ngroups, E, err2, nblocks, flag);
+                           codes, scales, ngroups, gmaxes, E, err2, nblocks, flag);
         prof_end(PROF_BLOCK_LOOP, st);
         PTQ_LAUNCH_CHECK();
         const int64_t b1 = b0 + bc;
@@ -267,6 +287,7 @@ size_t columns_workspace_bytes(int64_t out, int64_t n, int block) {
     z.take<float>((size_t)out * n);          // Wc
     z.take<float>((size_t)out * block);      // E
     z.take<float>((size_t)out * nblocks);    // err2
+    z.take<float>((size_t)out * cdiv(n, 8)); // group maxima (groups of >= 8 columns)
     z.take<double>((size_t)out * 2);         // per-row stats
     z.take<double>(2);                       // totals
     z.take<int>(1);                          // flag
@@ -282,10 +303,11 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
     float* Wc = ar.take<float>((size_t)out * n);
     float* E = ar.take<float>((size_t)out * block);
     float* err2 = ar.take<float>((size_t)out * nblocks);
+    float* gmaxes = ar.take<float>((size_t)out * cdiv(n, 8));
     double* rowst = ar.take<double>((size_t)out * 2);
     double* tot = ar.take<double>(2);
     int* flag = ar.take<int>(1);
-    if (!Wc || !E || !err2 || !rowst || !tot || !flag) {
+    if (!Wc || !E || !err2 || !gmaxes || !rowst || !tot || !flag) {
         set_error("gptq_quantize_columns: workspace of %zu bytes, %zu needed", ws_bytes,
                   columns_workspace_bytes(out, n, block));
         return PTQ_EWORKSPACE;
@@ -303,11 +325,14 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
                                perm, Wc);
         PTQ_LAUNCH_CHECK();
         if (block == 128)
-            PTQ_TRY(run_blocks<128>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, E, err2, nblocks, flag, st));
+            PTQ_TRY(run_blocks<128>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, gmaxes, E, err2, nblocks,
+                                    flag, st));
         else if (block == 64)
-            PTQ_TRY(run_blocks<64>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, E, err2, nblocks, flag, st));
+            PTQ_TRY(run_blocks<64>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, gmaxes, E, err2, nblocks,
+                                    flag, st));
         else
-            PTQ_TRY(run_blocks<32>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, E, err2, nblocks, flag, st));
+            PTQ_TRY(run_blocks<32>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, gmaxes, E, err2, nblocks,
+                                    flag, st));
     }
 
     if (g_idx) {

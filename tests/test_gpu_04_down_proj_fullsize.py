@@ -42,6 +42,8 @@ def down_proj(gpu):
     for r0 in range(0, cfg.rows, 8192):
         xc = X[r0:r0 + 8192].cpu().float().numpy().astype(np.float64)
         d0 += np.sum(xc * xc, axis=0)
+        if (r0 // 8192) % 8 == 7:
+            print(f"[oracle] column sums of squares: {r0 + 8192} of {cfg.rows} rows", flush=True)
     return cfg, W, X, H, d, d0
 
 
@@ -55,6 +57,7 @@ def test_hessian_blocks(down_proj):
         H0b, _ = oracle.proxy_hessian(to64(X[:, cols].cpu()), chunk_rows=16384)
         Hb = H[c0:c0 + TRAIL, c0:c0 + TRAIL].cpu().double().numpy()
         assert rel_fro(Hb, H0b) <= 1e-5
+        print(f"[oracle] H block at {c0} checked", flush=True)
     # an off-diagonal block, error measured against sqrt(H_ii H_jj)
     ci = list(range(1000, 1256))
     cj = list(range(n - 3000, n - 2744))
@@ -86,6 +89,7 @@ def test_gptq_fullsize(down_proj, bits):
     H0t, _ = oracle.proxy_hessian(to64(X[:, cols].cpu()), chunk_rows=16384)
     Ut = oracle.inverse_upper_factor(H0t + lam0 * np.eye(TRAIL))
     assert rel_fro(U[n - TRAIL:, n - TRAIL:].cpu().double().numpy(), Ut) <= 1e-4
+    print("[oracle] trailing block of U checked", flush=True)
 
     # U H_d U^T = I on sampled rows (fp64 on the device)
     Hd = H.double()
@@ -117,6 +121,7 @@ def test_gptq_fullsize(down_proj, bits):
     Hd.diagonal().sub_(lam)
     obj = float(((dW @ Hd) * dW).sum())
     assert abs(res["stats"]["objective"] - obj) <= 2e-3 * obj
+    print("[check] loop identities checked", flush=True)
     # calibration error below plain RTN's (the loop's purpose)
     Wrtn_codes, Wrtn_scales = oracle.rtn(to64(W.cpu()), bits, 128)
     Wrtn = torch.tensor(oracle.dequantize(Wrtn_codes, Wrtn_scales, np.arange(n) // 128), device=W.device)

@@ -49,5 +49,18 @@ def test_awq_llama70b_q_proj(gpu):
     alphas = list(inputs.AWQ_ALPHAS)
     res = api.awq_search_alpha(W, X, alphas, bits=4, group_size=128)
     torch.cuda.synchronize()
-    ref = oracle.awq_search(to64(W.cpu()), to64(X.cpu()), alphas, bits=4, g=128)
+    # the oracle's grid search (oracle.awq_search), one alpha at a time so
+    # the long fp64 evaluation reports its progress
+    W64, X64 = to64(W.cpu()), to64(X.cpu())
+    m = oracle.channel_mean_abs(X64)
+    errors = []
+    for a in alphas:
+        _, _, What = oracle.awq_quantize(W64, m ** a, 4, 128)
+        errors.append(oracle.output_error(X64, W64, What))
+        print(f"[oracle] alpha {a:.2f}: error {errors[-1]:.6e}", flush=True)
+    errors = np.array(errors)
+    best = int(np.argmin(errors))
+    s = m ** alphas[best]
+    codes, _, _ = oracle.awq_quantize(W64, s, 4, 128)
+    ref = {"errors": errors, "index": best, "codes": codes, "s": s}
     _compare(res, ref, alphas)
