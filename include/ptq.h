@@ -70,6 +70,7 @@ int ptq_abi_version(void);
  *   0 X^T X bf16 MFMA tiles        1 fp32 GEMMs of the U recursion
  *   2 diagonal-block factor/inverse 3 GPTQ in-block column loop
  *   4 GPTQ trailing fp32 GEMM       5 AWQ error GEMM
+ *   6 GPTQ fp32 update inside a super-block of columns
  * Enabling (any mask, 0 included) discards earlier records. ptq_profile_read
  * waits for the recorded events of class `kernel` and returns the sum of
  * their elapsed times (ms) and the number of launches. Process-wide; calls

@@ -111,7 +111,7 @@ def _rowmajor(t: torch.Tensor, name: str):
 # ------------------------------------------------------------- profiling ---
 
 PROFILE_KERNELS = {"xtx_gemm": 0, "factor_gemm": 1, "factor_base": 2, "block_loop": 3, "trail_gemm": 4,
-                   "awq_gemm": 5}
+                   "awq_gemm": 5, "inner_gemm": 6}
 
 
 def profile_enable(kernels=()):

@@ -104,14 +104,20 @@ __global__ void fill_int_kernel(int* p, int v) { *p = v; }
 // bit 1: NaN pivot.
 __global__ __launch_bounds__(256) void chol_inv_base_kernel(const float* __restrict__ A, float* __restrict__ U,
                                                              int m, int64_t ld, int* flag) {
+    static_assert(BASE == 64, "thread ownership below assumes a 64 x 64 block");
     __shared__ float a[BASE][BASE + 1];
     __shared__ float u[BASE][BASE + 1];
     const int t = threadIdx.x;
-    for (int e = t; e < m * m; e += 256) {
-        const int i = e / m, j = e % m;
-        a[i][j] = (i <= j) ? A[(int64_t)i * ld + j] : 0.f;
-        u[i][j] = 0.f;
-    }
+    // thread t owns the 4 x 4 sub-block rows 4*(t/16).., columns 4*(t%16)..
+    const int i0 = 4 * (t >> 4), k0 = 4 * (t & 15);
+#pragma unroll
+    for (int di = 0; di < 4; ++di)
+#pragma unroll
+        for (int dk = 0; dk < 4; ++dk) {
+            const int i = i0 + di, k = k0 + dk;
+            a[i][k] = (i <= k && k < m) ? A[(int64_t)i * ld + k] : 0.f;
+            u[i][k] = 0.f;
+        }
     __syncthreads();
     // reversed-order Cholesky: column j from the last to the first
     for (int j = m - 1; j >= 0; --j) {
@@ -122,14 +128,31 @@ __global__ __launch_bounds__(256) void chol_inv_base_kernel(const float* __restr
         }
         const float rjj = sqrtf(piv);
         __syncthreads();
-        for (int i = t; i < j; i += 256) a[i][j] = a[i][j] / rjj;
-        if (t == 0) a[j][j] = rjj;
+        // R[i][j] = A[i][j] / R[j][j] (i < j), by the owners of column j
+        if (j >= k0 && j < k0 + 4) {
+#pragma unroll
+            for (int di = 0; di < 4; ++di) {
+                const int i = i0 + di;
+                if (i < j) a[i][j] = a[i][j] / rjj;
+                else if (i == j) a[j][j] = rjj;
+            }
+        }
         __syncthreads();
         // A[i][k] -= R[i][j] R[k][j] for 0 <= i <= k < j
-        const int cnt = j * j;
-        for (int e = t; e < cnt; e += 256) {
-            const int i = e / j, k = e % j;
-            if (i <= k) a[i][k] -= a[i][j] * a[k][j];
+        if (i0 < j && k0 < j) {
+            float ck[4];
+#pragma unroll
+            for (int dk = 0; dk < 4; ++dk) ck[dk] = a[k0 + dk][j];
+#pragma unroll
+            for (int di = 0; di < 4; ++di) {
+                const int i = i0 + di;
+                const float ri = a[i][j];
+#pragma unroll
+                for (int dk = 0; dk < 4; ++dk) {
+                    const int k = k0 + dk;
+                    if (i <= k && k < j) a[i][k] -= ri * ck[dk];
+                }
+            }
         }
         __syncthreads();
     }
@@ -149,10 +172,13 @@ __global__ __launch_bounds__(256) void chol_inv_base_kernel(const float* __restr
         }
         __syncthreads();
     }
-    for (int e = t; e < m * m; e += 256) {
-        const int i = e / m, j = e % m;
-        U[(int64_t)i * ld + j] = (i <= j) ? u[i][j] : 0.f;
-    }
+#pragma unroll
+    for (int di = 0; di < 4; ++di)
+#pragma unroll
+        for (int dk = 0; dk < 4; ++dk) {
+            const int i = i0 + di, k = k0 + dk;
+            if (i < m && k < m) U[(int64_t)i * ld + k] = (i <= k) ? u[i][k] : 0.f;
+        }
 }
 
 struct Ctx {

@@ -108,7 +108,8 @@ enum ProfKernel {
     PROF_BLOCK_LOOP = 3,    // GPTQ in-block column loop
     PROF_TRAIL_GEMM = 4,    // GPTQ trailing fp32 MFMA update
     PROF_AWQ_GEMM = 5,      // AWQ error GEMM
-    PROF_NKERNELS = 6
+    PROF_INNER_GEMM = 6,    // GPTQ update inside a super-block
+    PROF_NKERNELS = 7
 };
 void prof_begin(int kernel, hipStream_t st);
 void prof_end(int kernel, hipStream_t st);

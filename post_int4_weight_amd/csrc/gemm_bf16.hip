@@ -398,43 +398,67 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // fragment addresses: the swizzle term only depends on the lane
-    const int fsw = (li >> 2) & 3;
-    for (int64_t s = 0; s < NSTAGE - 1 && s < nst; ++s) issue(s, (int)s);
-    for (int64_t s = 0; s < nst; ++s) {
-        // this wave's copies of stage s have landed once at most the two
-        // younger stages' loads are outstanding (loads retire in order); the
-        // barrier (no memory fence: a fence would drain every prefetch) then
-        // makes all waves' copies visible. Every ds_read of the buffer that
-        // the next issue overwrites completed before the previous MFMAs.
-        if (s + 2 < nst) wait_vmcnt<4 * PER>();
-        else if (s + 1 < nst) wait_vmcnt<2 * PER>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (s + NSTAGE - 1 < nst) issue(s + NSTAGE - 1, (int)((s + NSTAGE - 1) % NSTAGE));
+    // Software pipeline over half-stages (16-deep sub-steps): the fragment
+    // reads of the next sub-step are interleaved with the MFMAs of the current
+    // one, so after the prologue no LDS latency is exposed. The stage barrier
+    // sits in the middle of a stage (between its two sub-steps): by then every
+    // wave has finished reading the buffer the next issue overwrites (it was
+    // last read one full stage earlier). Waits: this wave's copies of a stage
+    // have landed once only the younger stages' loads are outstanding (loads
+    // retire in order); the barrier (no memory fence, which would drain every
+    // prefetch) then makes all waves' copies visible.
+    const int fsw = (li >> 2) & 3;   // fragment swizzle term, lane-only
+    bf16x8 fa[2][WT], fb[2][WT];
+    auto frags = [&](int64_t s, int kk, int slot) {
         const unsigned char* As = smem + (s % NSTAGE) * (2 * BMX * DROWB);
         const unsigned char* Bs = As + BMX * DROWB;
-        bf16x8 av[2][WT], bv[2][WT];
+        const int c = (2 * kk + lh) ^ fsw;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c = (2 * kk + lh) ^ fsw;
+        for (int a = 0; a < WT; ++a) fa[slot][a] = *(const bf16x8*)(As + (wm + 32 * a + li) * DROWB + 16 * c);
 #pragma unroll
-            for (int a = 0; a < WT; ++a) av[kk][a] = *(const bf16x8*)(As + (wm + 32 * a + li) * DROWB + 16 * c);
+        for (int b = 0; b < WT; ++b) fb[slot][b] = *(const bf16x8*)(Bs + (wn + 32 * b + li) * DROWB + 16 * c);
+    };
+    auto mfmas = [&](int slot) {
 #pragma unroll
-            for (int b = 0; b < WT; ++b) bv[kk][b] = *(const bf16x8*)(Bs + (wn + 32 * b + li) * DROWB + 16 * c);
+        for (int a = 0; a < WT; ++a)
+#pragma unroll
+            for (int b = 0; b < WT; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][a], fb[slot][b], acc[a][b], 0, 0, 0);
+    };
+    // one fragment read per (WT/2) MFMAs: reads of the next sub-step ride
+    // under the MFMAs (MFMAs first: the wait before the first one then only
+    // covers reads issued a whole sub-step earlier)
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2 * WT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, WT / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int a = 0; a < WT; ++a)
-#pragma unroll
-                for (int b = 0; b < WT; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][a], bv[kk][b], acc[a][b], 0, 0, 0);
-        // keep every fragment read of the stage ahead of its MFMAs (the
-        // scheduler would otherwise sink them and expose the LDS latency
-        // once per four MFMAs)
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * WT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * WT * WT, 0);
+    };
+
+    // Every issue moves 2*PER chunks per wave; past the last stage the issue
+    // repeats the last stage into the free buffer, so the counts (and the
+    // waits) are the same on every iteration and the loop has no joins that
+    // would force a full lgkmcnt drain.
+    if (nst > 0) {
+        for (int64_t s = 0; s < NSTAGE - 1; ++s) issue(std::min<int64_t>(s, nst - 1), (int)s);
+        wait_vmcnt<4 * PER>();
+        __builtin_amdgcn_s_barrier();
+        frags(0, 0, 0);
+        for (int64_t s = 0; s + 1 < nst; ++s) {
+            frags(s, 1, 1);
+            mfmas(0);
+            interleave();
+            wait_vmcnt<2 * PER>();
+            __builtin_amdgcn_s_barrier();
+            issue(std::min<int64_t>(s + NSTAGE - 1, nst - 1), (int)((s + NSTAGE - 1) % NSTAGE));
+            frags(s + 1, 0, 0);
+            mfmas(1);
+            interleave();
+        }
+        frags(nst - 1, 1, 1);
+        mfmas(0);
+        mfmas(1);
     }
     __syncthreads();
     store_tile<BMX, EPI>(g, acc, i0, j0, diag, L, smem);

@@ -16,7 +16,10 @@
 //    with one LDS read of U[j][..] (U's strictly lower part is zero, so
 //    columns <= j are untouched). Group maxima are lane-group reductions.
 //  * the trailing update W[:, b1:] -= E U[b0:b1, b1:] on fp32 MFMA
-//    (gemm_f32.hip), E being the block's errors.
+//    (gemm_f32.hip), E being the block's errors, batched a second time: the
+//    block's errors update the rest of its 512-column super-block at once,
+//    the columns past the super-block get all of its errors in one K = 512
+//    GEMM.
 // Act-order is a gather of W's columns into processing order up front; codes
 // are written straight back to their original column positions.
 #include "common.hpp"
@@ -28,6 +31,7 @@ namespace ptq {
 namespace {
 
 constexpr int CPL = 8;     // columns per lane
+constexpr int64_t SB_COLS = 512;   // super-block of the two-level lazy batch (a multiple of every block size)
 constexpr int NTH = 256;
 // |w/scale| <= 128.5 for bits <= 8, where one fp32 ulp is <= 2^-16: a band of
 // 2^-15 around each half-integer holds every fp32 quotient whose rounding
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
                                                           int g, float qmax, const int32_t* __restrict__ perm,
                                                           int8_t* __restrict__ codes, float* __restrict__ scales,
                                                           int64_t ngroups, float* __restrict__ gmaxes,
-                                                          float* __restrict__ E,
+                                                          float* __restrict__ E, int lde,
                                                           float* __restrict__ err2, int64_t nblocks,
                                                           int* __restrict__ flag) {
     constexpr int LPR = B / CPL;          // lanes per row
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
     for (int c = 0; c < CPL; ++c) {
         const int col = c0 + c;
         if (col < bc) {
-            E[r * B + col] = ce[c];
+            E[r * lde + col] = ce[c];
             bad |= !isfinite(ce[c]);
             const int64_t k = b0 + col;
             const int64_t oc = perm ? perm[k] : k;
@@ -255,26 +259,39 @@ int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float q
                int* flag, hipStream_t st) {
     constexpr int RPW = NTH / (B / CPL);
     const unsigned grid = (unsigned)cdiv(out, RPW);
-    for (int64_t b0 = 0; b0 < n; b0 += B) {
-        const int bc = (int)std::min<int64_t>(B, n - b0);
-        prof_begin(PROF_BLOCK_LOOP, st);
-        hipLaunchKernelGGL(gptq_block_kernel<B>, dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc, g, qmax, perm,
-                           codes, scales, ngroups, gmaxes, E, err2, nblocks, flag);
-        prof_end(PROF_BLOCK_LOOP, st);
-        PTQ_LAUNCH_CHECK();
-        const int64_t b1 = b0 + bc;
-        if (b1 < n) {
-            GemmArgs a{};
-            a.M = out; a.N = n - b1; a.K = bc;
-            a.A = E; a.lda = B; a.layout_a = A_MK;
-            a.B = U + b0 * n + b1; a.ldb = n; a.layout_b = B_KN;
-            a.C = Wc + b1; a.ldc = n;
-            a.alpha = -1.f; a.beta_one = 1; a.tri = TRI_NONE; a.upper_only = 0;
-            prof_begin(PROF_TRAIL_GEMM, st);
-            const int s = launch_gemm_f32(a, st);
-            prof_end(PROF_TRAIL_GEMM, st);
-            PTQ_TRY(s);
+    // W_cur[:, c1:] -= Err[:, 0:K] U[k0:k0+K, c1:c2]
+    // Two levels of lazy batching: inside a super-block of SB columns each
+    // block's errors update only the rest of the super-block; the columns past
+    // it receive the whole super-block's errors in one GEMM with K = SB (the
+    // same sums, regrouped). A group that spans blocks must not straddle a
+    // super-block (its scale reads columns ahead), so such group sizes that do
+    // not divide SB_COLS fall back to single blocks.
+    const int64_t SB = (g > B && SB_COLS % g != 0) ? B : SB_COLS;
+    auto update = [&](int64_t k0, int64_t K, int64_t c1, int64_t c2, int kernel) {
+        GemmArgs a{};
+        a.M = out; a.N = c2 - c1; a.K = K;
+        a.A = E + (k0 % SB); a.lda = SB; a.layout_a = A_MK;
+        a.B = U + k0 * n + c1; a.ldb = n; a.layout_b = B_KN;
+        a.C = Wc + c1; a.ldc = n;
+        a.alpha = -1.f; a.beta_one = 1; a.tri = TRI_NONE; a.upper_only = 0;
+        prof_begin(kernel, st);
+        const int s = launch_gemm_f32(a, st);
+        prof_end(kernel, st);
+        return s;
+    };
+    for (int64_t s0 = 0; s0 < n; s0 += SB) {
+        const int64_t s1 = std::min<int64_t>(n, s0 + SB);
+        for (int64_t b0 = s0; b0 < s1; b0 += B) {
+            const int bc = (int)std::min<int64_t>(B, s1 - b0);
+            prof_begin(PROF_BLOCK_LOOP, st);
+            hipLaunchKernelGGL(gptq_block_kernel<B>, dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc, g, qmax,
+                               perm, codes, scales, ngroups, gmaxes, E + (b0 - s0), (int)SB, err2, nblocks, flag);
+            prof_end(PROF_BLOCK_LOOP, st);
+            PTQ_LAUNCH_CHECK();
+            const int64_t b1 = b0 + bc;
+            if (b1 < s1) PTQ_TRY(update(b0, bc, b1, s1, PROF_INNER_GEMM));
         }
+        if (s1 < n) PTQ_TRY(update(s0, s1 - s0, s1, n, PROF_TRAIL_GEMM));
     }
     return PTQ_OK;
 }
@@ -285,7 +302,7 @@ size_t columns_workspace_bytes(int64_t out, int64_t n, int block) {
     Sizer z;
     const int64_t nblocks = cdiv(n, block);
     z.take<float>((size_t)out * n);          // Wc
-    z.take<float>((size_t)out * block);      // E
+    z.take<float>((size_t)out * SB_COLS);    // E (errors of one super-block)
     z.take<float>((size_t)out * nblocks);    // err2
     z.take<float>((size_t)out * cdiv(n, 8)); // group maxima (groups of >= 8 columns)
     z.take<double>((size_t)out * 2);         // per-row stats
@@ -301,7 +318,7 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
     const int64_t nblocks = cdiv(n, block);
     const int64_t ngroups = cdiv(n, g);
     float* Wc = ar.take<float>((size_t)out * n);
-    float* E = ar.take<float>((size_t)out * block);
+    float* E = ar.take<float>((size_t)out * SB_COLS);
     float* err2 = ar.take<float>((size_t)out * nblocks);
     float* gmaxes = ar.take<float>((size_t)out * cdiv(n, 8));
     double* rowst = ar.take<double>((size_t)out * 2);
