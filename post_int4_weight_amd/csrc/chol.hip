@@ -98,86 +98,97 @@ __global__ void fill_zero_kernel(float* p, int64_t count) {
 
 __global__ void fill_int_kernel(int* p, int v) { *p = v; }
 
-// Base case on an m x m diagonal block (m <= BASE): reversed Cholesky of the
-// block's upper triangle, A = R R^T, then U = R^-1, both in LDS; U is written
-// to the block (zeros below its diagonal). Bit 0 of *flag: non-positive pivot;
-// bit 1: NaN pivot.
+// Base case on an m x m diagonal block (m <= BASE, m % 4 == 0): the
+// reversed-order Cholesky A = R R^T (R upper) and U = R^-1 in one right-looking
+// sweep over j = m-1 .. 0. Each of the 256 threads keeps a 4 x 4 tile of the
+// (symmetric) trailing matrix A and of S = I - R[:, >j] U[>j, :] in registers;
+// at step j only column j of A and row j of S go through LDS:
+//
+//   R[i][j] = A[i][j] / sqrt(A[j][j])       (i < j)
+//   U[j][c] = S[j][c] / sqrt(A[j][j])       (row j of R U = I, final now)
+//   A[i][k] -= R[i][j] R[k][j],  S[i][c] -= R[i][j] U[j][c]    (i, k < j)
+//
+// so a step is one barrier, three 16-byte LDS reads and 32 FMAs per thread.
+// Outside m the block is padded with the identity. U is written to the block
+// (zeros below its diagonal). Bit 0 of *flag: non-positive pivot; bit 1: NaN.
 __global__ __launch_bounds__(256) void chol_inv_base_kernel(const float* __restrict__ A, float* __restrict__ U,
                                                              int m, int64_t ld, int* flag) {
     static_assert(BASE == 64, "thread ownership below assumes a 64 x 64 block");
-    __shared__ float a[BASE][BASE + 1];
-    __shared__ float u[BASE][BASE + 1];
+    __shared__ __attribute__((aligned(16))) float colb[BASE][BASE];   // colb[j][i] = A[i][j] at step j
+    __shared__ __attribute__((aligned(16))) float rowb[BASE][BASE];   // rowb[j][c] = S[j][c] at step j
     const int t = threadIdx.x;
-    // thread t owns the 4 x 4 sub-block rows 4*(t/16).., columns 4*(t%16)..
-    const int i0 = 4 * (t >> 4), k0 = 4 * (t & 15);
+    const int ib = t >> 4, kb = t & 15;        // this thread's tile: rows 4*ib.., columns 4*kb..
+    const int i0 = 4 * ib, k0 = 4 * kb;
+    float a[4][4], s[4][4];
 #pragma unroll
     for (int di = 0; di < 4; ++di)
 #pragma unroll
         for (int dk = 0; dk < 4; ++dk) {
             const int i = i0 + di, k = k0 + dk;
-            a[i][k] = (i <= k && k < m) ? A[(int64_t)i * ld + k] : 0.f;
-            u[i][k] = 0.f;
+            const int r = min(min(i, k), m - 1), c = min(max(i, k), m - 1);   // upper triangle only
+            a[di][dk] = A[(int64_t)r * ld + c];
         }
-    __syncthreads();
-    // reversed-order Cholesky: column j from the last to the first
-    for (int j = m - 1; j >= 0; --j) {
-        float piv = a[j][j];
-        if (!(piv > 0.f)) {
-            if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
-            piv = 1.f;
-        }
-        const float rjj = sqrtf(piv);
-        __syncthreads();
-        // R[i][j] = A[i][j] / R[j][j] (i < j), by the owners of column j
-        if (j >= k0 && j < k0 + 4) {
 #pragma unroll
-            for (int di = 0; di < 4; ++di) {
-                const int i = i0 + di;
-                if (i < j) a[i][j] = a[i][j] / rjj;
-                else if (i == j) a[j][j] = rjj;
+    for (int di = 0; di < 4; ++di)
+#pragma unroll
+        for (int dk = 0; dk < 4; ++dk) {
+            const int i = i0 + di, k = k0 + dk;
+            if (i >= m || k >= m) a[di][dk] = (i == k) ? 1.f : 0.f;
+            s[di][dk] = (i == k) ? 1.f : 0.f;
+        }
+    if (kb == 15) *(float4*)&colb[63][i0] = make_float4(a[0][3], a[1][3], a[2][3], a[3][3]);
+    if (ib == 15) *(float4*)&rowb[63][k0] = make_float4(s[3][0], s[3][1], s[3][2], s[3][3]);
+    for (int jb = 15; jb >= 0; --jb) {
+#pragma unroll
+        for (int dj = 3; dj >= 0; --dj) {
+            const int j = 4 * jb + dj;
+            __syncthreads();
+            float piv = colb[j][j];
+            const float4 ci = *(const float4*)&colb[j][i0];
+            const float4 ck = *(const float4*)&colb[j][k0];
+            const float4 rj = *(const float4*)&rowb[j][k0];
+            if (!(piv > 0.f)) {
+                if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
+                piv = 1.f;
             }
-        }
-        __syncthreads();
-        // A[i][k] -= R[i][j] R[k][j] for 0 <= i <= k < j
-        if (i0 < j && k0 < j) {
-            float ck[4];
+            const float r = 1.f / sqrtf(piv);
+            const float civ[4] = {ci.x, ci.y, ci.z, ci.w};
+            const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
+            const float rjv[4] = {rj.x, rj.y, rj.z, rj.w};
+            float Ri[4], Rk[4], Uj[4];
 #pragma unroll
-            for (int dk = 0; dk < 4; ++dk) ck[dk] = a[k0 + dk][j];
+            for (int q = 0; q < 4; ++q) {
+                Ri[q] = (i0 + q < j) ? civ[q] * r : 0.f;
+                Rk[q] = (k0 + q < j) ? ckv[q] * r : 0.f;
+                Uj[q] = rjv[q] * r;
+            }
+            if (ib == jb) {
 #pragma unroll
-            for (int di = 0; di < 4; ++di) {
-                const int i = i0 + di;
-                const float ri = a[i][j];
+                for (int q = 0; q < 4; ++q) s[dj][q] = Uj[q];
+            }
 #pragma unroll
-                for (int dk = 0; dk < 4; ++dk) {
-                    const int k = k0 + dk;
-                    if (i <= k && k < j) a[i][k] -= ri * ck[dk];
+            for (int di = 0; di < 4; ++di)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    a[di][q] -= Ri[di] * Rk[q];
+                    s[di][q] -= Ri[di] * Uj[q];
                 }
+            if (j > 0) {   // publish column j-1 of A and row j-1 of S (final after this update)
+                const int djn = (dj + 3) & 3;
+                const int jn = j - 1, jbn = jn >> 2;
+                if (kb == jbn)
+                    *(float4*)&colb[jn][i0] = make_float4(a[0][djn], a[1][djn], a[2][djn], a[3][djn]);
+                if (ib == jbn)
+                    *(float4*)&rowb[jn][k0] = make_float4(s[djn][0], s[djn][1], s[djn][2], s[djn][3]);
             }
         }
-        __syncthreads();
-    }
-    // U = R^-1, row by row from the bottom: U[i][i] = 1/R[i][i],
-    // U[i][c] = -(sum_{k=i+1..c} R[i][k] U[k][c]) / R[i][i]
-    // 4 threads per column c, each summing a strided quarter of k.
-    const int c = t >> 2, part = t & 3;
-    for (int i = m - 1; i >= 0; --i) {
-        float s = 0.f;
-        if (c < m && c > i)
-            for (int k = i + 1 + part; k <= c; k += 4) s += a[i][k] * u[k][c];
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if (c < m && part == 0) {
-            if (c == i) u[i][i] = 1.f / a[i][i];
-            else if (c > i) u[i][c] = -s / a[i][i];
-        }
-        __syncthreads();
     }
 #pragma unroll
     for (int di = 0; di < 4; ++di)
 #pragma unroll
         for (int dk = 0; dk < 4; ++dk) {
             const int i = i0 + di, k = k0 + dk;
-            if (i < m && k < m) U[(int64_t)i * ld + k] = (i <= k) ? u[i][k] : 0.f;
+            if (i < m && k < m) U[(int64_t)i * ld + k] = s[di][dk];
         }
 }
 
