@@ -8,17 +8,18 @@
 // the work runs as GEMMs) and the blocked products of the recursive
 // Cholesky / triangular inverse that produce U.
 //
-// Tile: 128 x 128 per workgroup of 256 threads (4 wave64s in 2 x 2), each
-// wave 64 x 64 = 2 x 2 MFMA 32x32 blocks; K staged through LDS 32 at a time,
-// double buffered through registers. LDS tiles are k-major (As[k][m],
-// Bs[k][n]) so an MFMA operand fetch is one conflict-free ds_read_b32 per
-// lane whatever the global layout; K-contiguous global layouts are
-// transposed while staging. Within a 32-deep K tile, each MFMA step (k = 2
-// per step) takes one k-row from lanes 0-31 and the row 8 further from lanes
-// 32-63 (the contraction is order-free); with a 132-float LDS row the two
-// half-waves read disjoint banks. Operand layouts are template parameters and interior
-// tiles take an unguarded load path, so the main loop has no divergent
-// branches; every operand read of a stage is issued before its MFMAs.
+// Two kernels share the 128 x 128 workgroup tile (256 threads, 4 wave64s in
+// 2 x 2, each wave 64 x 64 = 2 x 2 MFMA 32x32 blocks):
+//
+//  * gemm_f32_direct_kernel (below) for A K-contiguous and K, leading
+//    dimensions a multiple of 4: every product on the hot path;
+//  * gemm_f32_kernel, the general fallback (any layout, any K): K staged
+//    through LDS 32 at a time, double buffered through registers, k-major LDS
+//    tiles (K-contiguous operands transposed while staging) read with one
+//    ds_read_b32 per lane and MFMA step; each step takes one k-row from
+//    lanes 0-31 and the row 8 further from lanes 32-63, and the 132-float
+//    LDS row puts the two half-waves in disjoint banks. Interior tiles take
+//    an unguarded load path.
 #include "common.hpp"
 
 namespace ptq {
@@ -198,11 +199,293 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmArgs g) {
         }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for A K-contiguous (A_MK) and B either K-contiguous
+// (B_NK) or N-contiguous (B_KN): the forms every hot product of the path has.
+// global_load_lds_dwordx4 moves each lane's 16 bytes straight into LDS at
+// base + 16 * lane, so there is no register staging and no ds_write; the
+// layouts below are chosen on the global side (which chunk a lane fetches).
+//
+//   K-contiguous operand: LDS row = one m (or n) index, the stage's 16
+//     floats of k in four 16-byte chunks, chunk c stored at
+//     c ^ ((row >> 2) & 3). An MFMA operand fetch is one ds_read_b128 (4
+//     consecutive k) per lane, free of bank conflicts for each 16-lane group.
+//   N-contiguous operand: LDS row = one k, 128 floats of n in 32 chunks,
+//     chunk c stored at c ^ (8 * ((k >> 2) & 1)): the two half-waves of a
+//     ds_read_b32 (rows k and k + 4) fall in opposite halves of the banks.
+//
+// The contraction order inside an 8-deep step j is fixed by the ds_read_b128
+// fragments: MFMA e of the step takes k = 8j + e from lanes 0-31 and
+// k = 8j + 4 + e from lanes 32-63, for both operands.
+//
+// A ring of four 16-deep stages (64 KB, two workgroups per CU) keeps three
+// stages of loads in flight; one barrier per stage (no memory fence: waits
+// count only this wave's own loads, which retire in order) publishes every
+// wave's copies. Fragment reads of the next step ride under the MFMAs of the
+// current one. Rows (columns) past M (N) and k past K read clamped, valid
+// addresses; k past K is zeroed in the fragments of the last stage and the
+// other rows are discarded by the epilogue. Requires K, lda, ldb (and N for
+// B_KN) multiples of 4 and 16-byte aligned A and B.
+constexpr int DBK = 16;                 // k per stage
+constexpr int DNST = 4;                 // stages in the ring
+constexpr int DWG = 2;                  // workgroups per CU the kernel is built for
+constexpr int DSTAGE_BYTES = 2 * BM * DBK * 4;   // A and B tiles of one stage
+constexpr int DQ = BM * DBK * 4 / 1024 / 4;     // 1 KB copies per wave per operand per stage
+constexpr int DJ = DBK / 8;                      // 8-deep MFMA steps per stage
+constexpr int DCH = DBK / 4;                     // 16-byte chunks per K-contiguous LDS row
+constexpr int XCDS = 8;                          // accelerator complex dies, one L2 each
+static_assert(DJ % 2 == 0 && DNST >= 3, "fragment slots alternate; the ring needs three stages");
+
+typedef __attribute__((address_space(3))) void* lds_ptr_f32_t;
+
+// chunk swizzle of a K-contiguous LDS row r: the 16 rows one ds_read_b128
+// pass serves land on distinct 4-bank groups
+__device__ __forceinline__ int kswz(int r) {
+    static_assert(DCH == 8 || DCH == 4, "swizzle for 8 or 4 chunks per row");
+    return DCH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+template <int N>
+__device__ __forceinline__ void f32_wait_vmcnt() {
+    // s_waitcnt vmcnt(N) (bits 3:0 and 15:14), expcnt and lgkmcnt at their maxima
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool B_KMAJOR>
+__global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
+    // Tile order. blockIdx b runs on XCD b % 8. With at least 8 tile rows,
+    // XCD x takes the whole rows x, x + 8, x + 16, ... in row-major order:
+    // the tiles one XCD runs side by side share A panels (and B panels across
+    // its rows) in its own L2, and the rows' alternation keeps the triangular
+    // products (A upper, upper_only), whose work varies by row, balanced over
+    // the XCDs. Fewer rows: plain row-major order over all XCDs.
+    int64_t tm, tn;
+    if (tiles_m >= XCDS) {
+        const int64_t x = blockIdx.x % XCDS, i = blockIdx.x / XCDS;
+        tm = x + XCDS * (i / tiles_n);
+        tn = i % tiles_n;
+        if (tm >= tiles_m) return;
+    } else {
+        if ((int64_t)blockIdx.x >= tiles_m * tiles_n) return;
+        tm = blockIdx.x / tiles_n;
+        tn = blockIdx.x % tiles_n;
+    }
+    if (g.upper_only && tm > tn) return;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+
+    int64_t kb = 0, ke = g.K;
+    if (g.tri == TRI_A_UPPER) kb = m0;
+    else if (g.tri == TRI_B_UPPER_NK) kb = n0;
+    else if (g.tri == TRI_B_UPPER_KN) ke = min(g.K, n0 + BN);
+    kb = (kb / DBK) * DBK;
+    const int64_t nst = (ke > kb) ? cdiv(ke - kb, DBK) : 0;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int li = lane & 31, lh = lane >> 5;
+
+    // per-lane global offsets (elements) of the chunks this lane moves, at k = 0
+    int64_t offA[DQ], offB[DQ];
+    int kcA[DQ], kcB[DQ];        // k offset of the chunk (K-contiguous) or k row (N-contiguous)
+#pragma unroll
+    for (int q = 0; q < DQ; ++q) {
+        const int p = (wave * DQ + q) * 64 + lane;     // 16-byte position in the stage's tile
+        {
+            const int r = p / DCH, pc = p % DCH;
+            const int c = pc ^ kswz(r);
+            const int64_t row = min(m0 + r, g.M - 1);
+            offA[q] = row * g.lda;
+            kcA[q] = 4 * c;
+        }
+        if (!B_KMAJOR) {
+            const int r = p / DCH, pc = p % DCH;
+            const int c = pc ^ kswz(r);
+            const int64_t row = min(n0 + r, g.N - 1);
+            offB[q] = row * g.ldb;
+            kcB[q] = 4 * c;
+        } else {
+            const int kr = p >> 5, pc = p & 31;
+            const int c = pc ^ (8 * ((kr >> 2) & 1));
+            const int64_t col = min(n0 + 4 * c, g.N - 4);
+            offB[q] = col;
+            kcB[q] = kr;
+        }
+    }
+
+    auto issue = [&](int64_t s, int buf) {
+        const int64_t k0 = kb + s * DBK;
+        unsigned char* sa = dsm + buf * DSTAGE_BYTES;
+        unsigned char* sb = sa + BM * DBK * 4;
+#pragma unroll
+        for (int q = 0; q < DQ; ++q) {
+            const int64_t k = min(k0 + kcA[q], g.K - 4);
+            __builtin_amdgcn_global_load_lds((const void*)(g.A + offA[q] + k),
+                                             (lds_ptr_f32_t)(sa + (wave * DQ + q) * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < DQ; ++q) {
+            const float* src;
+            if (!B_KMAJOR) {
+                const int64_t k = min(k0 + kcB[q], g.K - 4);
+                src = g.B + offB[q] + k;
+            } else {
+                const int64_t k = min(k0 + kcB[q], g.K - 1);
+                src = g.B + k * g.ldb + offB[q];
+            }
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_f32_t)(sb + (wave * DQ + q) * 1024), 16, 0,
+                                             0);
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // fragments of one 8-deep step j: fa[a] = A[row][8j + 4lh .. +3], fb likewise
+    f32x4 fa[2][2], fb[2][2];
+    const int aswz = kswz(li);
+    auto frags = [&](int64_t s, int j, int slot, bool mask) {
+        const unsigned char* As = dsm + (s % DNST) * DSTAGE_BYTES;
+        const unsigned char* Bs = As + BM * DBK * 4;
+        const int c = (2 * j + lh) ^ aswz;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) fa[slot][a] = *(const f32x4*)(As + (wm + 32 * a + li) * (DBK * 4) + 16 * c);
+        if (!B_KMAJOR) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) fb[slot][b] = *(const f32x4*)(Bs + (wn + 32 * b + li) * (DBK * 4) + 16 * c);
+        } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int n = wn + 32 * b + li;
+                const int pc = (n >> 2) ^ (8 * lh);     // ((k >> 2) & 1) == lh for k = 8j + 4lh + e
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = 8 * j + 4 * lh + e;
+                    fb[slot][b][e] = *(const float*)(Bs + k * (BN * 4) + 16 * pc + 4 * (n & 3));
+                }
+            }
+        }
+        if (mask) {
+            const int64_t kbase = kb + s * DBK + 8 * j + 4 * lh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = kbase + e < g.K;
+#pragma unroll
+                for (int a = 0; a < 2; ++a) fa[slot][a][e] = ok ? fa[slot][a][e] : 0.f;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) fb[slot][b][e] = ok ? fb[slot][b][e] : 0.f;
+            }
+        }
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[slot][a][e], fb[slot][b][e], acc[a][b], 0, 0,
+                                                                    0);
+    };
+    constexpr int NREAD = B_KMAJOR ? 10 : 4;     // LDS reads per fragment set
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < NREAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 - NREAD, 0);
+    };
+
+    if (nst > 0) {
+        const bool tail = (kb + nst * DBK > g.K);     // last stage reaches past K
+#pragma unroll
+        for (int s = 0; s < DNST - 1; ++s) issue(min((int64_t)s, nst - 1), s);
+        f32_wait_vmcnt<2 * DQ * (DNST - 2)>();
+        __builtin_amdgcn_s_barrier();
+        frags(0, 0, 0, tail && nst == 1);
+        for (int64_t s = 0; s + 1 < nst; ++s) {
+#pragma unroll
+            for (int j = 0; j < DJ - 1; ++j) {
+                frags(s, j + 1, (j + 1) & 1, false);
+                mfmas(j & 1);
+                interleave();
+            }
+            f32_wait_vmcnt<2 * DQ * (DNST - 3)>();
+            __builtin_amdgcn_s_barrier();
+            issue(min(s + DNST - 1, nst - 1), (int)((s + DNST - 1) % DNST));
+            frags(s + 1, 0, 0, tail && s + 2 == nst);
+            mfmas((DJ - 1) & 1);
+            interleave();
+        }
+#pragma unroll
+        for (int j = 0; j < DJ - 1; ++j) {
+            frags(nst - 1, j + 1, (j + 1) & 1, tail);
+            mfmas(j & 1);
+            interleave();
+        }
+        mfmas((DJ - 1) & 1);
+        // the ring's last (duplicate) copies must land before the workgroup's
+        // LDS is released
+        f32_wait_vmcnt<0>();
+    }
+
+    // epilogue (same accumulator layout as above)
+    const int mi = (int)min((int64_t)BM, g.M - m0), nj = (int)min((int64_t)BN, g.N - n0);
+    float* Ct = g.C + m0 * g.ldc + n0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int jj = wn + 32 * j + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ii = wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (ii < mi && jj < nj) {
+                    float* c = Ct + (int64_t)ii * g.ldc + jj;
+                    const float v = g.alpha * acc[i][j][r];
+                    *c = g.beta_one ? (*c + v) : v;
+                }
+            }
+        }
+}
+
+template <bool B_KMAJOR>
+int launch_direct(const GemmArgs& a, hipStream_t st) {
+    static bool ready = false;
+    if (!ready) {
+        PTQ_HIP(hipFuncSetAttribute((const void*)gemm_f32_direct_kernel<B_KMAJOR>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, DNST * DSTAGE_BYTES));
+        ready = true;
+    }
+    const int64_t tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    const unsigned grid = (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<B_KMAJOR>), dim3(grid), dim3(NT), DNST * DSTAGE_BYTES, st, a, tm, tn);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
+bool direct_ok(const GemmArgs& a) {
+    if (a.layout_a != A_MK) return false;
+    if (a.K < 4 || a.K % 4 || a.lda % 4 || a.ldb % 4) return false;
+    if (((uintptr_t)a.A | (uintptr_t)a.B) & 15) return false;
+    if (a.layout_b == B_KN && (a.N % 4 || a.N < 4)) return false;
+    return true;
+}
+
 }  // namespace
 
 int launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
     if (a.M <= 0 || a.N <= 0) return PTQ_OK;
     if (a.K <= 0 && a.beta_one) return PTQ_OK;  // C += 0
+    if (direct_ok(a)) return a.layout_b == B_KN ? launch_direct<true>(a, st) : launch_direct<false>(a, st);
     const unsigned tiles = (unsigned)(cdiv(a.M, BM) * cdiv(a.N, BN));
     const bool akm = a.layout_a == A_KM, bkn = a.layout_b == B_KN;
     if (akm && bkn) hipLaunchKernelGGL((gemm_f32_kernel<true, true>), dim3(tiles), dim3(NT), 0, st, a);

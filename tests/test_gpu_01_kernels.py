@@ -15,7 +15,8 @@ from gpu_util import announce, rel_fro, to64, zeros_h
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 130, 77), (128, 128, 16), (300, 260, 300), (5, 9, 3)])
+@pytest.mark.parametrize("M,N,K", [(200, 130, 77), (128, 128, 16), (300, 260, 300), (5, 9, 3), (260, 388, 1000),
+                                   (37, 4, 36)])
 @pytest.mark.parametrize("la,lb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_gemm_f32_layouts(gpu, M, N, K, la, lb):
     from post_int4_weight_amd import api
@@ -68,15 +69,16 @@ def test_gemm_f32_triangles(gpu, tri):
     assert rel_fro(C.cpu().double().numpy(), ref.numpy()) < 1e-5
 
 
-def test_gemm_f32_upper_only(gpu):
+@pytest.mark.parametrize("k", [50, 64])
+def test_gemm_f32_upper_only(gpu, k):
     from post_int4_weight_amd import api
-    announce("gemm_f32 upper_only")
-    n, k = 300, 50
+    announce(f"gemm_f32 upper_only k={k}")
+    n = 300
     g = torch.Generator().manual_seed(7)
     P = torch.randn(n, k, generator=g)
     C0 = torch.randn(n, n, generator=g)
     C = C0.clone().to(gpu)
-    Pd = torch.zeros(n, 52)
+    Pd = torch.zeros(n, (k + 3) // 4 * 4)
     Pd[:, :k] = P
     Pd = Pd.to(gpu)
     api._test_gemm_f32(Pd, Pd, C, n, n, k, 0, 1, alpha=-1.0, beta_one=1, upper_only=1)
