@@ -39,7 +39,45 @@ def parse():
     ap.add_argument("--workload", default="llama70b_down_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="before the steps, run a copy-like elementwise kernel (torch.neg) over 1 GiB of fp32, "
+                         "whose FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "xtx_gemm_down_proj_traffic.md")
+TRAFFIC_SOURCES = ["post_int4_weight_amd/csrc/gemm_bf16.hip", "post_int4_weight_amd/csrc/common.hpp"]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per X^T X launch from the committed FETCH_SIZE / WRITE_SIZE
+    counter runs, each scaled by the factor a 1 GiB copy-like kernel gave in
+    the same run. None when the kernel source changed since they were taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith(("#", "|", " ")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != kernel_source_digest():
+            return None
+        fetch = float(kv["fetch_kib_per_launch"]) * float(kv["copy_fetch_factor"])
+        write = float(kv["write_kib_per_launch"]) * float(kv["copy_write_factor"])
+        return round((fetch + write) * 1024.0)
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, W, X, bits):
@@ -79,7 +117,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the path here is the single-GPU kernel set (--gpus {args.gpus} "
-              "is not supported; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "is not supported: this build measures one GPU's share at its real shape)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -101,6 +139,13 @@ def main():
     ws_h = torch.empty(api.hessian_workspace_bytes(n, N), dtype=torch.uint8, device=dev)
     ws_g = torch.empty(api.gptq_workspace_bytes(o, n, block), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         H.zero_()
@@ -132,8 +177,8 @@ def main():
     avg_launch_s = xtx_ms / 1e3 / max(1, xtx_launches)
     achieved = flops_per_launch / avg_launch_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "gemm_bf16_nt_kernel<256, EPI_HESSIAN> (X^T X tiles)",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                "kernel": "gemm_bf16_nt_direct_kernel<256, 0> (X^T X tiles, one launch per 65536-row chunk)",
                 "avg_launch_ms": round(avg_launch_s * 1e3, 3), "launches": xtx_launches}
 
     breakdown = None

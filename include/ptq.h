@@ -157,7 +157,8 @@ int gptq_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t in, i
  * column sums of squares (may be NULL). perm may be NULL when act_order == 0.
  * stats (host, may be NULL) double[4]: [0] sum err^2, [1] lambda,
  * [2] ||dW||_F^2, [3] calibration objective ||X dW^T||^2 =
- * stats[0] - lambda * stats[2] (an identity of the loop; see DESIGN).
+ * stats[0] - lambda * stats[2] (for any rounding, sum err^2 = tr(dW (H0 +
+ * lambda I) dW^T), so the undamped objective follows by subtraction).
  * Synchronous. Errors: union of the two stages.
  * ---------------------------------------------------------------------- */
 size_t gptq_workspace_bytes(int64_t out, int64_t in, int block_size);

@@ -20,7 +20,7 @@ Sources (cited by page title and section):
   objective), 2.2 (group size, act-order) and 2.3 (GPTQ equals Babai's
   nearest-plane algorithm on the lattice defined by the Hessian).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * H = X^T X without the factor 2 or a 1/N (codes are invariant to H -> cH
   because the damping is relative);

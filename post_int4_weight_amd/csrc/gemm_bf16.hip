@@ -14,18 +14,16 @@
 //    sum of squares to one fp64 partial per workgroup (E is never written).
 //
 // Tile 256 x 256 (or 128 x 128) per workgroup of 256 threads, 4 wave64s in
-// 2 x 2, each wave a (BM/2)^2 block of 32x32 MFMA accumulators. K is staged
-// 64 at a time through LDS (dynamic, double buffered): 16-byte chunks go
-// from global memory through registers into 128-byte LDS rows whose chunk
-// index is XOR-swizzled by (row >> 1) & 7, so both the staging writes (2 rows
-// x 8 chunks per 16 lanes) and the ds_read_b128 operand fetches (16 rows x 1
-// chunk) are free of bank conflicts. A stage is 64 MFMAs per wave, long enough
-// to cover the latency of the next stage's global loads.
+// 2 x 2, each wave a (BM/2)^2 block of 32x32 MFMA accumulators. Two main
+// loops: the direct-to-LDS one (K segments multiples of 32, every call on the
+// path) described further down, and a register-staged one for any K: 16-byte
+// chunks go through registers into 128-byte LDS rows whose chunk index is
+// XOR-swizzled by (row >> 1) & 7, so the staging writes and the ds_read_b128
+// operand fetches are free of bank conflicts.
 //
-// Workgroup order is XCD-aware: blockIdx b runs on XCD b % 8, so logical work
-// items are handed out in contiguous runs per XCD; Hessian tiles are ordered
-// in bands of 4 tile-rows so the ~32 tiles one XCD holds at a time reuse a
-// dozen panels from its L2.
+// Workgroup order is XCD-aware (blockIdx b runs on XCD b % 8): Hessian tiles
+// go in rounds of 16 x 16 super-blocks split into one 4 x 8 sub-block per XCD
+// (see hessian_tile); AWQ tiles in contiguous runs per XCD.
 #include "common.hpp"
 
 #include <algorithm>
@@ -37,7 +35,6 @@ constexpr int KT = 64;              // contraction depth per LDS stage
 constexpr int ROWB = KT * 2;        // bytes per staged row
 constexpr int CPR = ROWB / 16;      // 16-byte chunks per staged row
 constexpr int NTH = 256;
-constexpr int BAND = 4;
 constexpr int NXCD = 8;
 
 enum { EPI_HESSIAN = 0, EPI_SUMSQ = 1 };
@@ -47,29 +44,32 @@ __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + 16 * (c ^ (
 template <int BMX>
 constexpr int smem_bytes() { return 4 * BMX * ROWB; }   // A and B, two stages each
 
-// Upper-triangle tile at position L of the band order (T tile-rows).
-__device__ __forceinline__ void band_tile(int64_t L, int T, int& ti, int& tj) {
-    int r0 = 0;
-    while (true) {
-        const int h = min(BAND, T - r0);
-        const int64_t tri = (int64_t)h * (h + 1) / 2;
-        const int64_t cnt = tri + (int64_t)(T - r0 - h) * h;
-        if (L < cnt) {
-            if (L < tri) {
-                int c = 0;
-                while ((int64_t)(c + 1) * (c + 2) / 2 <= L) ++c;
-                tj = r0 + c;
-                ti = r0 + (int)(L - (int64_t)c * (c + 1) / 2);
-            } else {
-                const int64_t q = L - tri;
-                tj = r0 + h + (int)(q / h);
-                ti = r0 + (int)(q % h);
-            }
-            return;
-        }
-        L -= cnt;
-        r0 += h;
+// Hessian tiles (upper triangle of a T x T tile grid) in rounds of 256
+// workgroups; workgroup b runs on XCD b % 8. Round r is the r-th SB x SB
+// super-block (P <= Q, row-major) and XCD x takes its 4 x 8 sub-block (rows
+// 4 (x / 2).., columns 8 (x % 2)..): the 256 tiles of a round, which start
+// together and move through k together, read 32 panels (16 on the diagonal),
+// so the die-shared last-level cache serves most of what one XCD's L2
+// misses, and the 32 tiles of one XCD read 12 panels through its own L2.
+// Slots outside the triangle or the grid return at once.
+constexpr int SB = 16;
+__host__ __device__ inline int64_t hessian_rounds(int T) {
+    const int64_t nb = cdiv(T, SB);
+    return nb * (nb + 1) / 2;
+}
+__device__ __forceinline__ bool hessian_tile(int64_t b, int T, int& ti, int& tj) {
+    const int nb = (int)cdiv(T, SB);
+    int64_t r = b / 256;
+    const int w = (int)(b % 256), x = w % NXCD, i = w / NXCD;
+    int P = 0;
+    while (r >= nb - P) {
+        r -= nb - P;
+        ++P;
     }
+    const int Q = P + (int)r;
+    ti = SB * P + 4 * (x >> 1) + (i >> 3);
+    tj = SB * Q + 8 * (x & 1) + (i & 7);
+    return ti < T && tj < T && ti <= tj;
 }
 
 struct Bf16GemmArgs {
@@ -147,19 +147,19 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[
 template <int BMX, int EPI>
 __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, int64_t nwork) {
     constexpr int WT = BMX / 64;
-    const int64_t per = (nwork + NXCD - 1) / NXCD;
-    const int64_t L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
-    if (L >= nwork) return;
-
-    int64_t i0, j0;
+    int64_t i0, j0, L = 0;
     bool diag = false;
     if (EPI == EPI_HESSIAN) {
         int ti, tj;
-        band_tile(L, g.T, ti, tj);
+        if (!hessian_tile(blockIdx.x, g.T, ti, tj)) return;
         i0 = (int64_t)ti * BMX;
         j0 = (int64_t)tj * BMX;
         diag = (ti == tj);
     } else {
+        // row-major tiles, a contiguous run per XCD
+        const int64_t per = (nwork + NXCD - 1) / NXCD;
+        L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
+        if (L >= nwork) return;
         i0 = (L / g.tiles_n) * BMX;
         j0 = (L % g.tiles_n) * BMX;
     }
@@ -334,19 +334,19 @@ template <int BMX, int EPI>
 __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g, int64_t nwork) {
     constexpr int WT = BMX / 64;
     constexpr int PER = BMX / 64;      // load instructions per wave per panel per stage (BMX*4 chunks / 64 / 4 waves)
-    const int64_t per = (nwork + NXCD - 1) / NXCD;
-    const int64_t L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
-    if (L >= nwork) return;
-
-    int64_t i0, j0;
+    int64_t i0, j0, L = 0;
     bool diag = false;
     if (EPI == EPI_HESSIAN) {
         int ti, tj;
-        band_tile(L, g.T, ti, tj);
+        if (!hessian_tile(blockIdx.x, g.T, ti, tj)) return;
         i0 = (int64_t)ti * BMX;
         j0 = (int64_t)tj * BMX;
         diag = (ti == tj);
     } else {
+        // row-major tiles, a contiguous run per XCD
+        const int64_t per = (nwork + NXCD - 1) / NXCD;
+        L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
+        if (L >= nwork) return;
         i0 = (L / g.tiles_n) * BMX;
         j0 = (L % g.tiles_n) * BMX;
     }
@@ -418,6 +418,26 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
 #pragma unroll
         for (int b = 0; b < WT; ++b) fb[slot][b] = *(const bf16x8*)(Bs + (wn + 32 * b + li) * DROWB + 16 * c);
     };
+    // single-instruction pieces for the hand-interleaved half-stage below
+    auto load_one = [&](int64_t s, int buf, int q) {
+        const bool seg1 = s < n1;
+        const bool isa = q < PER;
+        const int qq = isa ? q : q - PER;
+        const uint16_t* P = isa ? ((seg1 ? g.A1 : g.A2) + (seg1 ? s : s - n1) * DK + offA[qq])
+                                : ((seg1 ? B1 : B2) + (seg1 ? s : s - n1) * DK + offB[qq]);
+        unsigned char* dst = smem + buf * (2 * BMX * DROWB) + (isa ? 0 : BMX * DROWB) + (wave * PER + qq) * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)P, (lds_ptr_t)dst, 16, 0, 0);
+    };
+    auto read_one = [&](int64_t s, int kk, int slot, int q) {
+        const unsigned char* As = smem + (s % NSTAGE) * (2 * BMX * DROWB);
+        const int c = (2 * kk + lh) ^ fsw;
+        if (q < WT) fa[slot][q] = *(const bf16x8*)(As + (wm + 32 * q + li) * DROWB + 16 * c);
+        else fb[slot][q - WT] = *(const bf16x8*)(As + BMX * DROWB + (wn + 32 * (q - WT) + li) * DROWB + 16 * c);
+    };
+    auto mfma_one = [&](int slot, int idx) {
+        const int a = idx / WT, b = idx % WT;
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][a], fb[slot][b], acc[a][b], 0, 0, 0);
+    };
     auto mfmas = [&](int slot) {
 #pragma unroll
         for (int a = 0; a < WT; ++a)
@@ -451,10 +471,21 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
             interleave();
             wait_vmcnt<2 * PER>();
             __builtin_amdgcn_s_barrier();
-            issue(std::min<int64_t>(s + NSTAGE - 1, nst - 1), (int)((s + NSTAGE - 1) % NSTAGE));
-            frags(s + 1, 0, 0);
-            mfmas(1);
-            interleave();
+            {
+                // one copy, one fragment read and WT/2 MFMAs per group, pinned
+                // in that order: a copy that waits for the address unit then
+                // stalls at most WT/2 MFMAs' worth of issue
+                const int64_t sl = std::min<int64_t>(s + NSTAGE - 1, nst - 1);
+                const int bl = (int)((s + NSTAGE - 1) % NSTAGE);
+#pragma unroll
+                for (int q = 0; q < 2 * WT; ++q) {
+#pragma unroll
+                    for (int m = 0; m < WT / 2; ++m) mfma_one(1, q * (WT / 2) + m);
+                    read_one(s + 1, 0, 0, q);
+                    load_one(sl, bl, q);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
         frags(nst - 1, 1, 1);
         mfmas(0);
@@ -483,7 +514,7 @@ int prepare_kernel() {
 // Launch either variant: the direct one when both K segments are multiples of DK.
 template <int BMX, int EPI>
 int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t st) {
-    const unsigned grid = (unsigned)(cdiv(nwork, NXCD) * NXCD);
+    const unsigned grid = (unsigned)(EPI == EPI_HESSIAN ? 256 * hessian_rounds(g.T) : cdiv(nwork, NXCD) * NXCD);
     if (g.K1 % DK == 0 && g.K2 % DK == 0 && g.M > 0 && g.N > 0) {
         PTQ_TRY((prepare_kernel<BMX, EPI, true>()));
         hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI>), dim3(grid, grid_y), dim3(NTH),
@@ -497,9 +528,10 @@ int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t
     return PTQ_OK;
 }
 
-// Xt[c][r] = X[r0 + r][c] for r < nr; rows nr..ldt-1 of Xt are zeroed.
+// Xt[c][r] = X[r0 + r][c] for r < nr; entries nr <= r < kt of each Xt row are
+// zeroed (the row stride ldt may be larger; that tail is never read).
 __global__ void transpose_rows_kernel(const uint16_t* __restrict__ X, int64_t ldx, int64_t n, int64_t r0,
-                                      int64_t nr, uint16_t* __restrict__ Xt, int64_t ldt) {
+                                      int64_t nr, uint16_t* __restrict__ Xt, int64_t ldt, int64_t kt) {
     __shared__ uint16_t tile[64][66];
     const int64_t cb = (int64_t)blockIdx.x * 64, rb = (int64_t)blockIdx.y * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 256 threads: 64 x 4
@@ -510,7 +542,7 @@ __global__ void transpose_rows_kernel(const uint16_t* __restrict__ X, int64_t ld
     __syncthreads();
     for (int y = ty; y < 64; y += 4) {
         const int64_t c = cb + y, r = rb + tx;
-        if (c < n && r < ldt) Xt[c * ldt + r] = tile[tx][y];
+        if (c < n && r < kt) Xt[c * ldt + r] = tile[tx][y];
     }
 }
 
@@ -574,6 +606,10 @@ __global__ void reduce_slabs_kernel(double* d, const double* part, int nslab, in
 constexpr int64_t SLAB_ROWS = 2048;
 constexpr int MAX_SLABS = 256;
 constexpr int64_t CHUNK_ROWS_MAX = 65536;   // calibration rows per transposed chunk
+// Row stride of the transposed chunk = its depth + XT_PAD elements: a
+// power-of-two stride (65536 bf16 = 128 KB) would send the 256 rows of a
+// panel slice to the same L2 channel and set.
+constexpr int64_t XT_PAD = 64;
 
 struct XtxPlan {
     int bm, T, nsplit;
@@ -585,7 +621,7 @@ struct XtxPlan {
 size_t plan_bytes(const XtxPlan& p, int64_t n) {
     Sizer z;
     if (p.nslab > 1) z.take<double>((size_t)p.nslab * n);
-    z.take<uint16_t>((size_t)n * p.chunk);
+    z.take<uint16_t>((size_t)n * (p.chunk + XT_PAD));
     if (p.nsplit > 1) z.take<float>((size_t)p.nsplit * n * n);
     return z.bytes();
 }
@@ -649,20 +685,21 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
         return PTQ_OK;
     }
 
-    uint16_t* Xt = ar.take<uint16_t>((size_t)n * p.chunk);
+    uint16_t* Xt = ar.take<uint16_t>((size_t)n * (p.chunk + XT_PAD));
     float* hpart = (p.nsplit > 1) ? ar.take<float>((size_t)p.nsplit * n * n) : nullptr;
     const int64_t ntiles = (int64_t)p.T * (p.T + 1) / 2;
     for (int64_t r0 = 0; r0 < rows; r0 += p.chunk) {
         const int64_t nr = std::min<int64_t>(p.chunk, rows - r0);
-        const int64_t ldt = cdiv(nr, 64) * 64;
-        hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)(ldt / 64)),
-                           dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt);
+        const int64_t kt = cdiv(nr, 64) * 64;     // contraction depth of this chunk (zero-padded rows)
+        const int64_t ldt = kt + XT_PAD;
+        hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)(kt / 64)),
+                           dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt, kt);
         PTQ_LAUNCH_CHECK();
         const bool last = r0 + p.chunk >= rows;
         const int ns = (p.nsplit > 1 && nr >= p.nsplit * 4096) ? p.nsplit : 1;
-        const int64_t kper = cdiv(cdiv(ldt, ns), KT) * KT;
+        const int64_t kper = cdiv(cdiv(kt, ns), KT) * KT;
         for (int s = 0; s < ns; ++s) {
-            const int64_t kb = s * kper, ke = std::min<int64_t>(ldt, kb + kper);
+            const int64_t kb = s * kper, ke = std::min<int64_t>(kt, kb + kper);
             Bf16GemmArgs g{};
             g.A1 = Xt + kb; g.B1 = Xt + kb; g.A2 = nullptr; g.B2 = nullptr;
             g.K1 = std::max<int64_t>(0, ke - kb); g.K2 = 0;
