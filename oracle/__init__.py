@@ -8,10 +8,12 @@ from .gptq import (qmax, hessian_nbytes, proxy_hessian, damped, act_order_permut
                    inverse_upper_factor, gptq_columns, rtn, dequantize, gptq_layer,
                    output_error, output_energy, quadratic_error)
 from .awq import channel_mean_abs, awq_quantize, awq_search
+from .pack import pack_int4, unpack_int4, dequantize_packed
 
 __all__ = [
     "qmax", "hessian_nbytes", "proxy_hessian", "damped", "act_order_permutation",
     "inverse_upper_factor", "gptq_columns", "rtn", "dequantize", "gptq_layer",
     "output_error", "output_energy", "quadratic_error",
     "channel_mean_abs", "awq_quantize", "awq_search",
+    "pack_int4", "unpack_int4", "dequantize_packed",
 ]

@@ -329,11 +329,42 @@ def check_hessian_sizes(impl):
         assert abs(impl.hessian_nbytes(n) - printed) <= precision / 2, (n, impl.hessian_nbytes(n))
 
 
+def check_pack_hand(impl):
+    gd = load_golden("pack_hand.json")["pack"]
+    words = impl.pack_int4(np.array(gd["codes"]))
+    assert words.dtype == np.uint32
+    assert np.array_equal(words.astype(np.int64), np.array(gd["words"], dtype=np.int64))
+    assert np.array_equal(impl.unpack_int4(words, 8), np.array(gd["codes"]))
+
+
+def check_pack_roundtrip(impl):
+    """Every nibble value at every position survives pack -> unpack."""
+    vals = np.arange(-8, 8)
+    codes = np.stack([np.roll(vals, s)[:16] for s in range(16)])       # [16, 16]: each value at each column
+    assert np.array_equal(impl.unpack_int4(impl.pack_int4(codes), 16), codes)
+    rng = np.random.default_rng(21)
+    c = rng.integers(-8, 8, size=(7, 40))
+    assert np.array_equal(impl.unpack_int4(impl.pack_int4(c), 40), c)
+
+
+def check_dequant_g_idx_hand(impl):
+    gd = load_golden("pack_hand.json")["dequant_g_idx"]
+    packed = impl.pack_int4(np.array(gd["codes"]))
+    What = impl.dequantize_packed(packed, np.array(gd["scales"]), np.array(gd["g_idx"]), 8)
+    assert np.array_equal(What, np.array(gd["What"]))
+    assert not np.array_equal(What, np.array(gd["What_ignoring_g_idx"]))
+    # same as dequantizing in processing order and un-permuting
+    perm = np.array(gd["perm"])
+    codes = np.array(gd["codes"])
+    proc = impl.dequantize(codes[:, perm], np.array(gd["scales"]), np.arange(8) // gd["g"])
+    assert np.array_equal(What[:, perm], proc)
+
+
 ALL_CHECKS = [
     check_rtn_hand, check_gptq_hand, check_damping_hand, check_act_order_hand,
     check_hessian_bruteforce, check_hessian_orthogonal, check_hessian_chunking,
     check_inverse_factor_closed_form, check_inverse_factor_identity, check_diagonal_H_is_rtn,
     check_babai_identity, check_babai_equivalence, check_grid_and_invariances,
     check_gptq_beats_rtn_correlated, check_act_order_matches_permuted_problem, check_awq,
-    check_hessian_sizes,
+    check_hessian_sizes, check_pack_hand, check_pack_roundtrip, check_dequant_g_idx_hand,
 ]

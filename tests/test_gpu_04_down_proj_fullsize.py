@@ -10,6 +10,9 @@ on what it can compute exactly:
     (H = R R^T with R upper: the trailing block of R, hence of U = R^-1,
     is the reversed Cholesky of H's trailing block);
   * the first group's scales (the loop has not touched those columns yet);
+  * the column loop on 8 sampled rows (rows are independent in the loop), run
+    by the oracle in fp64 on the device's U once U has passed the checks
+    above: >= 99% equal codes, relative output error within 1%;
 and on properties that hold at any size, evaluated in fp64 on the device:
   * U H_d U^T = I on sampled rows;
   * the loop identity sum err^2 = tr(dW H_d dW^T) over all rows;
@@ -21,11 +24,12 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, rel_fro, to64, zeros_h
+from gpu_util import announce, code_match, rel_fro, to64, zeros_h
 
 pytestmark = pytest.mark.gpu
 
 TRAIL = 512
+SAMPLE_ROWS = 8
 
 
 @pytest.fixture(scope="module")
@@ -103,6 +107,17 @@ def test_gptq_fullsize(down_proj, bits):
         assert float((w - e).abs().max()) <= 1e-3, i
     del U64
 
+    # the column loop on sampled rows: rows are independent in the loop, so
+    # the oracle's fp64 loop runs them alone, on this (checked) U
+    rows = list(range(0, out, out // SAMPLE_ROWS))
+    Uh = U.cpu().numpy().astype(np.float64)
+    c_ref, s_ref, _ = oracle.gptq_columns(to64(W[rows].cpu()), Uh, bits, 128)
+    del Uh
+    c_gpu = res["codes"][rows].cpu().numpy()
+    assert code_match(c_gpu, c_ref) >= 0.99, code_match(c_gpu, c_ref)
+    print(f"[oracle] loop on {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal",
+          flush=True)
+
     codes = res["codes"]
     q = 2 ** (bits - 1) - 1
     assert int(codes.min()) >= -q - 1 and int(codes.max()) <= q
@@ -122,6 +137,17 @@ def test_gptq_fullsize(down_proj, bits):
     obj = float(((dW @ Hd) * dW).sum())
     assert abs(res["stats"]["objective"] - obj) <= 2e-3 * obj
     print("[check] loop identities checked", flush=True)
+    # relative output error of the sampled rows within 1% of the oracle's
+    gi = torch.arange(n, device=W.device) // 128
+    Ws = W[rows].double()
+    dWg = Ws - codes[rows].double() * scales[rows].double()[:, gi]
+    dWr = Ws - torch.tensor(c_ref, device=W.device, dtype=torch.float64) * \
+        torch.tensor(s_ref, device=W.device)[:, gi]
+    den = float(((Ws @ Hd) * Ws).sum())
+    e_gpu = float(((dWg @ Hd) * dWg).sum()) / den
+    e_ref = float(((dWr @ Hd) * dWr).sum()) / den
+    assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
+    print(f"[oracle] sampled rows: relative output error {e_gpu:.6g} vs oracle {e_ref:.6g}", flush=True)
     # calibration error below plain RTN's (the loop's purpose)
     Wrtn_codes, Wrtn_scales = oracle.rtn(to64(W.cpu()), bits, 128)
     Wrtn = torch.tensor(oracle.dequantize(Wrtn_codes, Wrtn_scales, np.arange(n) // 128), device=W.device)

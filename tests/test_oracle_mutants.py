@@ -127,6 +127,34 @@ def _awq_rms(X):
     return np.sqrt(np.mean(X * X, axis=0))                # root-mean-square instead of mean |x|
 
 
+def _pack_reversed(codes):
+    """nibbles in the opposite order inside each word"""
+    codes = np.asarray(codes, dtype=np.int64)
+    out, n = codes.shape
+    words = np.zeros((out, n // 8), dtype=np.uint64)
+    for w in range(n // 8):
+        for k in range(8):
+            words[:, w] |= ((codes[:, 8 * w + k] & 0xF).astype(np.uint64)) << np.uint64(4 * (7 - k))
+    return words.astype(np.uint32)
+
+
+def _unpack_unsigned(packed, n):
+    """nibbles read as unsigned (no sign extension)"""
+    packed = np.asarray(packed, dtype=np.uint64)
+    codes = np.zeros((packed.shape[0], n), dtype=np.int64)
+    for w in range(n // 8):
+        for k in range(8):
+            codes[:, 8 * w + k] = ((packed[:, w] >> np.uint64(4 * k)) & np.uint64(0xF)).astype(np.int64)
+    return codes
+
+
+def _dequant_ignores_g_idx(packed, scales, g_idx, n):
+    """group taken as column // g (processing order assumed), g_idx unused"""
+    scales = np.asarray(scales, dtype=np.float64)
+    g = -(-n // scales.shape[1])
+    return oracle.unpack_int4(packed, n).astype(np.float64) * scales[:, np.arange(n) // g]
+
+
 MUTANTS = {
     "feedback sign flipped": dict(gptq_layer=_layer_with(columns=_columns_factory(sign=-1.0))),
     "error not divided by U_jj": dict(gptq_layer=_layer_with(columns=_columns_factory(divide_by_ujj=False))),
@@ -144,6 +172,9 @@ MUTANTS = {
                                     act_order_permutation=_ties_reversed),
     "awq channels reversed": dict(channel_mean_abs=_awq_channels_reversed),
     "awq rms instead of mean abs": dict(channel_mean_abs=_awq_rms),
+    "int4 nibbles reversed": dict(pack_int4=_pack_reversed),
+    "int4 unpack without sign": dict(unpack_int4=_unpack_unsigned),
+    "dequant ignores g_idx": dict(dequantize_packed=_dequant_ignores_g_idx),
 }
 
 
