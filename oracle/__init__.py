@@ -7,13 +7,13 @@ the seeded generators in ``inputs/`` are the only common dependency.
 from .gptq import (qmax, hessian_nbytes, proxy_hessian, damped, act_order_permutation,
                    inverse_upper_factor, gptq_columns, rtn, dequantize, gptq_layer,
                    output_error, output_energy, quadratic_error)
-from .awq import channel_mean_abs, awq_quantize, awq_search
+from .awq import channel_mean_abs, awq_quantize, awq_search, awq_gptq_layer
 from .pack import pack_int4, unpack_int4, dequantize_packed
 
 __all__ = [
     "qmax", "hessian_nbytes", "proxy_hessian", "damped", "act_order_permutation",
     "inverse_upper_factor", "gptq_columns", "rtn", "dequantize", "gptq_layer",
     "output_error", "output_energy", "quadratic_error",
-    "channel_mean_abs", "awq_quantize", "awq_search",
+    "channel_mean_abs", "awq_quantize", "awq_search", "awq_gptq_layer",
     "pack_int4", "unpack_int4", "dequantize_packed",
 ]

@@ -68,3 +68,26 @@ def awq_search(W, X, alphas, bits: int = 4, g: int = 128):
     codes, scales, What = awq_quantize(W, s, bits, g)
     return {"alpha": float(alphas[best]), "index": best, "errors": errors, "s": s,
             "codes": codes, "scales": scales, "What": What, "m": m}
+
+
+def awq_gptq_layer(W, H0, d, s, bits: int = 4, g: int = 128, damp: float = 0.01, act_order: bool = False):
+    """AWQ's scaling first, GPTQ's rounding after ("GPTQ versus AWQ
+    objectives", "A strong answer": the two compose).
+
+    With X' = X diag(s)^-1 and W' = W diag(s) the layer output is unchanged;
+    GPTQ then runs on the scaled layer as on any layer: H0' = X'^T X' =
+    diag(s)^-1 H0 diag(s)^-1, its fp64 column sums of squares d' = d / s^2,
+    and the damping is taken on H0'. Returns gptq_layer's dict for the
+    scaled layer (codes / scales quantize W') plus "What_orig" = What' / s,
+    the weights the original activations see.
+    """
+    from .gptq import gptq_layer
+    W = np.asarray(W, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    H0 = np.asarray(H0, dtype=np.float64)
+    Ws = W * s[None, :]
+    Hs = H0 / np.outer(s, s)
+    ds = None if d is None else np.asarray(d, dtype=np.float64) / (s * s)
+    res = gptq_layer(Ws, Hs, ds, bits=bits, g=g, damp=damp, act_order=act_order)
+    res["What_orig"] = res["What"] / s[None, :]
+    return res

@@ -360,11 +360,53 @@ def check_dequant_g_idx_hand(impl):
     assert np.array_equal(What[:, perm], proc)
 
 
+def check_awq_gptq(impl):
+    """AWQ scaling then GPTQ ("the two compose"): pinned by its definition
+    through the activations (X' = X / s), by s = 1 (plain GPTQ), by a diagonal
+    H (GPTQ is RTN, so the composition is AWQ's RTN) and by a global rescale
+    of s."""
+    rng = np.random.default_rng(31)
+    n, N = 32, 400
+    base = rng.standard_normal((N, 6))
+    X = (base @ rng.standard_normal((6, n)) + 0.5 * rng.standard_normal((N, n))) * np.exp(rng.standard_normal(n))
+    W = rng.standard_normal((6, n))
+    H0, d = impl.proxy_hessian(X)
+    s = impl.channel_mean_abs(X) ** 0.5
+    for act_order in (False, True):
+        res = impl.awq_gptq_layer(W, H0, d, s, bits=3, g=8, damp=0.01, act_order=act_order)
+        # definition: GPTQ on the scaled layer, its Hessian built from X / s
+        Hs, ds = impl.proxy_hessian(X / s[None, :])
+        ref = impl.gptq_layer(W * s[None, :], Hs, ds, bits=3, g=8, damp=0.01, act_order=act_order)
+        assert np.array_equal(res["codes"], ref["codes"])
+        assert np.allclose(res["scales"], ref["scales"], rtol=1e-12)
+        assert np.array_equal(res["perm"], ref["perm"])
+        assert np.allclose(res["What_orig"], ref["What"] / s[None, :], rtol=1e-12)
+        # the objective in the original basis equals the scaled layer's
+        e_orig = impl.output_error(X, W, res["What_orig"])
+        e_scaled = impl.output_error(X / s[None, :], W * s[None, :], res["What"])
+        assert abs(e_orig - e_scaled) <= 1e-9 * e_orig
+    # s = 1: plain GPTQ
+    one = impl.awq_gptq_layer(W, H0, d, np.ones(n), bits=4, g=8, damp=0.01)
+    plain = impl.gptq_layer(W, H0, d, bits=4, g=8, damp=0.01)
+    assert np.array_equal(one["codes"], plain["codes"])
+    # diagonal H: no feedback, so the composition is AWQ's RTN of W diag(s)
+    Hdiag = np.diag(np.diag(H0))
+    dg = impl.awq_gptq_layer(W, Hdiag, np.diag(H0), s, bits=4, g=8, damp=0.01)
+    c_awq, sc_awq, What_awq = impl.awq_quantize(W, s, 4, 8)
+    assert np.array_equal(dg["codes"], c_awq)
+    assert np.allclose(dg["What_orig"], What_awq, rtol=1e-12)
+    # a global rescale of s changes nothing the original activations see
+    r1 = impl.awq_gptq_layer(W, H0, d, s, bits=4, g=8, damp=0.01)
+    r2 = impl.awq_gptq_layer(W, H0, d, 3.7 * s, bits=4, g=8, damp=0.01)
+    assert np.array_equal(r1["codes"], r2["codes"])
+    assert np.allclose(r1["What_orig"], r2["What_orig"], rtol=1e-12)
+
+
 ALL_CHECKS = [
     check_rtn_hand, check_gptq_hand, check_damping_hand, check_act_order_hand,
     check_hessian_bruteforce, check_hessian_orthogonal, check_hessian_chunking,
     check_inverse_factor_closed_form, check_inverse_factor_identity, check_diagonal_H_is_rtn,
     check_babai_identity, check_babai_equivalence, check_grid_and_invariances,
     check_gptq_beats_rtn_correlated, check_act_order_matches_permuted_problem, check_awq,
-    check_hessian_sizes, check_pack_hand, check_pack_roundtrip, check_dequant_g_idx_hand,
+    check_hessian_sizes, check_pack_hand, check_pack_roundtrip, check_dequant_g_idx_hand, check_awq_gptq,
 ]

@@ -155,6 +155,20 @@ def _dequant_ignores_g_idx(packed, scales, g_idx, n):
     return oracle.unpack_int4(packed, n).astype(np.float64) * scales[:, np.arange(n) // g]
 
 
+def _awq_gptq_factory(h_scale="inverse", w_scale="mul", rescale_d=True, unscale=True):
+    def awq_gptq_layer(W, H0, d, s, bits=4, g=128, damp=0.01, act_order=False):
+        W = np.asarray(W, dtype=np.float64)
+        s = np.asarray(s, dtype=np.float64)
+        H0 = np.asarray(H0, dtype=np.float64)
+        Ws = W * s[None, :] if w_scale == "mul" else W / s[None, :]
+        Hs = H0 / np.outer(s, s) if h_scale == "inverse" else H0 * np.outer(s, s)
+        ds = None if d is None else (np.asarray(d) / (s * s) if rescale_d else np.asarray(d))
+        res = oracle.gptq_layer(Ws, Hs, ds, bits=bits, g=g, damp=damp, act_order=act_order)
+        res["What_orig"] = res["What"] / s[None, :] if unscale else res["What"]
+        return res
+    return awq_gptq_layer
+
+
 MUTANTS = {
     "feedback sign flipped": dict(gptq_layer=_layer_with(columns=_columns_factory(sign=-1.0))),
     "error not divided by U_jj": dict(gptq_layer=_layer_with(columns=_columns_factory(divide_by_ujj=False))),
@@ -175,6 +189,10 @@ MUTANTS = {
     "int4 nibbles reversed": dict(pack_int4=_pack_reversed),
     "int4 unpack without sign": dict(unpack_int4=_unpack_unsigned),
     "dequant ignores g_idx": dict(dequantize_packed=_dequant_ignores_g_idx),
+    "awq+gptq: H scaled by s s": dict(awq_gptq_layer=_awq_gptq_factory(h_scale="direct")),
+    "awq+gptq: W divided by s": dict(awq_gptq_layer=_awq_gptq_factory(w_scale="div")),
+    "awq+gptq: act-order key not rescaled": dict(awq_gptq_layer=_awq_gptq_factory(rescale_d=False)),
+    "awq+gptq: 1/s not applied": dict(awq_gptq_layer=_awq_gptq_factory(unscale=False)),
 }
 
 
