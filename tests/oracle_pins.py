@@ -402,6 +402,46 @@ def check_awq_gptq(impl):
     assert np.allclose(r1["What_orig"], r2["What_orig"], rtol=1e-12)
 
 
+def check_zero_point(impl):
+    """Zero-point groups: hand-worked grid, diagonal H => RTN, the loop
+    identity, the grid itself, and GPTQ below RTN on correlated inputs."""
+    gd = load_golden("zero_point_hand.json")["rtn"]
+    W = np.array(gd["W"])
+    codes, scales, zeros = impl.zp_rtn(W, gd["bits"], gd["g"])
+    assert np.array_equal(codes, np.array(gd["codes"]))
+    assert np.allclose(scales, gd["scales"], rtol=1e-15, atol=0)
+    assert np.array_equal(zeros, np.array(gd["zeros"]))
+    assert np.allclose(impl.zp_dequantize(codes, scales, zeros, np.zeros(4, dtype=int)), gd["What"], rtol=1e-15)
+    rng = np.random.default_rng(41)
+    n, N = 48, 500
+    base = rng.standard_normal((N, 6))
+    X = base @ rng.standard_normal((6, n)) + 0.3 * rng.standard_normal((N, n))
+    Wr = rng.standard_normal((7, n)) + 0.4          # off-centre weights: the zero-point matters
+    H0, d = impl.proxy_hessian(X)
+    for bits in (2, 3, 4):
+        # diagonal H: no feedback, so GPTQ is RTN
+        dg = impl.zp_gptq_layer(Wr, np.diag(np.diag(H0)), None, bits=bits, g=16, damp=0.01)
+        rc, rs, rz = impl.zp_rtn(Wr, bits, 16)
+        assert np.array_equal(dg["codes"], rc)
+        assert np.array_equal(dg["zeros"], rz)
+        res = impl.zp_gptq_layer(Wr, H0, d, bits=bits, g=16, damp=0.01)
+        q = 2 ** bits - 1
+        assert res["codes"].min() >= 0 and res["codes"].max() <= q
+        assert res["zeros"].min() >= 0 and res["zeros"].max() <= q
+        # the loop identity: sum err^2 = tr(dW (H0 + lambda I) dW^T)
+        Hd = H0 + res["lambda"] * np.eye(n)
+        dW = Wr - res["What"]
+        assert abs(res["sum_err2"] - float(np.sum((dW @ Hd) * dW))) <= 1e-9 * res["sum_err2"]
+        # GPTQ's calibration error below RTN's (empirical, large margin here)
+        What_r = impl.zp_dequantize(rc, rs, rz, np.arange(n) // 16)
+        assert impl.output_error(X, Wr, res["What"]) < 0.9 * impl.output_error(X, Wr, What_r)
+    # act-order: the permuted problem in natural order
+    res = impl.zp_gptq_layer(Wr, H0, d, bits=3, g=16, damp=0.01, act_order=True)
+    perm = np.argsort(-d, kind="stable")
+    ref = impl.zp_gptq_layer(Wr[:, perm], H0[np.ix_(perm, perm)], d[perm], bits=3, g=16, damp=0.01)
+    assert np.array_equal(res["codes"][:, perm], ref["codes"])
+
+
 ALL_CHECKS = [
     check_rtn_hand, check_gptq_hand, check_damping_hand, check_act_order_hand,
     check_hessian_bruteforce, check_hessian_orthogonal, check_hessian_chunking,
@@ -409,4 +449,5 @@ ALL_CHECKS = [
     check_babai_identity, check_babai_equivalence, check_grid_and_invariances,
     check_gptq_beats_rtn_correlated, check_act_order_matches_permuted_problem, check_awq,
     check_hessian_sizes, check_pack_hand, check_pack_roundtrip, check_dequant_g_idx_hand, check_awq_gptq,
+    check_zero_point,
 ]

@@ -169,6 +169,52 @@ def _awq_gptq_factory(h_scale="inverse", w_scale="mul", rescale_d=True, unscale=
     return awq_gptq_layer
 
 
+def _zp_dequant_no_zero(codes, scales, zeros, g_idx):
+    gi = np.asarray(g_idx)
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[:, gi]
+
+
+def _zp_params_without_origin(Wg, bits):
+    Wg = np.asarray(Wg, dtype=np.float64)
+    lo, hi = Wg.min(axis=1), Wg.max(axis=1)
+    scale = (hi - lo) / (2 ** bits - 1)
+    zero = np.zeros_like(scale)
+    live = scale != 0
+    zero[live] = np.round(-lo[live] / scale[live])
+    return scale, zero
+
+
+def _zp_params_floor(Wg, bits):
+    Wg = np.asarray(Wg, dtype=np.float64)
+    lo, hi = np.minimum(Wg.min(axis=1), 0.0), np.maximum(Wg.max(axis=1), 0.0)
+    scale = (hi - lo) / (2 ** bits - 1)
+    zero = np.zeros_like(scale)
+    live = scale != 0
+    zero[live] = np.floor(-lo[live] / scale[live])
+    return scale, zero
+
+
+def _zp_with_params(params):
+    import oracle.zero_point as zpm
+
+    def rtn(W, bits, g):
+        saved = zpm.group_params
+        zpm.group_params = params
+        try:
+            return zpm.rtn(W, bits, g)
+        finally:
+            zpm.group_params = saved
+
+    def layer(*a, **k):
+        saved = zpm.group_params
+        zpm.group_params = params
+        try:
+            return zpm.gptq_layer(*a, **k)
+        finally:
+            zpm.group_params = saved
+    return dict(zp_rtn=rtn, zp_gptq_layer=layer, zp_group_params=params)
+
+
 MUTANTS = {
     "feedback sign flipped": dict(gptq_layer=_layer_with(columns=_columns_factory(sign=-1.0))),
     "error not divided by U_jj": dict(gptq_layer=_layer_with(columns=_columns_factory(divide_by_ujj=False))),
@@ -193,6 +239,9 @@ MUTANTS = {
     "awq+gptq: W divided by s": dict(awq_gptq_layer=_awq_gptq_factory(w_scale="div")),
     "awq+gptq: act-order key not rescaled": dict(awq_gptq_layer=_awq_gptq_factory(rescale_d=False)),
     "awq+gptq: 1/s not applied": dict(awq_gptq_layer=_awq_gptq_factory(unscale=False)),
+    "zero-point: zero not subtracted": dict(zp_dequantize=_zp_dequant_no_zero),
+    "zero-point: range without the origin": _zp_with_params(_zp_params_without_origin),
+    "zero-point: zero floored": _zp_with_params(_zp_params_floor),
 }
 
 
