@@ -47,7 +47,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "xtx_gemm_down_proj_traffic.md")
-TRAFFIC_SOURCES = ["post_int4_weight_amd/csrc/gemm_bf16.hip", "post_int4_weight_amd/csrc/common.hpp"]
+TRAFFIC_SOURCES = ["post_int4_weight_amd/csrc/gemm_bf16.hip"]
 
 
 def kernel_source_digest() -> str:
@@ -225,6 +225,22 @@ def stage_breakdown(api, torch, cfg, W, X, H, d, codes, scales, g_idx, perm, ws_
                               g_idx=g_idx, workspace=cws)
     ev[3].record()
     torch.cuda.synchronize()
+    # INT4 storage after the path (not part of the step): pack, then the
+    # g_idx-aware dequantizer to bf16; both stream HBM
+    packed = api.pack_int4(codes)
+    What = torch.empty(o, n, dtype=torch.bfloat16, device=X.device)
+    api.dequantize_int4(packed, scales, g_idx, n, group_size=g, What=What)
+    ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev2[0].record()
+    api.pack_int4(codes, packed=packed)
+    ev2[1].record()
+    api.dequantize_int4(packed, scales, g_idx, n, group_size=g, What=What)
+    ev2[2].record()
+    torch.cuda.synchronize()
+    t_pack = ev2[0].elapsed_time(ev2[1]) / 1e3
+    t_deq = ev2[1].elapsed_time(ev2[2]) / 1e3
+    b_pack = o * n + o * n / 2
+    b_deq = o * n / 2 + 4.0 * o * ((n + g - 1) // g) + 4.0 * n + 2.0 * o * n
     t_h = ev[0].elapsed_time(ev[1]) / 1e3
     t_u = ev[1].elapsed_time(ev[2]) / 1e3
     t_c = ev[2].elapsed_time(ev[3]) / 1e3
@@ -244,6 +260,9 @@ def stage_breakdown(api, torch, cfg, W, X, H, d, codes, scales, g_idx, perm, ws_
         "xtx_tflops": round(f_xtx / t_h / 1e12, 1),
         "factor_tflops": round(f_u / t_u / 1e12, 2),
         "kernels": kern,
+        "int4_pack_ms": round(t_pack * 1e3, 4), "int4_pack_frac_hbm": round(b_pack / t_pack / 1e9 / PEAK_HBM_GBS, 4),
+        "int4_dequant_bf16_ms": round(t_deq * 1e3, 4),
+        "int4_dequant_frac_hbm": round(b_deq / t_deq / 1e9 / PEAK_HBM_GBS, 4),
     }
     if "xtx_gemm" in kern:
         out["xtx_kernel_frac_bf16_peak"] = round(f_xtx / (kern["xtx_gemm"]["total_ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)

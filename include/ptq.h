@@ -191,6 +191,53 @@ int awq_search_alpha(const void* W, int w_dtype, int64_t out, int64_t in, int64_
                      int8_t* codes, float* scales,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * AWQ's scaling first, GPTQ's rounding after.  [OBJ] "A strong answer" (the
+ * decision list: for 3-bit or aggressive targets the two compose).
+ *
+ * s fp32[in] (device, positive and finite; e.g. awq_search_alpha's output)
+ * defines W' = W diag(s) and X' = X diag(s)^-1, which leave the layer output
+ * unchanged. GPTQ then runs on the scaled layer exactly as
+ * gptq_quantize_layer does on a layer: H0' = diag(s)^-1 H diag(s)^-1 (H the
+ * UNDAMPED X^T X), d' = d / s^2 (may be NULL), damping on H0'. codes /
+ * scales / g_idx / perm quantize W' (the caller folds 1/s into the previous
+ * operator, as for AWQ: What = code * scale[g_idx] / s). stats as for
+ * gptq_quantize_layer, for the scaled layer; stats[3] = ||X' dW'^T||^2 equals
+ * the calibration error ||X (W - What)^T||^2 in the original basis.
+ * A zero or non-finite s gives ENONFINITE or ENOTPD. Synchronous.
+ * Errors: EINVAL, ENOTPD, ENONFINITE, EWORKSPACE, EHIP.
+ * ---------------------------------------------------------------------- */
+size_t awq_gptq_quantize_layer_workspace_bytes(int64_t out, int64_t in, int block_size);
+int awq_gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                            const float* H, const double* d, const float* s,
+                            int bits, int group_size, double damp, int act_order, int block_size,
+                            int8_t* codes, float* scales, int32_t* g_idx, int32_t* perm, double* stats,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * INT4 storage — the step after the path.  [OBJ] opening question and "A
+ * strong answer": INT4 weights with group scales; "What interviewers probe
+ * next" and "Common mistakes": with act-order each column carries its group
+ * index, and a dequantizer that ignores it applies wrong scales.
+ *
+ * pack_int4: codes int8[out, in] (row stride in, values of a `bits`-bit
+ * symmetric grid, bits in [2, 4], so in [-8, 7]) -> packed uint32[out, in/8]:
+ * word w of row r holds codes[r][8w .. 8w+7], code 8w+k in bits 4k..4k+3 as
+ * a two's-complement nibble. Requires in % 8 == 0. Codes outside [-8, 7]
+ * are a precondition violation (only their low nibble is kept).
+ * Asynchronous. Errors: EINVAL, EHIP.
+ *
+ * dequantize_int4: What[r][c] = code(r, c) * scales[r][gi(c)] with
+ * gi(c) = g_idx[c] (g_idx may be NULL: gi(c) = c / group_size). scales is
+ * fp32[out, ceil(in / group_size)] (row stride ceil(in / group_size)); a
+ * group index outside that range gives NaN in that column. What is fp32 or
+ * bf16 (out_dtype; the fp32 product rounded to nearest even) [out, in] with
+ * row stride ldo (>= in, multiple of 8). Asynchronous. Errors: EINVAL, EHIP.
+ * ---------------------------------------------------------------------- */
+int pack_int4(const int8_t* codes, int64_t out, int64_t in, int bits, uint32_t* packed, void* stream);
+int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, int64_t out, int64_t in,
+                    int group_size, int out_dtype, void* What, int64_t ldo, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

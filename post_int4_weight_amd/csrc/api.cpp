@@ -321,4 +321,59 @@ int awq_search_alpha(const void* W, int w_dtype, int64_t out, int64_t in, int64_
                    err_per_alpha, s, codes, scales, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+size_t awq_gptq_quantize_layer_workspace_bytes(int64_t out, int64_t in, int block_size) {
+    if (out < 0 || in < 1) return 0;
+    return awq_gptq_workspace_bytes(out, in, block_size);
+}
+
+int awq_gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw, const float* H,
+                            const double* d, const float* s, int bits, int group_size, double damp, int act_order,
+                            int block_size, int8_t* codes, float* scales, int32_t* g_idx, int32_t* perm,
+                            double* stats, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "awq_gptq_quantize_layer";
+    PTQ_TRY(check_gptq_common(out, in, bits, group_size, block_size, fn));
+    if (!dtype_ok(w_dtype)) return fail(PTQ_EINVAL, "%s: w_dtype = %d", fn, w_dtype);
+    if (ldw < in || ldw % elems16(w_dtype)) return fail(PTQ_EINVAL, "%s: bad ldw", fn);
+    if (!(damp >= 0.0) || !std::isfinite(damp)) return fail(PTQ_EINVAL, "%s: damp = %g", fn, damp);
+    if (act_order != 0 && act_order != 1) return fail(PTQ_EINVAL, "%s: act_order = %d", fn, act_order);
+    if (!H || !s) return fail(PTQ_EINVAL, "%s: H or s is NULL", fn);
+    if (out > 0 && (!W || !codes || !scales)) return fail(PTQ_EINVAL, "%s: W, codes or scales is NULL", fn);
+    if (!aligned16(H) || (W && !aligned16(W)) || (codes && !aligned16(codes)) || (d && ((uintptr_t)d & 7u)) ||
+        ((uintptr_t)s & 3u) || (scales && ((uintptr_t)scales & 3u)) || (g_idx && ((uintptr_t)g_idx & 3u)) ||
+        (perm && ((uintptr_t)perm & 3u)))
+        return fail(PTQ_EINVAL, "%s: misaligned pointer", fn);
+    const size_t need = awq_gptq_workspace_bytes(out, in, block_size);
+    if (!workspace || workspace_bytes < need)
+        return fail(PTQ_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(PTQ_EINVAL, "%s: misaligned workspace", fn);
+    return run_awq_gptq(W, w_dtype, out, in, ldw, H, d, s, bits, group_size, damp, act_order, block_size, codes,
+                        scales, g_idx, perm, stats, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int pack_int4(const int8_t* codes, int64_t out, int64_t in, int bits, uint32_t* packed, void* stream) {
+    const char* fn = "pack_int4";
+    if (out < 0 || in < 0) return fail(PTQ_EINVAL, "%s: negative size", fn);
+    if (in % 8) return fail(PTQ_EINVAL, "%s: in = %lld must be a multiple of 8", fn, (long long)in);
+    if (bits < 2 || bits > 4) return fail(PTQ_EINVAL, "%s: bits = %d: only codes of 2 to 4 bits fit a nibble", fn, bits);
+    if (out * in > 0 && (!codes || !packed)) return fail(PTQ_EINVAL, "%s: codes or packed is NULL", fn);
+    if ((codes && !aligned16(codes)) || (packed && !aligned16(packed)))
+        return fail(PTQ_EINVAL, "%s: misaligned pointer", fn);
+    return launch_pack_int4(codes, out, in, packed, (hipStream_t)stream);
+}
+
+int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, int64_t out, int64_t in,
+                    int group_size, int out_dtype, void* What, int64_t ldo, void* stream) {
+    const char* fn = "dequantize_int4";
+    if (out < 0 || in < 0) return fail(PTQ_EINVAL, "%s: negative size", fn);
+    if (in % 8) return fail(PTQ_EINVAL, "%s: in = %lld must be a multiple of 8", fn, (long long)in);
+    if (group_size < 1) return fail(PTQ_EINVAL, "%s: group_size = %d < 1", fn, group_size);
+    if (!dtype_ok(out_dtype)) return fail(PTQ_EINVAL, "%s: out_dtype = %d", fn, out_dtype);
+    if (ldo < in || ldo % 8) return fail(PTQ_EINVAL, "%s: ldo = %lld (need >= in, multiple of 8)", fn, (long long)ldo);
+    if (out * in > 0 && (!packed || !scales || !What)) return fail(PTQ_EINVAL, "%s: NULL pointer", fn);
+    if ((packed && !aligned16(packed)) || (What && !aligned16(What)) || (scales && ((uintptr_t)scales & 3u)) ||
+        (g_idx && ((uintptr_t)g_idx & 3u)))
+        return fail(PTQ_EINVAL, "%s: misaligned pointer", fn);
+    return launch_dequant_int4(packed, scales, g_idx, out, in, group_size, out_dtype, What, ldo, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -1,0 +1,129 @@
+// INT4 storage of the codes and the g_idx-aware dequantizer.
+//
+// "GPTQ versus AWQ objectives" (inferenceinterviews.com): both methods store
+// INT4 weights with group scales (opening question, "A strong answer"); with
+// act-order the groups follow the processing order, so every column carries
+// its group index and the dequantizer must look the scale up through it
+// ("What interviewers probe next", "Common mistakes").
+//
+// Layout (the pages fix none): eight codes per 32-bit word along the input
+// dimension, code 8w + k of a row in bits 4k .. 4k + 3 of word w, as a
+// two's-complement nibble. INT3 codes use the same nibbles.
+//
+// Both kernels are pure streaming (HBM-bound) with vector accesses: a pack
+// thread turns 32 codes (two 16-byte loads) into 4 words (one 16-byte
+// store); a dequantize thread turns one word into 8 values (32 bytes of fp32
+// or 16 bytes of bf16).
+#include "common.hpp"
+
+#include <algorithm>
+
+namespace ptq {
+namespace {
+
+__device__ __forceinline__ uint32_t pack8(uint2 b) {
+    // b holds 8 int8 codes (little-endian); keep the low nibble of each
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w |= ((b.x >> (8 * k)) & 0xFu) << (4 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w |= ((b.y >> (8 * k)) & 0xFu) << (4 * (k + 4));
+    return w;
+}
+
+// words: out * in / 8 in total, row-major [out, in / 8]
+__global__ void pack_int4_kernel(const int8_t* __restrict__ codes, int64_t nwords, uint32_t* __restrict__ packed) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * t < nwords; t += stride) {
+        const int64_t w0 = 4 * t;
+        if (w0 + 4 <= nwords) {
+            const uint4 a = *(const uint4*)(codes + 8 * w0);
+            const uint4 b = *(const uint4*)(codes + 8 * w0 + 16);
+            uint4 o;
+            o.x = pack8(make_uint2(a.x, a.y));
+            o.y = pack8(make_uint2(a.z, a.w));
+            o.z = pack8(make_uint2(b.x, b.y));
+            o.w = pack8(make_uint2(b.z, b.w));
+            *(uint4*)(packed + w0) = o;
+        } else {
+            for (int64_t w = w0; w < nwords; ++w) packed[w] = pack8(*(const uint2*)(codes + 8 * w));
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T from_float(float v);
+template <>
+__device__ __forceinline__ float from_float<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t from_float<uint16_t>(float v) { return float_to_bf16_bits(v); }
+
+// What[r][c] = code(r, c) * scales[r][gi(c)], gi(c) = g_idx[c] (or c / g).
+// A group index outside [0, ngroups) yields NaN for that column.
+template <typename T>
+__global__ void dequant_int4_kernel(const uint32_t* __restrict__ packed, const float* __restrict__ scales,
+                                    const int32_t* __restrict__ g_idx, int64_t out, int64_t in, int g,
+                                    int64_t ngroups, T* __restrict__ What, int64_t ldo) {
+    const int64_t wpr = in / 8;                       // words per row
+    const int64_t nwords = out * wpr;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nwords; w += stride) {
+        const int64_t r = w / wpr, c0 = 8 * (w % wpr);
+        const uint32_t word = packed[w];
+        const float* srow = scales + r * ngroups;
+        T v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t gi = g_idx ? (int64_t)g_idx[c0 + k] : (c0 + k) / g;
+            const int code = (int)((word >> (4 * k)) & 0xFu) - (((word >> (4 * k)) & 0x8u) ? 16 : 0);
+            const bool ok = gi >= 0 && gi < ngroups;
+            const float s = srow[ok ? gi : 0];
+            v[k] = from_float<T>(ok ? (float)code * s : __builtin_nanf(""));
+        }
+        T* dst = What + r * ldo + c0;
+        if constexpr (sizeof(T) == 4) {
+            *(float4*)dst = make_float4(*(float*)&v[0], *(float*)&v[1], *(float*)&v[2], *(float*)&v[3]);
+            *(float4*)(dst + 4) = make_float4(*(float*)&v[4], *(float*)&v[5], *(float*)&v[6], *(float*)&v[7]);
+        } else {
+            uint4 o;
+            const uint16_t* h = (const uint16_t*)v;
+            o.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            o.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            o.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
+            o.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
+            *(uint4*)dst = o;
+        }
+    }
+}
+
+unsigned stream_grid(int64_t items) {
+    return (unsigned)std::min<int64_t>(std::max<int64_t>(cdiv(items, 256), 1), 8192);
+}
+
+}  // namespace
+
+int launch_pack_int4(const int8_t* codes, int64_t out, int64_t in, uint32_t* packed, hipStream_t st) {
+    const int64_t nwords = out * (in / 8);
+    if (nwords == 0) return PTQ_OK;
+    hipLaunchKernelGGL(pack_int4_kernel, dim3(stream_grid(cdiv(nwords, 4))), dim3(256), 0, st, codes, nwords,
+                       packed);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
+int launch_dequant_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, int64_t out, int64_t in,
+                        int g, int out_dtype, void* What, int64_t ldo, hipStream_t st) {
+    const int64_t nwords = out * (in / 8);
+    if (nwords == 0) return PTQ_OK;
+    const int64_t ngroups = cdiv(in, g);
+    if (out_dtype == PTQ_F32)
+        hipLaunchKernelGGL(dequant_int4_kernel<float>, dim3(stream_grid(nwords)), dim3(256), 0, st, packed, scales,
+                           g_idx, out, in, g, ngroups, (float*)What, ldo);
+    else
+        hipLaunchKernelGGL(dequant_int4_kernel<uint16_t>, dim3(stream_grid(nwords)), dim3(256), 0, st, packed,
+                           scales, g_idx, out, in, g, ngroups, (uint16_t*)What, ldo);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
+}  // namespace ptq

@@ -21,7 +21,8 @@ def _declared_functions():
 def test_header_lists_the_entry_points():
     names = _declared_functions()
     for n in ("hessian_accumulate", "gptq_inverse_factor", "gptq_quantize_columns", "gptq_quantize_layer",
-              "awq_search_alpha", "ptq_last_error", "ptq_test_gemm_f32"):
+              "awq_search_alpha", "ptq_last_error", "ptq_test_gemm_f32", "pack_int4", "dequantize_int4",
+              "awq_gptq_quantize_layer"):
         assert n in names
 
 
@@ -122,3 +123,47 @@ def test_awq_validation(lib):
     assert call(bits=12) == 1
     assert call(g=0) == 1
     assert call(n=250) == 1
+
+
+def test_int4_storage_validation(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.pack_int4(fake, 4, 12, 4, fake, None) == 1          # in not a multiple of 8
+    assert lib.pack_int4(fake, 4, 16, 5, fake, None) == 1          # 5-bit codes do not fit a nibble
+    assert lib.pack_int4(None, 4, 16, 4, fake, None) == 1
+    assert lib.pack_int4(ctypes.c_void_p((1 << 20) + 4), 4, 16, 4, fake, None) == 1   # misaligned
+    assert "pack_int4" in _err(lib)
+    assert lib.pack_int4(None, 0, 16, 4, None, None) == 0          # empty: nothing to do
+
+    def deq(**k):
+        a = dict(dict(out=4, n=16, g=8, dt=1, ldo=16, packed=fake, scales=fake, what=fake), **k)
+        return lib.dequantize_int4(a["packed"], a["scales"], None, a["out"], a["n"], a["g"], a["dt"], a["what"],
+                                   a["ldo"], None)
+    assert deq(n=12) == 1
+    assert deq(g=0) == 1
+    assert deq(dt=7) == 1
+    assert deq(ldo=12) == 1
+    assert deq(ldo=20) == 1                                       # not a multiple of 8
+    assert deq(scales=None) == 1
+    assert "dequantize_int4" in _err(lib)
+
+
+def test_awq_gptq_validation(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    st = (ctypes.c_double * 4)()
+    ws = lib.awq_gptq_quantize_layer_workspace_bytes(32, 256, 128)
+    assert ws > 0
+
+    def call(**k):
+        a = dict(dict(out=32, n=256, s=fake, bits=4, g=128, damp=0.01, ao=0, blk=128, ws=ws, H=fake), **k)
+        return lib.awq_gptq_quantize_layer(fake, 0, a["out"], a["n"], 256, a["H"], None, a["s"], a["bits"], a["g"],
+                                           a["damp"], a["ao"], a["blk"], fake, fake, fake, fake, st, fake, a["ws"],
+                                           None)
+    assert call(s=None) == 1
+    assert call(H=None) == 1
+    assert call(bits=9) == 1
+    assert call(damp=-1.0) == 1
+    assert call(ao=2) == 1
+    assert call(blk=96) == 1
+    assert call(n=250) == 1
+    assert call(ws=64) == 4
+    assert "awq_gptq_quantize_layer" in _err(lib)
