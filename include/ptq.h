@@ -169,6 +169,28 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Stages 2 + 3 with zero-point groups.  [PTQ] 2.2: each group has its own
+ * quantization parameters, a scale and a zero-point; [PTQ] 2: GPTQ also
+ * serves 3- and 2-bit. The loop is gptq_quantize_layer's; only the grid
+ * differs: per (row, group), at the group's first column, lo = min(0, min w)
+ * and hi = max(0, max w) over the group's current weights, scale =
+ * (hi - lo) / maxq with maxq = 2^bits - 1, zero = round(-lo / scale) and
+ * code = clip(round(w / scale) + zero, 0, maxq) (round half to even; a group
+ * of zeros gets scale 0, zero 0, code 0). What = (code - zero) * scale.
+ *
+ * bits in [2, 7]; codes int8[out, in] in [0, maxq] (original column order);
+ * scales fp32 and zeros int8 [out, ceil(in / g)] (processing-order groups);
+ * other arguments, the workspace (gptq_workspace_bytes) and stats as for
+ * gptq_quantize_layer. Synchronous.
+ * Errors: EINVAL, ENOTPD, ENONFINITE, EWORKSPACE, EHIP.
+ * ---------------------------------------------------------------------- */
+int gptq_quantize_layer_zp(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                           const float* H, const double* d,
+                           int bits, int group_size, double damp, int act_order, int block_size,
+                           int8_t* codes, float* scales, int8_t* zeros, int32_t* g_idx, int32_t* perm,
+                           double* stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stage 4 — AWQ's per-layer alpha grid search.  [OBJ] "A strong answer",
  * AWQ: s_j = mean|x_j|^alpha; scale W's column j by s_j, round to nearest
  * (symmetric groups of g), and pick the alpha with the least calibration
@@ -220,23 +242,27 @@ int awq_gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
  * next" and "Common mistakes": with act-order each column carries its group
  * index, and a dequantizer that ignores it applies wrong scales.
  *
- * pack_int4: codes int8[out, in] (row stride in, values of a `bits`-bit
- * symmetric grid, bits in [2, 4], so in [-8, 7]) -> packed uint32[out, in/8]:
- * word w of row r holds codes[r][8w .. 8w+7], code 8w+k in bits 4k..4k+3 as
- * a two's-complement nibble. Requires in % 8 == 0. Codes outside [-8, 7]
- * are a precondition violation (only their low nibble is kept).
+ * pack_int4: codes int8[out, in] (row stride in; bits in [2, 4]: a
+ * symmetric grid's codes in [-8, 7], or a zero-point grid's in [0, 15]) ->
+ * packed uint32[out, in/8]: word w of row r holds codes[r][8w .. 8w+7], code
+ * 8w+k in bits 4k..4k+3 as its low nibble (two's complement for the
+ * symmetric grid). Requires in % 8 == 0. Codes outside both ranges are a
+ * precondition violation (only their low nibble is kept).
  * Asynchronous. Errors: EINVAL, EHIP.
  *
  * dequantize_int4: What[r][c] = code(r, c) * scales[r][gi(c)] with
- * gi(c) = g_idx[c] (g_idx may be NULL: gi(c) = c / group_size). scales is
- * fp32[out, ceil(in / group_size)] (row stride ceil(in / group_size)); a
- * group index outside that range gives NaN in that column. What is fp32 or
- * bf16 (out_dtype; the fp32 product rounded to nearest even) [out, in] with
- * row stride ldo (>= in, multiple of 8). Asynchronous. Errors: EINVAL, EHIP.
+ * gi(c) = g_idx[c] (g_idx may be NULL: gi(c) = c / group_size), nibbles read
+ * as signed; with zeros (int8[out, ceil(in / group_size)], may be NULL)
+ * nibbles are unsigned and What = (code - zeros[r][gi(c)]) * scales[r][gi(c)].
+ * scales is fp32[out, ceil(in / group_size)] (row stride ceil(in /
+ * group_size)); a group index outside that range gives NaN in that column.
+ * What is fp32 or bf16 (out_dtype; the fp32 product rounded to nearest even)
+ * [out, in] with row stride ldo (>= in, multiple of 8). Asynchronous.
+ * Errors: EINVAL, EHIP.
  * ---------------------------------------------------------------------- */
 int pack_int4(const int8_t* codes, int64_t out, int64_t in, int bits, uint32_t* packed, void* stream);
-int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, int64_t out, int64_t in,
-                    int group_size, int out_dtype, void* What, int64_t ldo, void* stream);
+int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, const int8_t* zeros,
+                    int64_t out, int64_t in, int group_size, int out_dtype, void* What, int64_t ldo, void* stream);
 
 #ifdef __cplusplus
 }

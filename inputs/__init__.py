@@ -138,3 +138,32 @@ def custom(out: int, inp: int, rows: int, seed: int, dtype: str = "f32", device=
     W = weights(out, inp, seed, dtype, device)
     X = activations(rows, sigma, seed, dtype, device, zero_frac)
     return W, X
+
+
+# Toy layer of "GPTQ versus AWQ objectives" ("A strong answer", the table of
+# output MSE under a distribution shift): 256 inputs, 128 outputs, correlated
+# Gaussian inputs with four outlier channels; a calibration sample, a fresh
+# sample of the same distribution, and one whose outliers moved to four other
+# channels. The page gives no mixing or outlier strength: here x = z M with
+# M = I + 0.5 G / 16 (G standard normal, fixed), outlier channels x10.
+TOY_IN, TOY_OUT, TOY_ROWS = 256, 128, 2048
+TOY_OUTLIER_MULT = 10.0
+TOY_SEED = 11
+
+
+def toy_layer(device="cpu"):
+    """(W [128, 256], X_cal, X_same, X_moved) in float32, drawn on the CPU."""
+    rng = np.random.default_rng([TOY_SEED, 0])
+    mix = np.eye(TOY_IN) + 0.5 * rng.standard_normal((TOY_IN, TOY_IN)) / math.sqrt(TOY_IN)
+    W = rng.standard_normal((TOY_OUT, TOY_IN)) / math.sqrt(TOY_IN)
+    ch = rng.choice(TOY_IN, size=8, replace=False)
+    ch_cal, ch_moved = ch[:4], ch[4:]
+
+    def sample(stream, channels):
+        z = np.random.default_rng([TOY_SEED, stream]).standard_normal((TOY_ROWS, TOY_IN))
+        x = z @ mix
+        x[:, channels] *= TOY_OUTLIER_MULT
+        return torch.tensor(x, dtype=torch.float32, device=device)
+
+    return (torch.tensor(W, dtype=torch.float32, device=device), sample(1, ch_cal), sample(2, ch_cal),
+            sample(3, ch_moved))

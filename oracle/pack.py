@@ -23,13 +23,15 @@ import numpy as np
 
 
 def pack_int4(codes):
-    """codes int [out, n] in [-8, 7], n % 8 == 0 -> uint32 [out, n / 8]."""
+    """codes int [out, n], n % 8 == 0 -> uint32 [out, n / 8]. Codes of a
+    symmetric grid lie in [-8, 7] (two's-complement nibbles), those of a
+    zero-point grid in [0, 15] (plain nibbles); both store their low 4 bits."""
     codes = np.asarray(codes, dtype=np.int64)
     out, n = codes.shape
     if n % 8:
         raise ValueError("the input dimension must be a multiple of 8")
-    if codes.size and (codes.min() < -8 or codes.max() > 7):
-        raise ValueError("codes outside [-8, 7] do not fit a 4-bit nibble")
+    if codes.size and (codes.min() < -8 or codes.max() > 15 or (codes.min() < 0 and codes.max() > 7)):
+        raise ValueError("codes must lie in [-8, 7] or in [0, 15] to fit a 4-bit nibble")
     words = np.zeros((out, n // 8), dtype=np.uint64)
     for w in range(n // 8):
         for k in range(8):
@@ -37,19 +39,24 @@ def pack_int4(codes):
     return words.astype(np.uint32)
 
 
-def unpack_int4(packed, n: int):
-    """Inverse of pack_int4: uint32 [out, n / 8] -> int64 codes [out, n]."""
+def unpack_int4(packed, n: int, signed: bool = True):
+    """Inverse of pack_int4: uint32 [out, n / 8] -> int64 codes [out, n]
+    (two's-complement nibbles, or plain ones with signed=False)."""
     packed = np.asarray(packed, dtype=np.uint64)
     out = packed.shape[0]
     codes = np.zeros((out, n), dtype=np.int64)
     for w in range(n // 8):
         for k in range(8):
             nib = ((packed[:, w] >> np.uint64(4 * k)) & np.uint64(0xF)).astype(np.int64)
-            codes[:, 8 * w + k] = np.where(nib >= 8, nib - 16, nib)
+            codes[:, 8 * w + k] = np.where(nib >= 8, nib - 16, nib) if signed else nib
     return codes
 
 
-def dequantize_packed(packed, scales, g_idx, n: int):
-    """What[r, c] = code(r, c) * scales[r, g_idx[c]] in float64."""
-    codes = unpack_int4(packed, n)
-    return codes.astype(np.float64) * np.asarray(scales, dtype=np.float64)[:, np.asarray(g_idx)]
+def dequantize_packed(packed, scales, g_idx, n: int, zeros=None):
+    """What[r, c] = code(r, c) * scales[r, g_idx[c]] in float64; with zeros
+    (zero-point grid) the nibbles are plain and What = (code - zero) * scale."""
+    gi = np.asarray(g_idx)
+    codes = unpack_int4(packed, n, signed=zeros is None).astype(np.float64)
+    if zeros is not None:
+        codes = codes - np.asarray(zeros, dtype=np.float64)[:, gi]
+    return codes * np.asarray(scales, dtype=np.float64)[:, gi]

@@ -66,7 +66,9 @@ def _load() -> ctypes.CDLL:
         "awq_gptq_quantize_layer_workspace_bytes": (sz, [i64, i64, i32]),
         "awq_gptq_quantize_layer": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32, i32, dbl, i32, i32, vp, vp, vp, vp,
                                           dp, vp, sz, vp]),
-        "dequantize_int4": (i32, [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp]),
+        "dequantize_int4": (i32, [vp, vp, vp, vp, i64, i64, i32, i32, vp, i64, vp]),
+        "gptq_quantize_layer_zp": (i32, [vp, i32, i64, i64, i64, vp, vp, i32, i32, dbl, i32, i32, vp, vp, vp, vp, vp,
+                                         dp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -258,6 +260,25 @@ def awq_search_alpha(W, X, alphas, bits=4, group_size=128, s=None, codes=None, s
 
 # ------------------------------------------- composition and INT4 storage ---
 
+def gptq_quantize_layer_zp(W, H, d=None, bits=4, group_size=128, damp=0.01, act_order=False, block_size=128,
+                           codes=None, scales=None, zeros=None, g_idx=None, perm=None, workspace=None):
+    """gptq_quantize_layer_zp (include/ptq.h): GPTQ with zero-point groups; codes in [0, 2^bits - 1]."""
+    out, n = W.shape
+    ldw = _rowmajor(W, "W")
+    codes, scales, g_idx = _alloc_codes(W, n, group_size, codes, scales, g_idx)
+    if zeros is None:
+        zeros = torch.empty(out, (n + group_size - 1) // group_size, dtype=torch.int8, device=W.device)
+    if perm is None:
+        perm = torch.empty(n, dtype=torch.int32, device=W.device)
+    ws, wsb = _workspace(gptq_workspace_bytes(out, n, block_size), W.device, workspace)
+    stats = (ctypes.c_double * 4)()
+    _check(_lib.gptq_quantize_layer_zp(_ptr(W), _dtype_code(W), out, n, ldw, _ptr(H), _ptr(d), bits, group_size,
+                                       float(damp), int(bool(act_order)), block_size, _ptr(codes), _ptr(scales),
+                                       _ptr(zeros), _ptr(g_idx), _ptr(perm), stats, _ptr(ws), wsb, _stream()))
+    return {"codes": codes, "scales": scales, "zeros": zeros, "g_idx": g_idx, "perm": perm,
+            "stats": {"sum_err2": stats[0], "lambda": stats[1], "dW_fro2": stats[2], "objective": stats[3]}}
+
+
 def awq_gptq_quantize_layer(W, H, d, s, bits=4, group_size=128, damp=0.01, act_order=False, block_size=128,
                             codes=None, scales=None, g_idx=None, perm=None, workspace=None):
     """awq_gptq_quantize_layer (include/ptq.h): GPTQ on W diag(s) with the Hessian of X diag(s)^-1."""
@@ -288,14 +309,15 @@ def pack_int4(codes: torch.Tensor, bits: int = 4, packed=None):
 
 
 def dequantize_int4(packed: torch.Tensor, scales: torch.Tensor, g_idx, n: int, group_size: int = 128,
-                    out_dtype=torch.float32, What=None):
-    """dequantize_int4 (include/ptq.h): What[r][c] = code * scales[r][g_idx[c]] (g_idx None: c // group_size)."""
+                    out_dtype=torch.float32, What=None, zeros=None):
+    """dequantize_int4 (include/ptq.h): What[r][c] = code * scales[r][g_idx[c]] (g_idx None: c // group_size);
+    with zeros, unsigned codes and What = (code - zero) * scale."""
     out = packed.shape[0]
     if What is None:
         What = torch.empty(out, n, dtype=out_dtype, device=packed.device)
     ldo = _rowmajor(What, "What") if out > 0 else n
-    _check(_lib.dequantize_int4(_ptr(packed), _ptr(scales), _ptr(g_idx), out, n, group_size, _dtype_code(What),
-                                _ptr(What), ldo, _stream()))
+    _check(_lib.dequantize_int4(_ptr(packed), _ptr(scales), _ptr(g_idx), _ptr(zeros), out, n, group_size,
+                                _dtype_code(What), _ptr(What), ldo, _stream()))
     return What
 
 

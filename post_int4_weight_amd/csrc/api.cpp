@@ -216,8 +216,8 @@ int gptq_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t in, i
     PTQ_TRY(check_columns(W, w_dtype, out, in, ldw, U, bits, group_size, block_size, codes, scales, g_idx, workspace,
                           workspace_bytes, "gptq_quantize_columns"));
     if (perm && ((uintptr_t)perm & 3u)) return fail(PTQ_EINVAL, "gptq_quantize_columns: misaligned perm");
-    return run_quantize_columns(W, w_dtype, out, in, ldw, U, perm, bits, group_size, block_size, codes, scales, g_idx,
-                                stats, workspace, workspace_bytes, (hipStream_t)stream);
+    return run_quantize_columns(W, w_dtype, out, in, ldw, U, perm, bits, group_size, block_size, codes, scales, nullptr,
+                                g_idx, stats, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 size_t gptq_workspace_bytes(int64_t out, int64_t in, int block_size) {
@@ -230,11 +230,13 @@ size_t gptq_workspace_bytes(int64_t out, int64_t in, int block_size) {
     return z.bytes();
 }
 
-int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw, const float* H,
-                        const double* d, int bits, int group_size, double damp, int act_order, int block_size,
-                        int8_t* codes, float* scales, int32_t* g_idx, int32_t* perm, double* stats, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-    const char* fn = "gptq_quantize_layer";
+}  // extern "C"
+
+// Stages 2 + 3; zeros == nullptr: symmetric grid, else zero-point groups.
+static int quantize_layer(const char* fn, const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                          const float* H, const double* d, int bits, int group_size, double damp, int act_order,
+                          int block_size, int8_t* codes, float* scales, int8_t* zeros, int32_t* g_idx, int32_t* perm,
+                          double* stats, void* workspace, size_t workspace_bytes, void* stream) {
     PTQ_TRY(check_gptq_common(out, in, bits, group_size, block_size, fn));
     if (!dtype_ok(w_dtype)) return fail(PTQ_EINVAL, "%s: w_dtype = %d", fn, w_dtype);
     if (ldw < in || ldw % elems16(w_dtype)) return fail(PTQ_EINVAL, "%s: bad ldw", fn);
@@ -261,10 +263,8 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int
     PTQ_TRY(run_inverse_factor(H, d, in, damp, act_order, U, p, &lam, fws, factor_workspace_bytes(in), st));
     double s[4] = {0.0, 0.0, 0.0, 0.0};
     PTQ_TRY(run_quantize_columns(W, w_dtype, out, in, ldw, U, act_order ? p : nullptr, bits, group_size, block_size,
-                                 codes, scales, g_idx, s, cws, columns_workspace_bytes(out, in, block_size), st));
-    if (perm && !act_order) {
-        // identity permutation was produced into perm by the factor stage: nothing more to do
-    }
+                                 codes, scales, zeros, g_idx, s, cws, columns_workspace_bytes(out, in, block_size),
+                                 st));
     if (stats) {
         stats[0] = s[0];
         stats[1] = lam;
@@ -272,6 +272,27 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int
         stats[3] = s[0] - lam * s[2];
     }
     return PTQ_OK;
+}
+
+extern "C" {
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw, const float* H,
+                        const double* d, int bits, int group_size, double damp, int act_order, int block_size,
+                        int8_t* codes, float* scales, int32_t* g_idx, int32_t* perm, double* stats, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return quantize_layer("gptq_quantize_layer", W, w_dtype, out, in, ldw, H, d, bits, group_size, damp, act_order,
+                          block_size, codes, scales, nullptr, g_idx, perm, stats, workspace, workspace_bytes, stream);
+}
+
+int gptq_quantize_layer_zp(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw, const float* H,
+                           const double* d, int bits, int group_size, double damp, int act_order, int block_size,
+                           int8_t* codes, float* scales, int8_t* zeros, int32_t* g_idx, int32_t* perm, double* stats,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "gptq_quantize_layer_zp";
+    if (bits < 2 || bits > 7) return fail(PTQ_EINVAL, "%s: bits = %d outside [2, 7] (codes are int8)", fn, bits);
+    if (out > 0 && !zeros) return fail(PTQ_EINVAL, "%s: zeros is NULL", fn);
+    return quantize_layer(fn, W, w_dtype, out, in, ldw, H, d, bits, group_size, damp, act_order, block_size, codes,
+                          scales, zeros, g_idx, perm, stats, workspace, workspace_bytes, stream);
 }
 
 int ptq_test_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int layout_a, const float* B,
@@ -361,8 +382,8 @@ int pack_int4(const int8_t* codes, int64_t out, int64_t in, int bits, uint32_t* 
     return launch_pack_int4(codes, out, in, packed, (hipStream_t)stream);
 }
 
-int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, int64_t out, int64_t in,
-                    int group_size, int out_dtype, void* What, int64_t ldo, void* stream) {
+int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, const int8_t* zeros,
+                    int64_t out, int64_t in, int group_size, int out_dtype, void* What, int64_t ldo, void* stream) {
     const char* fn = "dequantize_int4";
     if (out < 0 || in < 0) return fail(PTQ_EINVAL, "%s: negative size", fn);
     if (in % 8) return fail(PTQ_EINVAL, "%s: in = %lld must be a multiple of 8", fn, (long long)in);
@@ -373,7 +394,8 @@ int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* 
     if ((packed && !aligned16(packed)) || (What && !aligned16(What)) || (scales && ((uintptr_t)scales & 3u)) ||
         (g_idx && ((uintptr_t)g_idx & 3u)))
         return fail(PTQ_EINVAL, "%s: misaligned pointer", fn);
-    return launch_dequant_int4(packed, scales, g_idx, out, in, group_size, out_dtype, What, ldo, (hipStream_t)stream);
+    return launch_dequant_int4(packed, scales, g_idx, zeros, out, in, group_size, out_dtype, What, ldo,
+                               (hipStream_t)stream);
 }
 
 }  // extern "C"

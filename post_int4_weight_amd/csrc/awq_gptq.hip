@@ -97,7 +97,7 @@ int run_awq_gptq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw
                                st));
     double sv[4] = {0.0, 0.0, 0.0, 0.0};
     PTQ_TRY(run_quantize_columns(Ws, PTQ_F32, out, n, n, U, act_order ? p : nullptr, bits, g, block, codes, scales,
-                                 g_idx, sv, cws, columns_workspace_bytes(out, n, block), st));
+                                 nullptr, g_idx, sv, cws, columns_workspace_bytes(out, n, block), st));
     if (stats) {
         stats[0] = sv[0];
         stats[1] = lam;

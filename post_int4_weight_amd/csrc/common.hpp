@@ -155,7 +155,7 @@ int run_inverse_factor(const float* H, const double* d, int64_t n, double damp, 
 size_t columns_workspace_bytes(int64_t out, int64_t n, int block);
 int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw,
                          const float* U, const int32_t* perm, int bits, int g, int block,
-                         int8_t* codes, float* scales, int32_t* g_idx, double* stats_host,
+                         int8_t* codes, float* scales, int8_t* zeros, int32_t* g_idx, double* stats_host,
                          void* ws, size_t ws_bytes, hipStream_t st);
 
 // AWQ scaling composed with GPTQ (awq_gptq.hip)
@@ -167,8 +167,8 @@ int run_awq_gptq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw
 
 // INT4 storage (pack.hip)
 int launch_pack_int4(const int8_t* codes, int64_t out, int64_t in, uint32_t* packed, hipStream_t st);
-int launch_dequant_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, int64_t out, int64_t in,
-                        int g, int out_dtype, void* What, int64_t ldo, hipStream_t st);
+int launch_dequant_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, const int8_t* zeros,
+                        int64_t out, int64_t in, int g, int out_dtype, void* What, int64_t ldo, hipStream_t st);
 
 // Stage 4 (awq.hip)
 size_t awq_ws_bytes(int64_t out, int64_t n, int64_t rows, int n_alpha);

@@ -25,6 +25,7 @@
 #include "common.hpp"
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 namespace ptq {
@@ -49,11 +50,23 @@ __global__ void gather_columns_kernel(const T* __restrict__ W, int64_t ldw, int6
     }
 }
 
-template <int B>
+// Zero-point group parameters from the group's range [lo, hi] (0 included):
+// scale = (hi - lo) / maxq in fp32; zero = round(-lo / scale), decided in
+// fp64 like the codes.
+__device__ __forceinline__ void zp_params(float hi, float lo, float maxq, float& scale, float& zero) {
+    scale = (hi - lo) / maxq;
+    zero = (hi > lo) ? (float)rint(-(double)lo / (((double)hi - (double)lo) / (double)maxq)) : 0.f;
+}
+
+// ZP = false: symmetric grid, qmax = 2^(bits-1) - 1, codes in [-qmax-1, qmax].
+// ZP = true: zero-point grid, qmax = maxq = 2^bits - 1, codes in [0, maxq],
+// one zero-point per (row, group) in `zeros`.
+template <int B, bool ZP>
 __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc, int64_t out, int64_t n,
                                                           const float* __restrict__ U, int64_t b0, int bc,
                                                           int g, float qmax, const int32_t* __restrict__ perm,
                                                           int8_t* __restrict__ codes, float* __restrict__ scales,
+                                                          int8_t* __restrict__ zeros,
                                                           int64_t ngroups, float* __restrict__ gmaxes,
                                                           float* __restrict__ E, int lde,
                                                           float* __restrict__ err2, int64_t nblocks,
@@ -91,7 +104,9 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
     const int lane = t & 63;
     const int row_lane0 = lane - lr;              // first lane of this row in the wave
     float scale = 0.f;
-    float gmax = 0.f;       // the group's max |w| (scale = gmax / qmax)
+    float gmax = 0.f;       // symmetric: the group's max |w| (scale = gmax / qmax); zero-point: hi
+    float glo = 0.f;        // zero-point: lo
+    float zero = 0.f;       // zero-point: the group's zero
     float e2 = 0.f;
 
     if (g > B) {
@@ -100,20 +115,37 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             // new group: max over its columns of the current weights (all
             // earlier feedback has been applied to them)
             const int64_t j1 = std::min<int64_t>(n, b0 + g);
-            float mx = 0.f;
+            float mx = 0.f, mn = 0.f;
             if (live)
-                for (int64_t k = b0 + lr; k < j1; k += LPR) mx = fmaxf(mx, fabsf(Wc[r * n + k]));
+                for (int64_t k = b0 + lr; k < j1; k += LPR) {
+                    const float v = Wc[r * n + k];
+                    if (ZP) {
+                        mx = fmaxf(mx, v);
+                        mn = fminf(mn, v);
+                    } else {
+                        mx = fmaxf(mx, fabsf(v));
+                    }
+                }
 #pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            for (int off = 1; off < LPR; off <<= 1) {
+                mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                if (ZP) mn = fminf(mn, __shfl_xor(mn, off, 64));
+            }
             gmax = mx;
-            scale = mx / qmax;
+            glo = mn;
+            if (ZP) zp_params(mx, mn, qmax, scale, zero);
+            else scale = mx / qmax;
             if (live && lr == 0) {
                 scales[r * ngroups + b0 / g] = scale;
-                gmaxes[r * ngroups + b0 / g] = mx;
+                gmaxes[2 * (r * ngroups + b0 / g)] = mx;
+                gmaxes[2 * (r * ngroups + b0 / g) + 1] = mn;
+                if (ZP) zeros[r * ngroups + b0 / g] = (int8_t)(int)zero;
             }
         } else if (live) {
             scale = scales[r * ngroups + b0 / g];  // written by an earlier block
-            gmax = gmaxes[r * ngroups + b0 / g];
+            gmax = gmaxes[2 * (r * ngroups + b0 / g)];
+            glo = gmaxes[2 * (r * ngroups + b0 / g) + 1];
+            if (ZP) zero = (float)zeros[r * ngroups + b0 / g];
         }
     }
 
@@ -122,17 +154,32 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
         if (j < bc) {
             if (g <= B && (j % g) == 0) {
                 // the group [j, j+g) lies inside this block: lanes whose columns fall in it
-                float loc = 0.f;
+                float loc = 0.f, lmn = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     const int col = c0 + c;
-                    if (col >= j && col < j + g && col < bc) loc = fmaxf(loc, fabsf(w[c]));
+                    if (col >= j && col < j + g && col < bc) {
+                        if (ZP) {
+                            loc = fmaxf(loc, w[c]);
+                            lmn = fminf(lmn, w[c]);
+                        } else {
+                            loc = fmaxf(loc, fabsf(w[c]));
+                        }
+                    }
                 }
 #pragma unroll
-                for (int off = 1; off < LPR; off <<= 1) loc = fmaxf(loc, __shfl_xor(loc, off, 64));
+                for (int off = 1; off < LPR; off <<= 1) {
+                    loc = fmaxf(loc, __shfl_xor(loc, off, 64));
+                    if (ZP) lmn = fminf(lmn, __shfl_xor(lmn, off, 64));
+                }
                 gmax = loc;
-                scale = loc / qmax;
-                if (live && lr == 0) scales[r * ngroups + (b0 + j) / g] = scale;
+                glo = lmn;
+                if (ZP) zp_params(loc, lmn, qmax, scale, zero);
+                else scale = loc / qmax;
+                if (live && lr == 0) {
+                    scales[r * ngroups + (b0 + j) / g] = scale;
+                    if (ZP) zeros[r * ngroups + (b0 + j) / g] = (int8_t)(int)zero;
+                }
             }
             // round this lane's copy of column j (the owner's copy is the real one).
             // The rounding decision is the fp64 one, x / (gmax / qmax) in double:
@@ -143,10 +190,13 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             if (scale > 0.f) {
                 const float t = x / scale;
                 float rq = rintf(t);
-                if (fabsf(fabsf(t - rq) - 0.5f) < TIE_BAND) rq = (float)rint((double)x / ((double)gmax / (double)qmax));
-                q = fminf(fmaxf(rq, -qmax - 1.f), qmax);
+                if (fabsf(fabsf(t - rq) - 0.5f) < TIE_BAND) {
+                    const double s64 = ZP ? ((double)gmax - (double)glo) / (double)qmax : (double)gmax / (double)qmax;
+                    rq = (float)rint((double)x / s64);
+                }
+                q = ZP ? fminf(fmaxf(rq + zero, 0.f), qmax) : fminf(fmaxf(rq, -qmax - 1.f), qmax);
             }
-            const float e = (x - q * scale) / diag[j];
+            const float e = (x - (q - zero) * scale) / diag[j];
             const int owner = j / CPL;
             const float eb = __shfl(e, row_lane0 + owner, 64);
             if (lr == owner) {
@@ -198,6 +248,7 @@ __global__ void g_idx_kernel(const int32_t* perm, int64_t n, int g, int32_t* g_i
 template <typename T>
 __global__ void row_stats_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n,
                                  const int8_t* __restrict__ codes, const float* __restrict__ scales,
+                                 const int8_t* __restrict__ zeros,
                                  int64_t ngroups, const int32_t* __restrict__ perm, const float* __restrict__ err2,
                                  int64_t nblocks, int g, double* __restrict__ row_out) {
     // one workgroup per row; position of column c in processing order is needed for
@@ -207,7 +258,8 @@ __global__ void row_stats_kernel(const T* __restrict__ W, int64_t ldw, int64_t o
     double dw = 0.0, ee = 0.0;
     for (int64_t k = threadIdx.x; k < n; k += 256) {
         const int64_t c = perm ? perm[k] : k;
-        const float wh = (float)codes[r * n + c] * scales[r * ngroups + k / g];
+        const float z = zeros ? (float)zeros[r * ngroups + k / g] : 0.f;
+        const float wh = ((float)codes[r * n + c] - z) * scales[r * ngroups + k / g];
         const double dv = (double)load_as_float<T>(W, r * ldw + c) - (double)wh;
         dw += dv * dv;
     }
@@ -253,10 +305,10 @@ __global__ void sum_rows_kernel(const double* row_out, int64_t out, double* tot)
 
 __global__ void zero_int_kernel(int* p) { *p = 0; }
 
-template <int B>
+template <int B, bool ZP>
 int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float qmax, const int32_t* perm,
-               int8_t* codes, float* scales, int64_t ngroups, float* gmaxes, float* E, float* err2, int64_t nblocks,
-               int* flag, hipStream_t st) {
+               int8_t* codes, float* scales, int8_t* zeros, int64_t ngroups, float* gmaxes, float* E, float* err2,
+               int64_t nblocks, int* flag, hipStream_t st) {
     constexpr int RPW = NTH / (B / CPL);
     const unsigned grid = (unsigned)cdiv(out, RPW);
     // W_cur[:, c1:] -= Err[:, 0:K] U[k0:k0+K, c1:c2]
@@ -284,8 +336,9 @@ int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float q
         for (int64_t b0 = s0; b0 < s1; b0 += B) {
             const int bc = (int)std::min<int64_t>(B, s1 - b0);
             prof_begin(PROF_BLOCK_LOOP, st);
-            hipLaunchKernelGGL(gptq_block_kernel<B>, dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc, g, qmax,
-                               perm, codes, scales, ngroups, gmaxes, E + (b0 - s0), (int)SB, err2, nblocks, flag);
+            hipLaunchKernelGGL((gptq_block_kernel<B, ZP>), dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc, g,
+                               qmax, perm, codes, scales, zeros, ngroups, gmaxes, E + (b0 - s0), (int)SB, err2,
+                               nblocks, flag);
             prof_end(PROF_BLOCK_LOOP, st);
             PTQ_LAUNCH_CHECK();
             const int64_t b1 = b0 + bc;
@@ -304,7 +357,7 @@ size_t columns_workspace_bytes(int64_t out, int64_t n, int block) {
     z.take<float>((size_t)out * n);          // Wc
     z.take<float>((size_t)out * SB_COLS);    // E (errors of one super-block)
     z.take<float>((size_t)out * nblocks);    // err2
-    z.take<float>((size_t)out * cdiv(n, 8)); // group maxima (groups of >= 8 columns)
+    z.take<float>((size_t)out * 2 * cdiv(n, 8)); // group range ends (groups of >= 8 columns)
     z.take<double>((size_t)out * 2);         // per-row stats
     z.take<double>(2);                       // totals
     z.take<int>(1);                          // flag
@@ -313,14 +366,15 @@ size_t columns_workspace_bytes(int64_t out, int64_t n, int block) {
 
 int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, const float* U,
                          const int32_t* perm, int bits, int g, int block, int8_t* codes, float* scales,
-                         int32_t* g_idx, double* stats_host, void* ws, size_t ws_bytes, hipStream_t st) {
+                         int8_t* zeros, int32_t* g_idx, double* stats_host, void* ws, size_t ws_bytes,
+                         hipStream_t st) {
     Arena ar(ws, ws_bytes);
     const int64_t nblocks = cdiv(n, block);
     const int64_t ngroups = cdiv(n, g);
     float* Wc = ar.take<float>((size_t)out * n);
     float* E = ar.take<float>((size_t)out * SB_COLS);
     float* err2 = ar.take<float>((size_t)out * nblocks);
-    float* gmaxes = ar.take<float>((size_t)out * cdiv(n, 8));
+    float* gmaxes = ar.take<float>((size_t)out * 2 * cdiv(n, 8));
     double* rowst = ar.take<double>((size_t)out * 2);
     double* tot = ar.take<double>(2);
     int* flag = ar.take<int>(1);
@@ -329,7 +383,8 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
                   columns_workspace_bytes(out, n, block));
         return PTQ_EWORKSPACE;
     }
-    const float qmax = (float)((1 << (bits - 1)) - 1);
+    // symmetric: qmax = 2^(bits-1) - 1; zero-point: maxq = 2^bits - 1
+    const float qmax = zeros ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
     hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, st, flag);
     PTQ_LAUNCH_CHECK();
     if (out > 0) {
@@ -341,15 +396,19 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
             hipLaunchKernelGGL(gather_columns_kernel<float>, grid, dim3(256), 0, st, (const float*)W, ldw, out, n,
                                perm, Wc);
         PTQ_LAUNCH_CHECK();
-        if (block == 128)
-            PTQ_TRY(run_blocks<128>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, gmaxes, E, err2, nblocks,
-                                    flag, st));
-        else if (block == 64)
-            PTQ_TRY(run_blocks<64>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, gmaxes, E, err2, nblocks,
-                                    flag, st));
-        else
-            PTQ_TRY(run_blocks<32>(Wc, out, n, U, g, qmax, perm, codes, scales, ngroups, gmaxes, E, err2, nblocks,
-                                    flag, st));
+        auto blocks = [&](auto zp) {
+            constexpr bool Z = decltype(zp)::value;
+            if (block == 128)
+                return run_blocks<128, Z>(Wc, out, n, U, g, qmax, perm, codes, scales, zeros, ngroups, gmaxes, E, err2,
+                                          nblocks, flag, st);
+            if (block == 64)
+                return run_blocks<64, Z>(Wc, out, n, U, g, qmax, perm, codes, scales, zeros, ngroups, gmaxes, E, err2,
+                                         nblocks, flag, st);
+            return run_blocks<32, Z>(Wc, out, n, U, g, qmax, perm, codes, scales, zeros, ngroups, gmaxes, E, err2,
+                                     nblocks, flag, st);
+        };
+        if (zeros) PTQ_TRY(blocks(std::true_type{}));
+        else PTQ_TRY(blocks(std::false_type{}));
     }
 
     if (g_idx) {
@@ -362,10 +421,10 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
     } else if (stats_host) {
         if (w_dtype == PTQ_BF16)
             hipLaunchKernelGGL(row_stats_kernel<uint16_t>, dim3((unsigned)out), dim3(256), 0, st, (const uint16_t*)W,
-                               ldw, out, n, codes, scales, ngroups, perm, err2, nblocks, g, rowst);
+                               ldw, out, n, codes, scales, zeros, ngroups, perm, err2, nblocks, g, rowst);
         else
             hipLaunchKernelGGL(row_stats_kernel<float>, dim3((unsigned)out), dim3(256), 0, st, (const float*)W, ldw,
-                               out, n, codes, scales, ngroups, perm, err2, nblocks, g, rowst);
+                               out, n, codes, scales, zeros, ngroups, perm, err2, nblocks, g, rowst);
         PTQ_LAUNCH_CHECK();
         hipLaunchKernelGGL(sum_rows_kernel, dim3(1), dim3(256), 0, st, rowst, out, tot);
         PTQ_LAUNCH_CHECK();

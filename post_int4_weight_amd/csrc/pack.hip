@@ -58,11 +58,13 @@ __device__ __forceinline__ float from_float<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ uint16_t from_float<uint16_t>(float v) { return float_to_bf16_bits(v); }
 
-// What[r][c] = code(r, c) * scales[r][gi(c)], gi(c) = g_idx[c] (or c / g).
+// What[r][c] = code(r, c) * scales[r][gi(c)], gi(c) = g_idx[c] (or c / g);
+// with zeros: unsigned nibbles, What = (code - zeros[r][gi(c)]) * scale.
 // A group index outside [0, ngroups) yields NaN for that column.
 template <typename T>
 __global__ void dequant_int4_kernel(const uint32_t* __restrict__ packed, const float* __restrict__ scales,
-                                    const int32_t* __restrict__ g_idx, int64_t out, int64_t in, int g,
+                                    const int32_t* __restrict__ g_idx, const int8_t* __restrict__ zeros,
+                                    int64_t out, int64_t in, int g,
                                     int64_t ngroups, T* __restrict__ What, int64_t ldo) {
     const int64_t wpr = in / 8;                       // words per row
     const int64_t nwords = out * wpr;
@@ -75,9 +77,11 @@ __global__ void dequant_int4_kernel(const uint32_t* __restrict__ packed, const f
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int64_t gi = g_idx ? (int64_t)g_idx[c0 + k] : (c0 + k) / g;
-            const int code = (int)((word >> (4 * k)) & 0xFu) - (((word >> (4 * k)) & 0x8u) ? 16 : 0);
+            const int nib = (int)((word >> (4 * k)) & 0xFu);
             const bool ok = gi >= 0 && gi < ngroups;
-            const float s = srow[ok ? gi : 0];
+            const int64_t gs = ok ? gi : 0;
+            const float s = srow[gs];
+            const int code = zeros ? nib - (int)zeros[r * ngroups + gs] : nib - ((nib & 8) ? 16 : 0);
             v[k] = from_float<T>(ok ? (float)code * s : __builtin_nanf(""));
         }
         T* dst = What + r * ldo + c0;
@@ -111,17 +115,17 @@ int launch_pack_int4(const int8_t* codes, int64_t out, int64_t in, uint32_t* pac
     return PTQ_OK;
 }
 
-int launch_dequant_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, int64_t out, int64_t in,
-                        int g, int out_dtype, void* What, int64_t ldo, hipStream_t st) {
+int launch_dequant_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, const int8_t* zeros,
+                        int64_t out, int64_t in, int g, int out_dtype, void* What, int64_t ldo, hipStream_t st) {
     const int64_t nwords = out * (in / 8);
     if (nwords == 0) return PTQ_OK;
     const int64_t ngroups = cdiv(in, g);
     if (out_dtype == PTQ_F32)
         hipLaunchKernelGGL(dequant_int4_kernel<float>, dim3(stream_grid(nwords)), dim3(256), 0, st, packed, scales,
-                           g_idx, out, in, g, ngroups, (float*)What, ldo);
+                           g_idx, zeros, out, in, g, ngroups, (float*)What, ldo);
     else
         hipLaunchKernelGGL(dequant_int4_kernel<uint16_t>, dim3(stream_grid(nwords)), dim3(256), 0, st, packed,
-                           scales, g_idx, out, in, g, ngroups, (uint16_t*)What, ldo);
+                           scales, g_idx, zeros, out, in, g, ngroups, (uint16_t*)What, ldo);
     PTQ_LAUNCH_CHECK();
     return PTQ_OK;
 }

@@ -347,6 +347,18 @@ def check_pack_roundtrip(impl):
     assert np.array_equal(impl.unpack_int4(impl.pack_int4(c), 40), c)
 
 
+def check_pack_zero_point(impl):
+    """Zero-point codes (0..15) pack as plain nibbles and dequantize with their zero."""
+    codes = np.array([[0, 15, 7, 8, 1, 14, 3, 12]])
+    words = impl.pack_int4(codes)
+    # nibbles 0, F, 7, 8, 1, E, 3, C -> 0xC3E187F0
+    assert int(words[0, 0]) == 0xC3E187F0
+    assert np.array_equal(impl.unpack_int4(words, 8, signed=False), codes)
+    zeros = np.array([[7.0]])
+    What = impl.dequantize_packed(words, np.array([[0.5]]), np.zeros(8, dtype=int), 8, zeros=zeros)
+    assert np.array_equal(What, (codes - 7.0) * 0.5)
+
+
 def check_dequant_g_idx_hand(impl):
     gd = load_golden("pack_hand.json")["dequant_g_idx"]
     packed = impl.pack_int4(np.array(gd["codes"]))
@@ -449,5 +461,5 @@ ALL_CHECKS = [
     check_babai_identity, check_babai_equivalence, check_grid_and_invariances,
     check_gptq_beats_rtn_correlated, check_act_order_matches_permuted_problem, check_awq,
     check_hessian_sizes, check_pack_hand, check_pack_roundtrip, check_dequant_g_idx_hand, check_awq_gptq,
-    check_zero_point,
+    check_zero_point, check_pack_zero_point,
 ]

@@ -22,7 +22,7 @@ def test_header_lists_the_entry_points():
     names = _declared_functions()
     for n in ("hessian_accumulate", "gptq_inverse_factor", "gptq_quantize_columns", "gptq_quantize_layer",
               "awq_search_alpha", "ptq_last_error", "ptq_test_gemm_f32", "pack_int4", "dequantize_int4",
-              "awq_gptq_quantize_layer"):
+              "awq_gptq_quantize_layer", "gptq_quantize_layer_zp"):
         assert n in names
 
 
@@ -136,8 +136,8 @@ def test_int4_storage_validation(lib):
 
     def deq(**k):
         a = dict(dict(out=4, n=16, g=8, dt=1, ldo=16, packed=fake, scales=fake, what=fake), **k)
-        return lib.dequantize_int4(a["packed"], a["scales"], None, a["out"], a["n"], a["g"], a["dt"], a["what"],
-                                   a["ldo"], None)
+        return lib.dequantize_int4(a["packed"], a["scales"], None, None, a["out"], a["n"], a["g"], a["dt"],
+                                   a["what"], a["ldo"], None)
     assert deq(n=12) == 1
     assert deq(g=0) == 1
     assert deq(dt=7) == 1
@@ -167,3 +167,19 @@ def test_awq_gptq_validation(lib):
     assert call(n=250) == 1
     assert call(ws=64) == 4
     assert "awq_gptq_quantize_layer" in _err(lib)
+
+
+def test_zero_point_validation(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    st = (ctypes.c_double * 4)()
+
+    def call(**k):
+        a = dict(dict(bits=4, zeros=fake, g=128), **k)
+        return lib.gptq_quantize_layer_zp(fake, 0, 32, 256, 256, fake, None, a["bits"], a["g"], 0.01, 0, 128, fake,
+                                          fake, a["zeros"], fake, fake, st, fake, 64, None)
+    assert call(bits=8) == 1          # codes 0..255 do not fit int8
+    assert call(bits=1) == 1
+    assert call(zeros=None) == 1
+    assert call(g=0) == 1
+    assert call() == 4                # workspace too small
+    assert "gptq_quantize_layer_zp" in _err(lib)

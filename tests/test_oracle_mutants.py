@@ -138,7 +138,7 @@ def _pack_reversed(codes):
     return words.astype(np.uint32)
 
 
-def _unpack_unsigned(packed, n):
+def _unpack_unsigned(packed, n, signed=True):
     """nibbles read as unsigned (no sign extension)"""
     packed = np.asarray(packed, dtype=np.uint64)
     codes = np.zeros((packed.shape[0], n), dtype=np.int64)
@@ -148,11 +148,15 @@ def _unpack_unsigned(packed, n):
     return codes
 
 
-def _dequant_ignores_g_idx(packed, scales, g_idx, n):
+def _dequant_ignores_g_idx(packed, scales, g_idx, n, zeros=None):
     """group taken as column // g (processing order assumed), g_idx unused"""
     scales = np.asarray(scales, dtype=np.float64)
     g = -(-n // scales.shape[1])
-    return oracle.unpack_int4(packed, n).astype(np.float64) * scales[:, np.arange(n) // g]
+    gi = np.arange(n) // g
+    codes = oracle.unpack_int4(packed, n, signed=zeros is None).astype(np.float64)
+    if zeros is not None:
+        codes = codes - np.asarray(zeros, dtype=np.float64)[:, gi]
+    return codes * scales[:, gi]
 
 
 def _awq_gptq_factory(h_scale="inverse", w_scale="mul", rescale_d=True, unscale=True):
