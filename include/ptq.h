@@ -91,10 +91,11 @@ int ptq_profile_read(int kernel, double* total_ms, int64_t* launches);
  * be NULL. The call is additive: zero H and d before the first chunk, then
  * call once per chunk of calibration rows (large chunks are faster: each call
  * re-reads and re-writes H once). rows may be 0 (no-op).
- * Workspace: hessian_workspace_bytes(in, rows) (0 is always acceptable; more
- * lets small `in` use split-K partial sums for parallelism).
+ * Workspace: hessian_workspace_bytes(in, rows) bytes: bf16 X needs it (a
+ * transposed copy of up to 65536 rows, split-K partial sums for small `in`,
+ * partial sums of squares); fp32 X runs with none (NULL, 0).
  * Errors: EINVAL (in < 1, rows < 0, ldx < in, bad dtype, NULL H or X with
- * rows > 0, misalignment), EHIP.
+ * rows > 0, misalignment), EWORKSPACE, EHIP.
  * ---------------------------------------------------------------------- */
 size_t hessian_workspace_bytes(int64_t in, int64_t rows);
 int hessian_accumulate(float* H, double* d, int64_t in,

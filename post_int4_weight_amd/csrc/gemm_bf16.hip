@@ -546,6 +546,79 @@ __global__ void transpose_rows_kernel(const uint16_t* __restrict__ X, int64_t ld
     }
 }
 
+// Xt[c][r] = X[r0 + r][c] for r < nr (zero for nr <= r < kt) with 16-byte
+// accesses on both sides: a workgroup moves a 64-column strip over TR_ROWS
+// rows of the chunk through a 64 x 64 LDS tile. With dpart, it also adds up
+// the fp64 squares of the strip's values over those rows, one partial per
+// (row group, column) in dpart[blockIdx.y][c] (X is read once for both).
+// Requires n % 8 == 0 and 16-byte aligned rows of X.
+constexpr int TR_ROWS = 1024;
+__global__ __launch_bounds__(256) void transpose_sumsq_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                              int64_t n, int64_t r0, int64_t nr,
+                                                              uint16_t* __restrict__ Xt, int64_t ldt, int64_t kt,
+                                                              double* __restrict__ dpart) {
+    __shared__ uint32_t tile[64][33];        // 64 rows x 64 bf16 (as 32 words) + 1 word of padding
+    __shared__ double red[32][65];
+    const int t = threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int64_t rg = (int64_t)blockIdx.y * TR_ROWS;
+    const int ch = t & 7;                    // 8-column piece of the strip this thread reads
+    const int rr = t >> 3;                   // row (0..31) within a half tile
+    double sq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sq[j] = 0.0;
+    const bool col_ok = c0 + 8 * ch < n;
+    for (int64_t rb = rg; rb < std::min<int64_t>(kt, rg + TR_ROWS); rb += 64) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = rr + 32 * h;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (col_ok && rb + r < nr) v = *(const uint4*)(X + (r0 + rb + r) * ldx + c0 + 8 * ch);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tile[r][4 * ch + j] = w[j];
+                const double lo = (double)bf16_bits_to_float((uint16_t)(w[j] & 0xFFFFu));
+                const double hi = (double)bf16_bits_to_float((uint16_t)(w[j] >> 16));
+                sq[2 * j] += lo * lo;
+                sq[2 * j + 1] += hi * hi;
+            }
+        }
+        __syncthreads();
+        // write: thread -> column c = t / 8 (+ 32), rows 8 * (t % 8) .. + 7
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = (t >> 3) + 32 * h;
+            const int rw = 8 * (t & 7);
+            uint16_t e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t word = tile[rw + j][c >> 1];
+                e[j] = (uint16_t)((c & 1) ? (word >> 16) : (word & 0xFFFFu));
+            }
+            if (c0 + c < n && rb + rw < kt) {
+                uint4 o;
+                o.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+                o.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+                o.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+                o.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+                *(uint4*)(Xt + (c0 + c) * ldt + rb + rw) = o;
+            }
+        }
+        __syncthreads();
+    }
+    if (!dpart) return;
+    // column sums over the 32 threads that read each 8-column piece, fixed order
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[rr][8 * ch + j] = sq[j];
+    __syncthreads();
+    if (t < 64 && c0 + t < n) {
+        double s = 0.0;
+        for (int i = 0; i < 32; ++i) s += red[i][t];
+        dpart[(int64_t)blockIdx.y * n + c0 + t] = s;
+    }
+}
+
 __global__ void mirror_diag_blocks_kernel(float* H, int64_t n, int bm) {
     const int64_t base = (int64_t)blockIdx.y * bm;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < (int64_t)bm * bm;
@@ -616,6 +689,7 @@ struct XtxPlan {
     int64_t chunk;        // rows per transposed chunk (multiple of 64)
     int nslab;
     int64_t slab_rows;
+    int64_t ngroups;      // row groups of the fused transpose + sums, over all chunks
 };
 
 size_t plan_bytes(const XtxPlan& p, int64_t n) {
@@ -623,6 +697,7 @@ size_t plan_bytes(const XtxPlan& p, int64_t n) {
     if (p.nslab > 1) z.take<double>((size_t)p.nslab * n);
     z.take<uint16_t>((size_t)n * (p.chunk + XT_PAD));
     if (p.nsplit > 1) z.take<float>((size_t)p.nsplit * n * n);
+    z.take<double>((size_t)p.ngroups * n);
     return z.bytes();
 }
 
@@ -637,6 +712,7 @@ XtxPlan plan_xtx(int64_t n, int64_t rows) {
     p.nsplit = s;
     p.slab_rows = std::max<int64_t>(SLAB_ROWS, cdiv(cdiv(rows, MAX_SLABS), 64) * 64);
     p.nslab = (int)std::max<int64_t>(1, cdiv(rows, p.slab_rows));
+    p.ngroups = cdiv(std::max<int64_t>(rows, 1), TR_ROWS) + cdiv(std::max<int64_t>(rows, 1), p.chunk);
     return p;
 }
 
@@ -655,8 +731,10 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
     Arena ar(ws, ws_bytes);
     double* dpart = (p.nslab > 1 && ws) ? ar.take<double>((size_t)p.nslab * n) : nullptr;
     if (!dpart) { p.nslab = 1; p.slab_rows = rows; }
+    // bf16 rows in 16-byte pieces: the transpose also produces the sums of squares
+    const bool vec = (x_dtype == PTQ_BF16) && (n % 8 == 0) && (ldx % 8 == 0) && (((uintptr_t)X & 15u) == 0);
 
-    if (d) {
+    if (d && !vec) {
         dim3 grid((unsigned)cdiv(cdiv(n, 2), 256), (unsigned)p.nslab);
         if (x_dtype == PTQ_BF16)
             hipLaunchKernelGGL(colsumsq_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)X, ldx,
@@ -687,13 +765,23 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
 
     uint16_t* Xt = ar.take<uint16_t>((size_t)n * (p.chunk + XT_PAD));
     float* hpart = (p.nsplit > 1) ? ar.take<float>((size_t)p.nsplit * n * n) : nullptr;
+    double* dsum = ar.take<double>((size_t)p.ngroups * n);
     const int64_t ntiles = (int64_t)p.T * (p.T + 1) / 2;
+    int64_t gofs = 0;   // row groups of the fused sums so far
     for (int64_t r0 = 0; r0 < rows; r0 += p.chunk) {
         const int64_t nr = std::min<int64_t>(p.chunk, rows - r0);
         const int64_t kt = cdiv(nr, 64) * 64;     // contraction depth of this chunk (zero-padded rows)
         const int64_t ldt = kt + XT_PAD;
-        hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)(kt / 64)),
-                           dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt, kt);
+        if (vec) {
+            const int64_t ng = cdiv(kt, TR_ROWS);
+            hipLaunchKernelGGL(transpose_sumsq_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)ng), dim3(256), 0,
+                               st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt, kt,
+                               d ? dsum + gofs * n : (double*)nullptr);
+            gofs += ng;
+        } else {
+            hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)(kt / 64)),
+                               dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt, kt);
+        }
         PTQ_LAUNCH_CHECK();
         const bool last = r0 + p.chunk >= rows;
         const int ns = (p.nsplit > 1 && nr >= p.nsplit * 4096) ? p.nsplit : 1;
@@ -720,6 +808,11 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
             hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(64, (unsigned)p.T), dim3(256), 0, st, H, n, p.bm);
             PTQ_LAUNCH_CHECK();
         }
+    }
+    if (vec && d) {
+        hipLaunchKernelGGL(reduce_slabs_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, d, dsum, (int)gofs,
+                           n);
+        PTQ_LAUNCH_CHECK();
     }
     if (p.nsplit > 1) {
         // chunks that ran without splitting left only their upper triangle: mirror all
