@@ -17,7 +17,7 @@
 //                              U12 = -U11 R12 U22,
 //
 // so 2n^3/3 flops run as large fp32 MFMA GEMMs (gemm_f32.hip) and only
-// 64 x 64 diagonal blocks are factored and inverted inside one workgroup's
+// BASE x BASE (128 x 128) diagonal blocks are factored and inverted inside one workgroup's
 // LDS. A non-positive (or NaN) pivot raises a device flag read once at the end.
 #include "common.hpp"
 
@@ -27,7 +27,8 @@
 namespace ptq {
 namespace {
 
-constexpr int BASE = 64;
+constexpr int BASE = 128;                 // diagonal blocks factored by one workgroup
+constexpr int BASE_THREADS = (BASE / 4) * (BASE / 4);
 
 // lambda = damp * mean(key); key = d (fp64) or diag(H). One workgroup, fixed order.
 __global__ void damping_kernel(const float* H, const double* d, int64_t n, double damp, double* lam) {
@@ -100,7 +101,7 @@ __global__ void fill_int_kernel(int* p, int v) { *p = v; }
 
 // Base case on an m x m diagonal block (m <= BASE, m % 4 == 0): the
 // reversed-order Cholesky A = R R^T (R upper) and U = R^-1 in one right-looking
-// sweep over j = m-1 .. 0. Each of the 256 threads keeps a 4 x 4 tile of the
+// sweep over j = m-1 .. 0. Each of the (BASE/4)^2 threads keeps a 4 x 4 tile of the
 // (symmetric) trailing matrix A and of S = I - R[:, >j] U[>j, :] in registers;
 // at step j only column j of A and row j of S go through LDS:
 //
@@ -111,13 +112,14 @@ __global__ void fill_int_kernel(int* p, int v) { *p = v; }
 // so a step is one barrier, three 16-byte LDS reads and 32 FMAs per thread.
 // Outside m the block is padded with the identity. U is written to the block
 // (zeros below its diagonal). Bit 0 of *flag: non-positive pivot; bit 1: NaN.
-__global__ __launch_bounds__(256) void chol_inv_base_kernel(const float* __restrict__ A, float* __restrict__ U,
-                                                             int m, int64_t ld, int* flag) {
-    static_assert(BASE == 64, "thread ownership below assumes a 64 x 64 block");
+__global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float* __restrict__ A,
+                                                                      float* __restrict__ U, int m, int64_t ld,
+                                                                      int* flag) {
+    constexpr int TB = BASE / 4;               // 4 x 4 tiles per block row
     __shared__ __attribute__((aligned(16))) float colb[BASE][BASE];   // colb[j][i] = A[i][j] at step j
     __shared__ __attribute__((aligned(16))) float rowb[BASE][BASE];   // rowb[j][c] = S[j][c] at step j
     const int t = threadIdx.x;
-    const int ib = t >> 4, kb = t & 15;        // this thread's tile: rows 4*ib.., columns 4*kb..
+    const int ib = t / TB, kb = t % TB;        // this thread's tile: rows 4*ib.., columns 4*kb..
     const int i0 = 4 * ib, k0 = 4 * kb;
     float a[4][4], s[4][4];
 #pragma unroll
@@ -136,9 +138,9 @@ __global__ __launch_bounds__(256) void chol_inv_base_kernel(const float* __restr
             if (i >= m || k >= m) a[di][dk] = (i == k) ? 1.f : 0.f;
             s[di][dk] = (i == k) ? 1.f : 0.f;
         }
-    if (kb == 15) *(float4*)&colb[63][i0] = make_float4(a[0][3], a[1][3], a[2][3], a[3][3]);
-    if (ib == 15) *(float4*)&rowb[63][k0] = make_float4(s[3][0], s[3][1], s[3][2], s[3][3]);
-    for (int jb = 15; jb >= 0; --jb) {
+    if (kb == TB - 1) *(float4*)&colb[BASE - 1][i0] = make_float4(a[0][3], a[1][3], a[2][3], a[3][3]);
+    if (ib == TB - 1) *(float4*)&rowb[BASE - 1][k0] = make_float4(s[3][0], s[3][1], s[3][2], s[3][3]);
+    for (int jb = TB - 1; jb >= 0; --jb) {
 #pragma unroll
         for (int dj = 3; dj >= 0; --dj) {
             const int j = 4 * jb + dj;
@@ -220,7 +222,7 @@ int recurse(Ctx& c, int64_t o, int64_t m) {
     const int64_t n = c.n;
     if (m <= BASE) {
         prof_begin(PROF_FACTOR_BASE, c.st);
-        hipLaunchKernelGGL(chol_inv_base_kernel, dim3(1), dim3(256), 0, c.st, c.A + o * n + o, c.U + o * n + o,
+        hipLaunchKernelGGL(chol_inv_base_kernel, dim3(1), dim3(BASE_THREADS), 0, c.st, c.A + o * n + o, c.U + o * n + o,
                            (int)m, n, c.flag);
         prof_end(PROF_FACTOR_BASE, c.st);
         PTQ_LAUNCH_CHECK();
