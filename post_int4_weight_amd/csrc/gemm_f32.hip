@@ -218,23 +218,25 @@ __global__ __launch_bounds__(NT, 2) void gemm_f32_kernel(GemmArgs g) {
 // fragments: MFMA e of the step takes k = 8j + e from lanes 0-31 and
 // k = 8j + 4 + e from lanes 32-63, for both operands.
 //
-// A ring of four 16-deep stages (64 KB, two workgroups per CU) keeps three
-// stages of loads in flight; one barrier per stage (no memory fence: waits
-// count only this wave's own loads, which retire in order) publishes every
-// wave's copies. Fragment reads of the next step ride under the MFMAs of the
+// A ring of four 16-deep stages (64 KB, two workgroups per CU; three stages
+// and three workgroups for K <= 1024) keeps the next stages' loads in
+// flight; one barrier per stage (no memory fence: waits count only this
+// wave's own loads, which retire in order) publishes every wave's copies. Fragment reads of the next step ride under the MFMAs of the
 // current one. Rows (columns) past M (N) and k past K read clamped, valid
 // addresses; k past K is zeroed in the fragments of the last stage and the
 // other rows are discarded by the epilogue. Requires K, lda, ldb (and N for
 // B_KN) multiples of 4 and 16-byte aligned A and B.
 constexpr int DBK = 16;                 // k per stage
-constexpr int DNST = 4;                 // stages in the ring
+constexpr int DNST_LONG = 4;            // ring stages for long contractions
+constexpr int DNST_SHORT = 3;           // K <= 1024: a smaller ring fits three workgroups per CU
+constexpr int SHORT_K = 1024;
 constexpr int DWG = 2;                  // workgroups per CU the kernel is built for
 constexpr int DSTAGE_BYTES = 2 * BM * DBK * 4;   // A and B tiles of one stage
 constexpr int DQ = BM * DBK * 4 / 1024 / 4;     // 1 KB copies per wave per operand per stage
 constexpr int DJ = DBK / 8;                      // 8-deep MFMA steps per stage
 constexpr int DCH = DBK / 4;                     // 16-byte chunks per K-contiguous LDS row
 constexpr int XCDS = 8;                          // accelerator complex dies, one L2 each
-static_assert(DJ % 2 == 0 && DNST >= 3, "fragment slots alternate; the ring needs three stages");
+static_assert(DJ % 2 == 0, "fragment slots alternate");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_f32_t;
 
@@ -252,8 +254,9 @@ __device__ __forceinline__ void f32_wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool B_KMAJOR>
+template <bool B_KMAJOR, int DNST>
 __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
+    static_assert(DNST >= 3, "the ring needs three stages");
     // Tile order. blockIdx b runs on XCD b % 8. With at least 8 tile rows,
     // XCD x takes the whole rows x, x + 8, x + 16, ... in row-major order:
     // the tiles one XCD runs side by side share A panels (and B panels across
@@ -457,19 +460,29 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
         }
 }
 
-template <bool B_KMAJOR>
-int launch_direct(const GemmArgs& a, hipStream_t st) {
+template <bool B_KMAJOR, int DNST>
+int launch_direct_ring(const GemmArgs& a, hipStream_t st) {
     static bool ready = false;
     if (!ready) {
-        PTQ_HIP(hipFuncSetAttribute((const void*)gemm_f32_direct_kernel<B_KMAJOR>,
+        PTQ_HIP(hipFuncSetAttribute((const void*)gemm_f32_direct_kernel<B_KMAJOR, DNST>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, DNST * DSTAGE_BYTES));
         ready = true;
     }
     const int64_t tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
     const unsigned grid = (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
-    hipLaunchKernelGGL((gemm_f32_direct_kernel<B_KMAJOR>), dim3(grid), dim3(NT), DNST * DSTAGE_BYTES, st, a, tm, tn);
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<B_KMAJOR, DNST>), dim3(grid), dim3(NT), DNST * DSTAGE_BYTES, st, a,
+                       tm, tn);
     PTQ_LAUNCH_CHECK();
     return PTQ_OK;
+}
+
+// Short contractions (the trailing updates) are dominated by the tile's
+// prologue and C read-modify-write: a 3-stage ring (48 KB) lets a third
+// workgroup per CU cover them; long ones keep the deeper ring.
+template <bool B_KMAJOR>
+int launch_direct(const GemmArgs& a, hipStream_t st) {
+    return a.K <= SHORT_K ? launch_direct_ring<B_KMAJOR, DNST_SHORT>(a, st)
+                          : launch_direct_ring<B_KMAJOR, DNST_LONG>(a, st);
 }
 
 bool direct_ok(const GemmArgs& a) {
