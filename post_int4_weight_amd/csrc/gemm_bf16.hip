@@ -15,8 +15,9 @@
 //
 // Tile 256 x 256 (or 128 x 128) per workgroup of 256 threads, 4 wave64s in
 // 2 x 2, each wave a (BM/2)^2 block of 32x32 MFMA accumulators. Two main
-// loops: the direct-to-LDS one (K segments multiples of 32, every call on the
-// path) described further down, and a register-staged one for any K: 16-byte
+// loops: the direct-to-LDS one (K segments multiples of 64, or of 32, which
+// covers every call on the path) described further down, and a
+// register-staged one for any K: 16-byte
 // chunks go through registers into 128-byte LDS rows whose chunk index is
 // XOR-swizzled by (row >> 1) & 7, so the staging writes and the ds_read_b128
 // operand fetches are free of bank conflicts.
@@ -305,35 +306,52 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant (K1 and K2 multiples of 32). global_load_lds_dwordx4
+// Direct-to-LDS variant (K1 and K2 multiples of DKT). global_load_lds_dwordx4
 // moves each lane's 16 bytes straight into LDS at base + 16 * lane, so no
 // staging registers and no ds_write are spent; the XOR swizzle is applied on
-// the global side by choosing which chunk each lane fetches. A ring of four
-// 32-deep stages keeps three stages of loads in flight behind the MFMAs.
+// the global side by choosing which chunk each lane fetches. A ring of NST
+// stages, each DKT deep, keeps the next stages' loads in flight behind the
+// MFMAs. With DKT = 64 one load instruction covers eight whole 128-byte rows
+// of a panel slice (a 32-deep stage moves half rows, so every cache line is
+// requested twice, one stage apart) and there is one barrier per 64 of depth.
 // Rows past M (or N) read a clamped valid row: they only feed output rows
 // (columns) that the epilogue discards.
-constexpr int DK = 32;                 // contraction depth per stage
-constexpr int DROWB = DK * 2;          // bytes per staged row
-constexpr int NSTAGE = 4;
+template <int DKT>
+struct DStage {
+    static constexpr int ROWB = DKT * 2;            // bytes per staged row
+    static constexpr int CH = ROWB / 16;            // 16-byte chunks per staged row
+    static constexpr int KSUB = DKT / 16;           // MFMA k-steps per stage
+    // Slot of chunk c in row r: the 16 lanes of one ds_read_b128 phase read 16
+    // consecutive rows at one chunk, and these swizzles put them on 64
+    // distinct banks (rows sharing a 256-byte bank window get distinct slots).
+    __device__ static __forceinline__ int sw(int r) { return DKT == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+};
 
-template <int BMX>
-constexpr int dsmem_bytes() { return NSTAGE * 2 * BMX * DROWB; }
+// ring depth per stage depth: 4 x 32 or 2 x 64 (128 KB of LDS at BMX = 256)
+template <int DKT>
+constexpr int DNST = DKT == 32 ? 4 : 2;
 
-__device__ __forceinline__ int dswz(int r, int c) { return r * DROWB + 16 * (c ^ ((r >> 2) & 3)); }
+template <int BMX, int DKT, int NST>
+constexpr int dsmem_bytes() { return NST * 2 * BMX * DStage<DKT>::ROWB; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int N>
+template <int N, bool LGKM0>
 __device__ __forceinline__ void wait_vmcnt() {
-    // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt at their maxima
+    // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt at its maximum,
+    // lgkmcnt at 0 (LGKM0) or at its maximum
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8));
 }
 
-template <int BMX, int EPI>
+template <int BMX, int EPI, int DKT, int NST>
 __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g, int64_t nwork) {
+    using S = DStage<DKT>;
+    constexpr int ROWB = S::ROWB, KSUB = S::KSUB;
     constexpr int WT = BMX / 64;
-    constexpr int PER = BMX / 64;      // load instructions per wave per panel per stage (BMX*4 chunks / 64 / 4 waves)
+    constexpr int PER = BMX * S::CH / (64 * 4);   // load instructions per wave per panel per stage
+    constexpr int PANEL = BMX * ROWB;              // bytes of one operand panel per stage
+    static_assert(NST >= 2 && KSUB % 2 == 0 && PER % WT == 0, "pipeline shape");
     int64_t i0, j0, L = 0;
     bool diag = false;
     if (EPI == EPI_HESSIAN) {
@@ -364,30 +382,29 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int p = (wave * PER + q) * 64 + lane;      // 16-byte granule of the panel slab
-        const int r = p >> 2;
-        const int c = (p & 3) ^ ((r >> 2) & 3);
+        const int r = p / S::CH;
+        const int c = (p % S::CH) ^ S::sw(r);
         const int64_t ra = std::min<int64_t>(i0 + r, g.M - 1);
         const int64_t rb = std::min<int64_t>(j0 + r, g.N - 1);
         offA[q] = ra * g.lda + 8 * c;
         offB[q] = rb * g.ldb + 8 * c;
     }
-    const int64_t n1 = g.K1 / DK, n2 = g.K2 / DK;
+    const int64_t n1 = g.K1 / DKT, n2 = g.K2 / DKT;
     const int64_t nst = n1 + n2;
 
-    auto issue = [&](int64_t s, int buf) {
+    // one 16-byte-per-lane copy: q < PER moves A's granules, else B's
+    auto load_one = [&](int64_t s, int buf, int q) {
         const bool seg1 = s < n1;
-        const uint16_t* A = (seg1 ? g.A1 : g.A2) + (seg1 ? s : s - n1) * DK;
-        const uint16_t* B = (seg1 ? B1 : B2) + (seg1 ? s : s - n1) * DK;
-        unsigned char* sa = smem + buf * (2 * BMX * DROWB);
-        unsigned char* sb = sa + BMX * DROWB;
+        const bool isa = q < PER;
+        const int qq = isa ? q : q - PER;
+        const uint16_t* P = isa ? ((seg1 ? g.A1 : g.A2) + (seg1 ? s : s - n1) * DKT + offA[qq])
+                                : ((seg1 ? B1 : B2) + (seg1 ? s : s - n1) * DKT + offB[qq]);
+        unsigned char* dst = smem + buf * (2 * PANEL) + (isa ? 0 : PANEL) + (wave * PER + qq) * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)P, (lds_ptr_t)dst, 16, 0, 0);
+    };
+    auto issue = [&](int64_t s, int buf) {
 #pragma unroll
-        for (int q = 0; q < PER; ++q)
-            __builtin_amdgcn_global_load_lds((const void*)(A + offA[q]), (lds_ptr_t)(sa + (wave * PER + q) * 1024),
-                                             16, 0, 0);
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-            __builtin_amdgcn_global_load_lds((const void*)(B + offB[q]), (lds_ptr_t)(sb + (wave * PER + q) * 1024),
-                                             16, 0, 0);
+        for (int q = 0; q < 2 * PER; ++q) load_one(s, buf, q);
     };
 
     f32x16 acc[WT][WT];
@@ -398,41 +415,31 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // Software pipeline over half-stages (16-deep sub-steps): the fragment
-    // reads of the next sub-step are interleaved with the MFMAs of the current
-    // one, so after the prologue no LDS latency is exposed. The stage barrier
-    // sits in the middle of a stage (between its two sub-steps): by then every
-    // wave has finished reading the buffer the next issue overwrites (it was
-    // last read one full stage earlier). Waits: this wave's copies of a stage
-    // have landed once only the younger stages' loads are outstanding (loads
-    // retire in order); the barrier (no memory fence, which would drain every
-    // prefetch) then makes all waves' copies visible.
-    const int fsw = (li >> 2) & 3;   // fragment swizzle term, lane-only
+    // Software pipeline over k-steps (16 deep): the fragment reads of the next
+    // k-step are interleaved with the MFMAs of the current one, so after the
+    // prologue no LDS latency is exposed. The stage barrier sits before a
+    // stage's last k-step, whose fragments are already in registers: each
+    // wave first waits until its reads of the stage have returned (lgkmcnt 0)
+    // and its copies of the next stage have landed (loads retire in order, so
+    // only the younger stages' copies may still be outstanding); after the
+    // barrier (no memory fence, which would drain every prefetch) the next
+    // stage is visible to all waves and this stage's buffer is free, and the
+    // copies of stage s + NST go into it.
+    const int fsw = S::sw(li);   // fragment swizzle term, lane-only (row = wm + 32 a + li)
     bf16x8 fa[2][WT], fb[2][WT];
-    auto frags = [&](int64_t s, int kk, int slot) {
-        const unsigned char* As = smem + (s % NSTAGE) * (2 * BMX * DROWB);
-        const unsigned char* Bs = As + BMX * DROWB;
-        const int c = (2 * kk + lh) ^ fsw;
-#pragma unroll
-        for (int a = 0; a < WT; ++a) fa[slot][a] = *(const bf16x8*)(As + (wm + 32 * a + li) * DROWB + 16 * c);
-#pragma unroll
-        for (int b = 0; b < WT; ++b) fb[slot][b] = *(const bf16x8*)(Bs + (wn + 32 * b + li) * DROWB + 16 * c);
-    };
-    // single-instruction pieces for the hand-interleaved half-stage below
-    auto load_one = [&](int64_t s, int buf, int q) {
-        const bool seg1 = s < n1;
-        const bool isa = q < PER;
-        const int qq = isa ? q : q - PER;
-        const uint16_t* P = isa ? ((seg1 ? g.A1 : g.A2) + (seg1 ? s : s - n1) * DK + offA[qq])
-                                : ((seg1 ? B1 : B2) + (seg1 ? s : s - n1) * DK + offB[qq]);
-        unsigned char* dst = smem + buf * (2 * BMX * DROWB) + (isa ? 0 : BMX * DROWB) + (wave * PER + qq) * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)P, (lds_ptr_t)dst, 16, 0, 0);
-    };
+    // k-step kk reads chunk 2 kk + lh of its rows
+    auto fragp = [&](int64_t s, int kk) { return smem + (s % NST) * (2 * PANEL) + 16 * ((2 * kk + lh) ^ fsw); };
+    // fragment q of a k-step, in the order the MFMAs (a-major) consume them:
+    // A block 0, the B blocks, then the other A blocks
     auto read_one = [&](int64_t s, int kk, int slot, int q) {
-        const unsigned char* As = smem + (s % NSTAGE) * (2 * BMX * DROWB);
-        const int c = (2 * kk + lh) ^ fsw;
-        if (q < WT) fa[slot][q] = *(const bf16x8*)(As + (wm + 32 * q + li) * DROWB + 16 * c);
-        else fb[slot][q - WT] = *(const bf16x8*)(As + BMX * DROWB + (wn + 32 * (q - WT) + li) * DROWB + 16 * c);
+        const unsigned char* As = fragp(s, kk);
+        if (q == 0) fa[slot][0] = *(const bf16x8*)(As + (wm + li) * ROWB);
+        else if (q <= WT) fb[slot][q - 1] = *(const bf16x8*)(As + PANEL + (wn + 32 * (q - 1) + li) * ROWB);
+        else fa[slot][q - WT] = *(const bf16x8*)(As + (wm + 32 * (q - WT) + li) * ROWB);
+    };
+    auto frags = [&](int64_t s, int kk, int slot) {
+#pragma unroll
+        for (int q = 0; q < 2 * WT; ++q) read_one(s, kk, slot, q);
     };
     auto mfma_one = [&](int slot, int idx) {
         const int a = idx / WT, b = idx % WT;
@@ -440,69 +447,78 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
-        for (int a = 0; a < WT; ++a)
-#pragma unroll
-            for (int b = 0; b < WT; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][a], fb[slot][b], acc[a][b], 0, 0, 0);
+        for (int i = 0; i < WT * WT; ++i) mfma_one(slot, i);
     };
-    // one fragment read per (WT/2) MFMAs: reads of the next sub-step ride
-    // under the MFMAs (MFMAs first: the wait before the first one then only
-    // covers reads issued a whole sub-step earlier)
+    // The reads of the next k-step ride under the first 2 WT MFMAs of the
+    // current one, one per MFMA, so the last of them has the remaining
+    // WT^2 - 2 WT MFMAs' time to return before the next k-step needs it.
     auto interleave = [&]() {
 #pragma unroll
         for (int i = 0; i < 2 * WT; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, WT / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        if constexpr (WT * WT > 2 * WT) __builtin_amdgcn_sched_group_barrier(0x008, WT * WT - 2 * WT, 0);
     };
 
-    // Every issue moves 2*PER chunks per wave; past the last stage the issue
-    // repeats the last stage into the free buffer, so the counts (and the
-    // waits) are the same on every iteration and the loop has no joins that
-    // would force a full lgkmcnt drain.
+    // Past the last stage the issue repeats the last stage into the free
+    // buffer, so the counts (and the waits) are the same on every iteration
+    // and the loop has no joins that would force a full lgkmcnt drain.
     if (nst > 0) {
-        for (int64_t s = 0; s < NSTAGE - 1; ++s) issue(std::min<int64_t>(s, nst - 1), (int)s);
-        wait_vmcnt<4 * PER>();
+#pragma unroll
+        for (int s = 0; s < NST; ++s) issue(std::min<int64_t>(s, nst - 1), s);
+        wait_vmcnt<(NST - 1) * 2 * PER, false>();
         __builtin_amdgcn_s_barrier();
         frags(0, 0, 0);
+        auto steps = [&](int64_t s) {
+#pragma unroll
+            for (int kk = 0; kk + 1 < KSUB; ++kk) {
+                frags(s, kk + 1, (kk + 1) & 1);
+                mfmas(kk & 1);
+                interleave();
+            }
+        };
         for (int64_t s = 0; s + 1 < nst; ++s) {
-            frags(s, 1, 1);
-            mfmas(0);
-            interleave();
-            wait_vmcnt<2 * PER>();
+            steps(s);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(NST - 2) * 2 * PER, true>();
             __builtin_amdgcn_s_barrier();
             {
-                // one copy, one fragment read and WT/2 MFMAs per group, pinned
-                // in that order: a copy that waits for the address unit then
-                // stalls at most WT/2 MFMAs' worth of issue
-                const int64_t sl = std::min<int64_t>(s + NSTAGE - 1, nst - 1);
-                const int bl = (int)((s + NSTAGE - 1) % NSTAGE);
+                // After the barrier: the last k-step's MFMAs, the next
+                // stage's first fragment reads (one after each of the first
+                // 2 WT MFMAs) and the 2 PER copies of stage s + NST spread
+                // evenly over the MFMAs, pinned in that order: a copy that
+                // waits for the address unit stalls at most one MFMA's issue.
+                const int64_t sl = std::min<int64_t>(s + NST, nst - 1);
+                const int bl = (int)(s % NST);
+                constexpr int NL = 2 * PER, NM = WT * WT;
 #pragma unroll
-                for (int q = 0; q < 2 * WT; ++q) {
+                for (int m = 0; m < NM; ++m) {
+                    mfma_one(1, m);
+                    if (m < 2 * WT) read_one(s + 1, 0, 0, m);
 #pragma unroll
-                    for (int m = 0; m < WT / 2; ++m) mfma_one(1, q * (WT / 2) + m);
-                    read_one(s + 1, 0, 0, q);
-                    load_one(sl, bl, q);
+                    for (int l = m * NL / NM; l < (m + 1) * NL / NM; ++l) load_one(sl, bl, l);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
-        frags(nst - 1, 1, 1);
-        mfmas(0);
+        steps(nst - 1);
         mfmas(1);
     }
+    wait_vmcnt<0, true>();
     __syncthreads();
     store_tile<BMX, EPI>(g, acc, i0, j0, diag, L, smem);
 }
 
 // Opt a kernel into more than 64 KB of dynamic LDS (once per instantiation).
-template <int BMX, int EPI, bool DIRECT>
+template <int BMX, int EPI, int DKT>
 int prepare_kernel() {
     static bool done = false;
     if (!done) {
-        if (DIRECT)
-            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_direct_kernel<BMX, EPI>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, dsmem_bytes<BMX>()));
+        if constexpr (DKT > 0)
+            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, DNST<DKT>>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        dsmem_bytes<BMX, DKT, DNST<DKT>>()));
         else
             PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_kernel<BMX, EPI>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, smem_bytes<BMX>()));
@@ -511,16 +527,27 @@ int prepare_kernel() {
     return PTQ_OK;
 }
 
-// Launch either variant: the direct one when both K segments are multiples of DK.
+template <int BMX, int EPI, int DKT>
+int launch_direct(const Bf16GemmArgs& g, int64_t nwork, unsigned grid, unsigned grid_y, hipStream_t st) {
+    constexpr int nst = DNST<DKT>;
+    constexpr int lds = dsmem_bytes<BMX, DKT, nst>();
+    PTQ_TRY((prepare_kernel<BMX, EPI, DKT>()));
+    hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, nst>), dim3(grid, grid_y), dim3(NTH), lds, st, g,
+                       nwork);
+    return PTQ_OK;
+}
+
+// Launch the direct variant when both K segments are multiples of its stage
+// depth (64, else 32), the register-staged one otherwise.
 template <int BMX, int EPI>
 int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t st) {
     const unsigned grid = (unsigned)(EPI == EPI_HESSIAN ? 256 * hessian_rounds(g.T) : cdiv(nwork, NXCD) * NXCD);
-    if (g.K1 % DK == 0 && g.K2 % DK == 0 && g.M > 0 && g.N > 0) {
-        PTQ_TRY((prepare_kernel<BMX, EPI, true>()));
-        hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI>), dim3(grid, grid_y), dim3(NTH),
-                           dsmem_bytes<BMX>(), st, g, nwork);
+    if (g.M > 0 && g.N > 0 && g.K1 % 64 == 0 && g.K2 % 64 == 0) {
+        PTQ_TRY((launch_direct<BMX, EPI, 64>(g, nwork, grid, grid_y, st)));
+    } else if (g.M > 0 && g.N > 0 && g.K1 % 32 == 0 && g.K2 % 32 == 0) {
+        PTQ_TRY((launch_direct<BMX, EPI, 32>(g, nwork, grid, grid_y, st)));
     } else {
-        PTQ_TRY((prepare_kernel<BMX, EPI, false>()));
+        PTQ_TRY((prepare_kernel<BMX, EPI, 0>()));
         hipLaunchKernelGGL((gemm_bf16_nt_kernel<BMX, EPI>), dim3(grid, grid_y), dim3(NTH), smem_bytes<BMX>(), st,
                            g, nwork);
     }
