@@ -265,6 +265,33 @@ int pack_int4(const int8_t* codes, int64_t out, int64_t in, int bits, uint32_t* 
 int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* g_idx, const int8_t* zeros,
                     int64_t out, int64_t in, int group_size, int out_dtype, void* What, int64_t ldo, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Calibration output error of a quantized layer (evaluation; not part of
+ * producing the codes).  [OBJ] "A strong answer": the objective
+ * ||X W^T - X What^T||^2 (the quantity GPTQ's loop and AWQ's grid search
+ * minimise) and its normaliser ||X W^T||^2; the page's table reports the
+ * former per element as output MSE.
+ *
+ * What[r][c] = (codes[r][c] - z) * scales[r][gi] / s[c] with
+ * gi = g_idx[c] (g_idx may be NULL: gi = c / group_size), z =
+ * zeros[r][gi] (zeros may be NULL: z = 0, the symmetric grid), s fp32[in]
+ * AWQ's channel scales (may be NULL: s = 1). codes int8[out, in] (row stride
+ * in), scales fp32 and zeros int8 [out, ceil(in / group_size)]; a group
+ * index outside that range makes the result NaN. X [rows, in] and W [out, in]
+ * bf16 or fp32. out2 (host, 2 doubles) receives ||X (W - What)^T||_F^2 and
+ * ||X W^T||_F^2. What is formed in fp64; with bf16 X the products run on the
+ * bf16 MFMA with W and W - What split into a bf16 high part plus a bf16
+ * residual (~16 significant bits), with fp32 X on the fp32 MFMA GEMM; the sums
+ * of squares are fp64. The workspace depends on x_dtype. Synchronous.
+ * Errors: EINVAL, EWORKSPACE, EHIP.
+ * ---------------------------------------------------------------------- */
+size_t layer_output_error_workspace_bytes(int64_t out, int64_t in, int64_t rows, int x_dtype);
+int layer_output_error(const void* X, int x_dtype, int64_t rows, int64_t ldx,
+                       const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                       const int8_t* codes, const float* scales, const int32_t* g_idx, const int8_t* zeros,
+                       const float* s, int group_size, double* out2,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

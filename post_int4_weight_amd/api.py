@@ -69,6 +69,9 @@ def _load() -> ctypes.CDLL:
         "dequantize_int4": (i32, [vp, vp, vp, vp, i64, i64, i32, i32, vp, i64, vp]),
         "gptq_quantize_layer_zp": (i32, [vp, i32, i64, i64, i64, vp, vp, i32, i32, dbl, i32, i32, vp, vp, vp, vp, vp,
                                          dp, vp, sz, vp]),
+        "layer_output_error_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "layer_output_error": (i32, [vp, i32, i64, i64, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, dp, vp, sz,
+                                     vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -319,6 +322,30 @@ def dequantize_int4(packed: torch.Tensor, scales: torch.Tensor, g_idx, n: int, g
     _check(_lib.dequantize_int4(_ptr(packed), _ptr(scales), _ptr(g_idx), _ptr(zeros), out, n, group_size,
                                 _dtype_code(What), _ptr(What), ldo, _stream()))
     return What
+
+
+# ------------------------------------------------------------ evaluation ---
+
+def layer_output_error_workspace_bytes(out: int, n: int, rows: int, x_dtype: int) -> int:
+    return int(_lib.layer_output_error_workspace_bytes(out, n, rows, x_dtype))
+
+
+def layer_output_error(X, W, codes, scales, g_idx=None, zeros=None, s=None, group_size=128, workspace=None):
+    """layer_output_error (include/ptq.h): (||X (W - What)^T||^2, ||X W^T||^2) with
+    What = (codes - zeros[g_idx]) * scales[g_idx] / s."""
+    out, n = W.shape
+    rows = X.shape[0]
+    ldw = _rowmajor(W, "W")
+    ldx = _rowmajor(X, "X")
+    if codes.dtype != torch.int8 or not codes.is_contiguous() or tuple(codes.shape) != (out, n):
+        raise ValueError("codes must be a contiguous int8 [out, in] tensor")
+    xd = _dtype_code(X)
+    ws, wsb = _workspace(layer_output_error_workspace_bytes(out, n, rows, xd), W.device, workspace)
+    res = (ctypes.c_double * 2)()
+    _check(_lib.layer_output_error(_ptr(X), xd, rows, ldx, _ptr(W), _dtype_code(W), out, n, ldw, _ptr(codes),
+                                   _ptr(scales), _ptr(g_idx), _ptr(zeros), _ptr(s), group_size, res, _ptr(ws), wsb,
+                                   _stream()))
+    return res[0], res[1]
 
 
 # ------------------------------------------------------------- test hook ---

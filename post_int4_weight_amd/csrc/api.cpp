@@ -398,4 +398,32 @@ int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* 
                                (hipStream_t)stream);
 }
 
+size_t layer_output_error_workspace_bytes(int64_t out, int64_t in, int64_t rows, int x_dtype) {
+    if (out < 1 || in < 1 || rows < 1 || !dtype_ok(x_dtype)) return 0;
+    return output_error_ws_bytes(out, in, rows, x_dtype);
+}
+
+int layer_output_error(const void* X, int x_dtype, int64_t rows, int64_t ldx, const void* W, int w_dtype, int64_t out,
+                       int64_t in, int64_t ldw, const int8_t* codes, const float* scales, const int32_t* g_idx,
+                       const int8_t* zeros, const float* s, int group_size, double* out2, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    const char* fn = "layer_output_error";
+    if (out < 1 || in < 1 || rows < 1) return fail(PTQ_EINVAL, "%s: empty layer (out, in, rows >= 1 required)", fn);
+    if (in % 8) return fail(PTQ_EINVAL, "%s: in must be a multiple of 8", fn);
+    if (!dtype_ok(w_dtype) || !dtype_ok(x_dtype)) return fail(PTQ_EINVAL, "%s: bad dtype", fn);
+    if (ldw < in || ldw % elems16(w_dtype) || ldx < in || ldx % elems16(x_dtype))
+        return fail(PTQ_EINVAL, "%s: bad ldw/ldx", fn);
+    if (group_size < 1) return fail(PTQ_EINVAL, "%s: group_size = %d", fn, group_size);
+    if (!X || !W || !codes || !scales || !out2) return fail(PTQ_EINVAL, "%s: NULL array", fn);
+    if (!aligned16(W) || !aligned16(X) || ((uintptr_t)scales & 3u) || (g_idx && ((uintptr_t)g_idx & 3u)) ||
+        (s && ((uintptr_t)s & 3u)))
+        return fail(PTQ_EINVAL, "%s: misaligned pointer", fn);
+    const size_t need = output_error_ws_bytes(out, in, rows, x_dtype);
+    if (!workspace || workspace_bytes < need)
+        return fail(PTQ_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(PTQ_EINVAL, "%s: misaligned workspace", fn);
+    return run_output_error(X, x_dtype, rows, ldx, W, w_dtype, out, in, ldw, codes, scales, g_idx, zeros, s,
+                            group_size, out2, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -168,6 +168,42 @@ __global__ void reduce_err_kernel(const double* partial, int64_t ntiles, double*
     if (threadIdx.x == 0) err[a] = red[0];
 }
 
+// Calibration output error of a quantized layer: per element of W,
+// What = (code - zero) * scale[gi] / s (fp64) and dW = W - What. Batch 0 of
+// the outputs gets dW, batch 1 gets W itself: as bf16 high and residual parts
+// (hi, lo) for the bf16 MFMA error GEMM, or as fp32 (f32). A group index
+// outside [0, ngroups) makes What NaN.
+template <typename T>
+__global__ void eval_prep_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n,
+                                 const int8_t* __restrict__ codes, const float* __restrict__ scales,
+                                 const int32_t* __restrict__ g_idx, const int8_t* __restrict__ zeros,
+                                 const float* __restrict__ s, int g, int64_t ngroups, uint16_t* __restrict__ hi,
+                                 uint16_t* __restrict__ lo, float* __restrict__ f32) {
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= out * n) return;
+    const int64_t r = id / n, c = id % n;
+    const int64_t gi = g_idx ? (int64_t)g_idx[c] : c / g;
+    const double w = (double)load_as_float<T>(W, r * ldw + c);
+    double what = __builtin_nan("");
+    if (gi >= 0 && gi < ngroups) {
+        const double q = (double)codes[r * n + c] - (zeros ? (double)zeros[r * ngroups + gi] : 0.0);
+        what = q * (double)scales[r * ngroups + gi];
+        if (s) what /= (double)s[c];
+    }
+    const float v[2] = {(float)(w - what), (float)w};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t o = b * out * n + id;
+        if (f32) {
+            f32[o] = v[b];
+        } else {
+            const uint16_t h = float_to_bf16_bits(v[b]);
+            hi[o] = h;
+            lo[o] = float_to_bf16_bits(v[b] - bf16_bits_to_float(h));
+        }
+    }
+}
+
 constexpr int64_t SLAB = 1024;
 constexpr int64_t F32_SLICE = 1 << 16;
 
@@ -321,6 +357,96 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
         hipLaunchKernelGGL(awq_quant_kernel<float>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st, (const float*)W,
                            ldw, out, n, g, qmax, sb, 1, (uint16_t*)nullptr, (uint16_t*)nullptr, codes, scales, ngroups);
     PTQ_LAUNCH_CHECK();
+    PTQ_HIP(hipStreamSynchronize(st));
+    return PTQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// ||X (W - What)^T||^2 and ||X W^T||^2 (the objective of "A strong answer" and
+// its normaliser) for a quantized layer. bf16 X: both through the bf16 MFMA
+// error GEMM (W and dW as hi + lo bf16 pairs, E never written). fp32 X: E in
+// row chunks through the fp32 MFMA GEMM, then fp64 sums of squares.
+constexpr int64_t EVAL_ROWS = 4096;   // fp32 path: rows of X per GEMM
+
+size_t output_error_ws_bytes(int64_t out, int64_t n, int64_t rows, int x_dtype) {
+    Sizer z;
+    z.take<double>(2);
+    if (x_dtype == PTQ_BF16) {
+        z.take<uint16_t>((size_t)2 * out * n);
+        z.take<uint16_t>((size_t)2 * out * n);
+        z.take<double>((size_t)2 * cdiv(rows, 256) * cdiv(out, 256));
+    } else {
+        const int64_t rc = std::min<int64_t>(rows, EVAL_ROWS);
+        z.take<float>((size_t)2 * out * n);
+        z.take<float>((size_t)rc * out);
+        z.take<double>((size_t)2 * cdiv(rows, EVAL_ROWS) * cdiv(rc * out, F32_SLICE));
+    }
+    return z.bytes();
+}
+
+int run_output_error(const void* X, int x_dtype, int64_t rows, int64_t ldx, const void* W, int w_dtype, int64_t out,
+                     int64_t n, int64_t ldw, const int8_t* codes, const float* scales, const int32_t* g_idx,
+                     const int8_t* zeros, const float* s, int g, double* out2, void* ws, size_t ws_bytes,
+                     hipStream_t st) {
+    Arena ar(ws, ws_bytes);
+    double* err = ar.take<double>(2);
+    const int64_t ngroups = cdiv(n, g);
+    const bool bf = (x_dtype == PTQ_BF16);
+    uint16_t *hi = nullptr, *lo = nullptr;
+    float *f32 = nullptr, *E = nullptr;
+    double* partial = nullptr;
+    const int64_t rc = std::min<int64_t>(rows, EVAL_ROWS);
+    const int64_t nchunk = cdiv(rows, EVAL_ROWS), per_chunk = cdiv(rc * out, F32_SLICE);
+    if (bf) {
+        hi = ar.take<uint16_t>((size_t)2 * out * n);
+        lo = ar.take<uint16_t>((size_t)2 * out * n);
+        partial = ar.take<double>((size_t)2 * cdiv(rows, 256) * cdiv(out, 256));
+    } else {
+        f32 = ar.take<float>((size_t)2 * out * n);
+        E = ar.take<float>((size_t)rc * out);
+        partial = ar.take<double>((size_t)2 * nchunk * per_chunk);
+    }
+    if (!err || !partial || (bf && (!hi || !lo)) || (!bf && (!f32 || !E))) {
+        set_error("layer_output_error: workspace of %zu bytes, %zu needed", ws_bytes,
+                  output_error_ws_bytes(out, n, rows, x_dtype));
+        return PTQ_EWORKSPACE;
+    }
+    const unsigned blocks = (unsigned)cdiv(out * n, 256);
+    if (w_dtype == PTQ_BF16)
+        hipLaunchKernelGGL(eval_prep_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t*)W, ldw, out, n,
+                           codes, scales, g_idx, zeros, s, g, ngroups, hi, lo, f32);
+    else
+        hipLaunchKernelGGL(eval_prep_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)W, ldw, out, n,
+                           codes, scales, g_idx, zeros, s, g, ngroups, hi, lo, f32);
+    PTQ_LAUNCH_CHECK();
+    if (bf) {
+        int64_t ntiles = 0;
+        PTQ_TRY(launch_awq_error_gemm((const uint16_t*)X, ldx, rows, n, hi, lo, n, out, out * n, 2, partial, &ntiles,
+                                      st));
+        hipLaunchKernelGGL(reduce_err_kernel, dim3(2), dim3(256), 0, st, partial, ntiles, err);
+        PTQ_LAUNCH_CHECK();
+    } else {
+        // slice partials packed densely: full chunks first, then the last
+        const int64_t last = rows - (nchunk - 1) * EVAL_ROWS;
+        const int64_t total = (nchunk - 1) * per_chunk + cdiv(last * out, F32_SLICE);
+        for (int b = 0; b < 2; ++b) {
+            for (int64_t k = 0; k < nchunk; ++k) {
+                const int64_t r0 = k * EVAL_ROWS, nr = std::min<int64_t>(EVAL_ROWS, rows - r0);
+                GemmArgs ga{};
+                ga.M = nr; ga.N = out; ga.K = n;
+                ga.A = (const float*)X + r0 * ldx; ga.lda = ldx; ga.layout_a = A_MK;
+                ga.B = f32 + (int64_t)b * out * n; ga.ldb = n; ga.layout_b = B_NK;
+                ga.C = E; ga.ldc = out; ga.alpha = 1.f; ga.beta_one = 0; ga.tri = TRI_NONE; ga.upper_only = 0;
+                PTQ_TRY(launch_gemm_f32(ga, st));
+                hipLaunchKernelGGL(sumsq_slices_kernel, dim3((unsigned)cdiv(nr * out, F32_SLICE)), dim3(256), 0, st, E,
+                                   nr * out, F32_SLICE, partial + b * total + k * per_chunk);
+                PTQ_LAUNCH_CHECK();
+            }
+        }
+        hipLaunchKernelGGL(reduce_err_kernel, dim3(2), dim3(256), 0, st, partial, total, err);
+        PTQ_LAUNCH_CHECK();
+    }
+    PTQ_HIP(hipMemcpyAsync(out2, err, sizeof(double) * 2, hipMemcpyDeviceToHost, st));
     PTQ_HIP(hipStreamSynchronize(st));
     return PTQ_OK;
 }

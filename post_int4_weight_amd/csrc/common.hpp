@@ -172,6 +172,11 @@ int launch_dequant_int4(const uint32_t* packed, const float* scales, const int32
 
 // Stage 4 (awq.hip)
 size_t awq_ws_bytes(int64_t out, int64_t n, int64_t rows, int n_alpha);
+size_t output_error_ws_bytes(int64_t out, int64_t n, int64_t rows, int x_dtype);
+int run_output_error(const void* X, int x_dtype, int64_t rows, int64_t ldx, const void* W, int w_dtype, int64_t out,
+                     int64_t n, int64_t ldw, const int8_t* codes, const float* scales, const int32_t* g_idx,
+                     const int8_t* zeros, const float* s, int g, double* out2, void* ws, size_t ws_bytes,
+                     hipStream_t st);
 int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, const void* X,
             int x_dtype, int64_t rows, int64_t ldx, const float* alphas, int n_alpha, int bits,
             int g, float* alpha_best, double* err_per_alpha, float* s, int8_t* codes,

@@ -22,7 +22,7 @@ def test_header_lists_the_entry_points():
     names = _declared_functions()
     for n in ("hessian_accumulate", "gptq_inverse_factor", "gptq_quantize_columns", "gptq_quantize_layer",
               "awq_search_alpha", "ptq_last_error", "ptq_test_gemm_f32", "pack_int4", "dequantize_int4",
-              "awq_gptq_quantize_layer", "gptq_quantize_layer_zp"):
+              "awq_gptq_quantize_layer", "gptq_quantize_layer_zp", "layer_output_error"):
         assert n in names
 
 
@@ -183,3 +183,27 @@ def test_zero_point_validation(lib):
     assert call(g=0) == 1
     assert call() == 4                # workspace too small
     assert "gptq_quantize_layer_zp" in _err(lib)
+
+
+def test_output_error_validation(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    res = (ctypes.c_double * 2)()
+    ws = lib.layer_output_error_workspace_bytes(32, 256, 64, 0)
+    assert ws > 0 and lib.layer_output_error_workspace_bytes(32, 256, 64, 1) > 0
+    assert lib.layer_output_error_workspace_bytes(0, 256, 64, 0) == 0
+    assert lib.layer_output_error_workspace_bytes(32, 256, 64, 7) == 0
+
+    def call(out=32, n=256, rows=64, xd=0, wd=0, g=128, ldx=256, ldw=256, codes=fake, r=res, wsb=ws, w=fake):
+        return lib.layer_output_error(fake, xd, rows, ldx, fake, wd, out, n, ldw, codes, fake, None, None, None, g, r,
+                                      w, wsb, None)
+    assert call(rows=0) == 1
+    assert call(out=0) == 1
+    assert call(n=250, ldx=256, ldw=256) == 1        # in not a multiple of 8
+    assert call(xd=3) == 1
+    assert call(g=0) == 1
+    assert call(ldx=100) == 1
+    assert call(codes=None) == 1
+    assert call(r=None) == 1
+    assert "layer_output_error" in _err(lib)
+    assert call(wsb=ws - 1) == 4                      # PTQ_EWORKSPACE
+    assert call(w=None) == 4
