@@ -71,6 +71,7 @@ int ptq_abi_version(void);
  *   2 diagonal-block factor/inverse 3 GPTQ in-block column loop
  *   4 GPTQ trailing fp32 GEMM       5 AWQ error GEMM
  *   6 GPTQ fp32 update inside a super-block of columns
+ *   7 fp32 GEMMs run as bf16 MFMAs on three-term bf16 splits (inside 1)
  * Enabling (any mask, 0 included) discards earlier records. ptq_profile_read
  * waits for the recorded events of class `kernel` and returns the sum of
  * their elapsed times (ms) and the number of launches. Process-wide; calls

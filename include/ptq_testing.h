@@ -28,6 +28,18 @@ int ptq_test_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
                       int64_t ldb, int layout_b, float* C, int64_t ldc, float alpha, int beta_one, int tri,
                       int upper_only, void* stream);
 
+/* The same product on the bf16 MFMA from three-term bf16 splits of A and B
+ * (x = hi + mid + lo, six term products kept: fp32 GEMM accuracy), as used
+ * for the large GEMMs of the U recursion. Output tiles are 256 x 256
+ * (upper_only: tiles on or above the diagonal). The workspace (16-byte
+ * aligned, size from the query) holds the split planes. Asynchronous.
+ * Returns PTQ_OK, PTQ_EINVAL, PTQ_EWORKSPACE or PTQ_EHIP. */
+size_t ptq_test_gemm_f32_split3_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int ptq_test_gemm_f32_split3(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int layout_a,
+                             const float* B, int64_t ldb, int layout_b, float* C, int64_t ldc, float alpha,
+                             int beta_one, int tri, int upper_only, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,9 @@ def _load() -> ctypes.CDLL:
         "gptq_quantize_layer_zp": (i32, [vp, i32, i64, i64, i64, vp, vp, i32, i32, dbl, i32, i32, vp, vp, vp, vp, vp,
                                          dp, vp, sz, vp]),
         "layer_output_error_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "ptq_test_gemm_f32_split3_workspace_bytes": (sz, [i64, i64, i64]),
+        "ptq_test_gemm_f32_split3": (i32, [i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64, ctypes.c_float, i32,
+                                           i32, i32, vp, sz, vp]),
         "layer_output_error": (i32, [vp, i32, i64, i64, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, dp, vp, sz,
                                      vp]),
     }
@@ -121,7 +124,7 @@ def _rowmajor(t: torch.Tensor, name: str):
 # ------------------------------------------------------------- profiling ---
 
 PROFILE_KERNELS = {"xtx_gemm": 0, "factor_gemm": 1, "factor_base": 2, "block_loop": 3, "trail_gemm": 4,
-                   "awq_gemm": 5, "inner_gemm": 6}
+                   "awq_gemm": 5, "inner_gemm": 6, "split3_gemm": 7}
 
 
 def profile_enable(kernels=()):
@@ -354,4 +357,13 @@ def _test_gemm_f32(A, B, C, M, N, K, layout_a, layout_b, alpha=1.0, beta_one=0, 
     """ptq_test_gemm_f32 (include/ptq_testing.h): the fp32 MFMA GEMM alone."""
     _check(_lib.ptq_test_gemm_f32(M, N, K, _ptr(A), A.stride(0), layout_a, _ptr(B), B.stride(0), layout_b, _ptr(C),
                                   C.stride(0), float(alpha), int(beta_one), int(tri), int(upper_only), _stream()))
+    return C
+
+
+def _test_gemm_f32_split3(A, B, C, M, N, K, layout_a, layout_b, alpha=1.0, beta_one=0, tri=0, upper_only=0):
+    """ptq_test_gemm_f32_split3 (include/ptq_testing.h): the same product on the bf16 MFMA from split operands."""
+    ws, wsb = _workspace(int(_lib.ptq_test_gemm_f32_split3_workspace_bytes(M, N, K)), C.device, None)
+    _check(_lib.ptq_test_gemm_f32_split3(M, N, K, _ptr(A), A.stride(0), layout_a, _ptr(B), B.stride(0), layout_b,
+                                         _ptr(C), C.stride(0), float(alpha), int(beta_one), int(tri),
+                                         int(upper_only), _ptr(ws), wsb, _stream()))
     return C

@@ -311,6 +311,37 @@ int ptq_test_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     return launch_gemm_f32(g, (hipStream_t)stream);
 }
 
+size_t ptq_test_gemm_f32_split3_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return 0;
+    Sizer z;
+    z.take<uint16_t>(gemm_f32_split3_elems(M, K));
+    z.take<uint16_t>(gemm_f32_split3_elems(N, K));
+    return z.bytes();
+}
+
+int ptq_test_gemm_f32_split3(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int layout_a,
+                             const float* B, int64_t ldb, int layout_b, float* C, int64_t ldc, float alpha,
+                             int beta_one, int tri, int upper_only, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (M < 0 || N < 0 || K < 0 || !A || !B || !C || (layout_a != 0 && layout_a != 1) ||
+        (layout_b != 0 && layout_b != 1) || tri < 0 || tri > 3)
+        return fail(PTQ_EINVAL, "ptq_test_gemm_f32_split3: bad arguments");
+    const size_t need = ptq_test_gemm_f32_split3_workspace_bytes(M, N, K);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(PTQ_EWORKSPACE, "ptq_test_gemm_f32_split3: workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    Arena ar(workspace, workspace_bytes);
+    uint16_t* pa = ar.take<uint16_t>(gemm_f32_split3_elems(M, K));
+    uint16_t* pb = ar.take<uint16_t>(gemm_f32_split3_elems(N, K));
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.layout_a = layout_a;
+    g.B = B; g.ldb = ldb; g.layout_b = layout_b;
+    g.C = C; g.ldc = ldc;
+    g.alpha = alpha; g.beta_one = beta_one; g.tri = tri; g.upper_only = upper_only;
+    return launch_gemm_f32_split3(g, pa, pb, (hipStream_t)stream);
+}
+
 size_t awq_workspace_bytes(int64_t out, int64_t in, int64_t rows, int n_alpha) {
     if (out < 1 || in < 1 || rows < 1 || n_alpha < 1) return 0;
     return awq_ws_bytes(out, in, rows, n_alpha);

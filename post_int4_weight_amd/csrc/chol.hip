@@ -16,7 +16,8 @@
 //                              (R11, U11) from H11 (recursively),
 //                              U12 = -U11 R12 U22,
 //
-// so 2n^3/3 flops run as large fp32 MFMA GEMMs (gemm_f32.hip) and only
+// so 2n^3/3 flops run as large GEMMs (the big ones on the bf16 MFMA from
+// three-term bf16 splits, at fp32 accuracy; the rest on the fp32 MFMA) and only
 // BASE x BASE (128 x 128) diagonal blocks are factored and inverted inside one workgroup's
 // LDS. A non-positive (or NaN) pivot raises a device flag read once at the end.
 #include "common.hpp"
@@ -194,25 +195,33 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
         }
 }
 
+// GEMMs with all of M, N, K at least this large run on the bf16 MFMA from
+// three-term splits of their operands (fp32 accuracy, gemm_bf16.hip); the
+// smaller ones, deep in the recursion, on the fp32 MFMA GEMM.
+constexpr int64_t SPLIT3_MIN = 2048;
+
 struct Ctx {
     float* A;      // damped (permuted) H, destroyed
     float* U;      // output
     float* T;      // scratch, >= (n/2)^2 + slack
+    uint16_t* Pa;  // split planes of the GEMM operands (NULL: fp32 GEMMs only)
+    uint16_t* Pb;
     int64_t n;
     int* flag;
     hipStream_t st;
 };
 
-int gemm(Ctx& c, int64_t M, int64_t N, int64_t K, const float* A, int la, const float* B, int lb,
+int gemm(Ctx& c, int64_t M, int64_t N, int64_t K, const float* A, int la, int64_t lda, const float* B, int lb,
          int64_t ldb, float* C, int64_t ldc, float alpha, int beta_one, int tri, int upper_only) {
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
-    g.A = A; g.lda = c.n; g.layout_a = la;
+    g.A = A; g.lda = lda; g.layout_a = la;
     g.B = B; g.ldb = ldb; g.layout_b = lb;
     g.C = C; g.ldc = ldc;
     g.alpha = alpha; g.beta_one = beta_one; g.tri = tri; g.upper_only = upper_only;
     prof_begin(PROF_FACTOR_GEMM, c.st);
-    const int s = launch_gemm_f32(g, c.st);
+    const bool split = c.Pa && M >= SPLIT3_MIN && N >= SPLIT3_MIN && K >= SPLIT3_MIN;
+    const int s = split ? launch_gemm_f32_split3(g, c.Pa, c.Pb, c.st) : launch_gemm_f32(g, c.st);
     prof_end(PROF_FACTOR_GEMM, c.st);
     return s;
 }
@@ -238,38 +247,35 @@ int recurse(Ctx& c, int64_t o, int64_t m) {
     float* U22 = c.U + (o + n1) * n + (o + n1);
     PTQ_TRY(recurse(c, o + n1, n2));
     // R12 = H12 U22^T  (U22 stored [N][K], upper: entries with k < j are zero)
-    PTQ_TRY(gemm(c, n1, n2, n2, A12, A_MK, U22, B_NK, n, U12, n, 1.f, 0, TRI_B_UPPER_NK, 0));
+    PTQ_TRY(gemm(c, n1, n2, n2, A12, A_MK, n, U22, B_NK, n, U12, n, 1.f, 0, TRI_B_UPPER_NK, 0));
     // H11 -= R12 R12^T (upper tiles only)
-    PTQ_TRY(gemm(c, n1, n1, n2, U12, A_MK, U12, B_NK, n, A11, n, -1.f, 1, TRI_NONE, 1));
+    PTQ_TRY(gemm(c, n1, n1, n2, U12, A_MK, n, U12, B_NK, n, A11, n, -1.f, 1, TRI_NONE, 1));
     PTQ_TRY(recurse(c, o, n1));
     // T = R12 U22 (U22 upper: B[k][j] = 0 for k > j), T is [n1, n2] with row stride n2
-    PTQ_TRY(gemm(c, n1, n2, n2, U12, A_MK, U22, B_KN, n, c.T, n2, 1.f, 0, TRI_B_UPPER_KN, 0));
+    PTQ_TRY(gemm(c, n1, n2, n2, U12, A_MK, n, U22, B_KN, n, c.T, n2, 1.f, 0, TRI_B_UPPER_KN, 0));
     // U12 = -U11 T (U11 upper: A[i][k] = 0 for k < i)
-    {
-        GemmArgs g{};
-        g.M = n1; g.N = n2; g.K = n1;
-        g.A = U11; g.lda = n; g.layout_a = A_MK;
-        g.B = c.T; g.ldb = n2; g.layout_b = B_KN;
-        g.C = U12; g.ldc = n;
-        g.alpha = -1.f; g.beta_one = 0; g.tri = TRI_A_UPPER; g.upper_only = 0;
-        prof_begin(PROF_FACTOR_GEMM, c.st);
-        const int s = launch_gemm_f32(g, c.st);
-        prof_end(PROF_FACTOR_GEMM, c.st);
-        PTQ_TRY(s);
-    }
+    PTQ_TRY(gemm(c, n1, n2, n1, U11, A_MK, n, c.T, B_KN, n2, U12, n, -1.f, 0, TRI_A_UPPER, 0));
     return PTQ_OK;
 }
 
 }  // namespace
 
+// Largest GEMM operand of the recursion: rows and depth at most the top
+// split's trailing size.
+int64_t split_half(int64_t n) { return cdiv(n / 2, BASE) * BASE; }
+
 size_t factor_workspace_bytes(int64_t n) {
     Sizer z;
     z.take<float>((size_t)n * n);                          // A
-    const int64_t half = cdiv(n / 2, BASE) * BASE;
+    const int64_t half = split_half(n);
     z.take<float>((size_t)half * half + 1024);             // T
     z.take<double>(1);                                     // lambda
     z.take<int>(1);                                        // flag
     z.take<int32_t>((size_t)n);                            // perm (when the caller passes none)
+    if (half >= SPLIT3_MIN) {                              // split planes of both operands
+        z.take<uint16_t>(gemm_f32_split3_elems(half, half));
+        z.take<uint16_t>(gemm_f32_split3_elems(half, half));
+    }
     return z.bytes();
 }
 
@@ -280,12 +286,15 @@ int run_inverse_factor(const float* H, const double* d, int64_t n, double damp, 
     c.n = n;
     c.st = st;
     c.A = ar.take<float>((size_t)n * n);
-    const int64_t half = cdiv(n / 2, BASE) * BASE;
+    const int64_t half = split_half(n);
     c.T = ar.take<float>((size_t)half * half + 1024);
     double* lam = ar.take<double>(1);
     c.flag = ar.take<int>(1);
     int32_t* ptmp = ar.take<int32_t>((size_t)n);
-    if (!c.A || !c.T || !lam || !c.flag || !ptmp) {
+    const bool split = half >= SPLIT3_MIN;
+    c.Pa = split ? ar.take<uint16_t>(gemm_f32_split3_elems(half, half)) : nullptr;
+    c.Pb = split ? ar.take<uint16_t>(gemm_f32_split3_elems(half, half)) : nullptr;
+    if (!c.A || !c.T || !lam || !c.flag || !ptmp || (split && (!c.Pa || !c.Pb))) {
         set_error("gptq_inverse_factor: workspace of %zu bytes, %zu needed", ws_bytes, factor_workspace_bytes(n));
         return PTQ_EWORKSPACE;
     }

@@ -109,7 +109,8 @@ enum ProfKernel {
     PROF_TRAIL_GEMM = 4,    // GPTQ trailing fp32 MFMA update
     PROF_AWQ_GEMM = 5,      // AWQ error GEMM
     PROF_INNER_GEMM = 6,    // GPTQ update inside a super-block
-    PROF_NKERNELS = 7
+    PROF_SPLIT3_GEMM = 7,   // fp32 GEMM as bf16 MFMAs on three-term splits (main loop only)
+    PROF_NKERNELS = 8
 };
 void prof_begin(int kernel, hipStream_t st);
 void prof_end(int kernel, hipStream_t st);
@@ -144,6 +145,11 @@ struct GemmArgs {
     int upper_only;   // only output tiles with tile_row <= tile_col (SYRK-style)
 };
 int launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+// The same GEMM on the bf16 MFMA from three-term bf16 splits of both
+// operands (gemm_bf16.hip): pa and pb hold gemm_f32_split3_elems(M, K) and
+// (N, K) bf16 elements of scratch (pb is unused when B is A's transpose view).
+size_t gemm_f32_split3_elems(int64_t rows, int64_t K);
+int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStream_t st);
 
 // Stage 2 helpers (chol.hip)
 size_t factor_workspace_bytes(int64_t n);

@@ -38,7 +38,7 @@ constexpr int CPR = ROWB / 16;      // 16-byte chunks per staged row
 constexpr int NTH = 256;
 constexpr int NXCD = 8;
 
-enum { EPI_HESSIAN = 0, EPI_SUMSQ = 1 };
+enum { EPI_HESSIAN = 0, EPI_SUMSQ = 1, EPI_GEMM = 2 };
 
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + 16 * (c ^ ((r >> 1) & 7)); }
 
@@ -86,6 +86,15 @@ struct Bf16GemmArgs {
     // EPI_SUMSQ
     double* partial;           // [gridDim.y][tiles]
     int64_t tiles_n, ntiles;
+    // EPI_GEMM (fp32 GEMM from three-term bf16 splits): A and B are three
+    // planes each (hi, mid, lo; plane strides a_plane, b_plane elements), K1
+    // the padded depth; C = alpha * sum of the six significant plane products
+    // (+ C when beta_one), with GemmArgs' tri / upper_only meaning.
+    const uint16_t* Ap; const uint16_t* Bp;
+    int64_t a_plane, b_plane;
+    float* C; int64_t ldc;
+    float alpha; int beta_one; int tri; int upper_only;
+    int64_t tiles_m;
 };
 
 template <int BMX>
@@ -276,6 +285,25 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[
                     }
                 }
             }
+    } else if (EPI == EPI_GEMM) {
+        const int mi = (int)std::min<int64_t>(BMX, g.M - i0);
+        const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
+        float* Ct = g.C + i0 * g.ldc + j0;
+#pragma unroll
+        for (int a = 0; a < WT; ++a)
+#pragma unroll
+            for (int b = 0; b < WT; ++b) {
+                const int jj = wn + 32 * b + li;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ii = wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (ii < mi && jj < nj) {
+                        float* p = Ct + (int64_t)ii * g.ldc + jj;
+                        const float v = g.alpha * acc[a][b][r];
+                        *p = g.beta_one ? *p + v : v;
+                    }
+                }
+            }
     } else {
         const int mi = (int)std::min<int64_t>(BMX, g.M - i0);
         const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
@@ -360,6 +388,24 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
         i0 = (int64_t)ti * BMX;
         j0 = (int64_t)tj * BMX;
         diag = (ti == tj);
+    } else if (EPI == EPI_GEMM) {
+        // With at least 8 tile rows, XCD x takes the whole rows x, x + 8, ...
+        // (its tiles share A panels in its L2, and the rows' alternation
+        // balances triangular work over the XCDs); else plain row-major.
+        int64_t tm, tn;
+        if (g.tiles_m >= NXCD) {
+            const int64_t x = blockIdx.x % NXCD, i = blockIdx.x / NXCD;
+            tm = x + NXCD * (i / g.tiles_n);
+            tn = i % g.tiles_n;
+            if (tm >= g.tiles_m) return;
+        } else {
+            if ((int64_t)blockIdx.x >= g.tiles_m * g.tiles_n) return;
+            tm = blockIdx.x / g.tiles_n;
+            tn = blockIdx.x % g.tiles_n;
+        }
+        if (g.upper_only && tm > tn) return;
+        i0 = tm * BMX;
+        j0 = tn * BMX;
     } else {
         // row-major tiles, a contiguous run per XCD
         const int64_t per = (nwork + NXCD - 1) / NXCD;
@@ -389,16 +435,43 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
         offA[q] = ra * g.lda + 8 * c;
         offB[q] = rb * g.ldb + 8 * c;
     }
-    const int64_t n1 = g.K1 / DKT, n2 = g.K2 / DKT;
-    const int64_t nst = n1 + n2;
+    int64_t n1 = g.K1 / DKT, nst = n1 + g.K2 / DKT;
+    int64_t kb = 0;
+    if (EPI == EPI_GEMM) {
+        // depth range of the tile (triangular operands skip their zero
+        // blocks); stage s covers depth kb + (s / 6) * DKT in plane pair s % 6
+        int64_t ke = g.K1;
+        if (g.tri == TRI_A_UPPER) kb = i0;
+        else if (g.tri == TRI_B_UPPER_NK) kb = j0;
+        else if (g.tri == TRI_B_UPPER_KN) ke = std::min<int64_t>(g.K1, j0 + BMX);
+        nst = (ke > kb) ? 6 * ((ke - kb) / DKT) : 0;
+    }
+    // operand bases of stage s
+    auto stage_a = [&](int64_t s) -> const uint16_t* {
+        if constexpr (EPI == EPI_GEMM) {
+            // plane pairs (A, B): hi.hi, hi.mid, mid.hi, hi.lo, lo.hi, mid.mid
+            const int64_t kc = s / 6;
+            const int pq = (int)(s - 6 * kc);
+            return g.Ap + ((0x120100 >> (4 * pq)) & 15) * g.a_plane + kb + kc * DKT;
+        } else {
+            return s < n1 ? g.A1 + s * DKT : g.A2 + (s - n1) * DKT;
+        }
+    };
+    auto stage_b = [&](int64_t s) -> const uint16_t* {
+        if constexpr (EPI == EPI_GEMM) {
+            const int64_t kc = s / 6;
+            const int pq = (int)(s - 6 * kc);
+            return g.Bp + ((0x102010 >> (4 * pq)) & 15) * g.b_plane + kb + kc * DKT;
+        } else {
+            return s < n1 ? B1 + s * DKT : B2 + (s - n1) * DKT;
+        }
+    };
 
     // one 16-byte-per-lane copy: q < PER moves A's granules, else B's
     auto load_one = [&](int64_t s, int buf, int q) {
-        const bool seg1 = s < n1;
         const bool isa = q < PER;
         const int qq = isa ? q : q - PER;
-        const uint16_t* P = isa ? ((seg1 ? g.A1 : g.A2) + (seg1 ? s : s - n1) * DKT + offA[qq])
-                                : ((seg1 ? B1 : B2) + (seg1 ? s : s - n1) * DKT + offB[qq]);
+        const uint16_t* P = isa ? stage_a(s) + offA[qq] : stage_b(s) + offB[qq];
         unsigned char* dst = smem + buf * (2 * PANEL) + (isa ? 0 : PANEL) + (wave * PER + qq) * 1024;
         __builtin_amdgcn_global_load_lds((const void*)P, (lds_ptr_t)dst, 16, 0, 0);
     };
@@ -554,6 +627,135 @@ int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t
     PTQ_LAUNCH_CHECK();
     return PTQ_OK;
 }
+
+// ---------------------------------------------------------------------------
+// fp32 GEMM on the bf16 MFMA. Each fp32 operand x is split into three bf16
+// terms, hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid) (both
+// differences are exact in fp32), so x = hi + mid + lo to about 2^-24
+// relative: 24 significant bits, fp32's own. A product keeps the six term
+// products down to 2^-16 (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi, mid.mid) and
+// drops those of order 2^-24 and below; each term product is exact and all
+// six accumulate in the same fp32 MFMA accumulators, so the result carries
+// fp32 GEMM accuracy at six bf16 MFMAs (16 x the fp32 MFMA's rate each) per
+// 32 x 32 x 16 block.
+__device__ __forceinline__ void split3(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+    if (!(fabsf(x) <= 3.3e38f)) {   // NaN / Inf (or a value bf16 rounding would overflow): keep hi only
+        h = (uint16_t)(__float_as_uint(x) >> 16) | (uint16_t)((x != x) ? 0x40 : 0);
+        m = l = 0;
+        return;
+    }
+    h = float_to_bf16_bits(x);
+    const float r1 = x - bf16_bits_to_float(h);
+    m = float_to_bf16_bits(r1);
+    l = float_to_bf16_bits(r1 - bf16_bits_to_float(m));
+}
+
+__device__ __forceinline__ void split3_store8(const float (&v)[8], uint16_t* p, int64_t plane) {
+    uint16_t h[8], m[8], l[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) split3(v[q], h[q], m[q], l[q]);
+    auto pack = [](const uint16_t (&u)[8]) {
+        return make_uint4((uint32_t)u[0] | ((uint32_t)u[1] << 16), (uint32_t)u[2] | ((uint32_t)u[3] << 16),
+                          (uint32_t)u[4] | ((uint32_t)u[5] << 16), (uint32_t)u[6] | ((uint32_t)u[7] << 16));
+    };
+    *(uint4*)p = pack(h);
+    *(uint4*)(p + plane) = pack(m);
+    *(uint4*)(p + 2 * plane) = pack(l);
+}
+
+// P[t][r][k] (t = hi, mid, lo; row stride ldp, plane stride plane) from
+// S[r][k] = X[r * ldx + k] for k < K, zero for K <= k < kp (kp % 8 == 0).
+__global__ __launch_bounds__(256) void split3_rows_kernel(const float* __restrict__ X, int64_t ldx, int64_t R,
+                                                          int64_t K, int vec, uint16_t* __restrict__ P, int64_t ldp,
+                                                          int64_t kp, int64_t plane) {
+    const int64_t nch = kp / 8;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < R * nch; e += (int64_t)gridDim.x * 256) {
+        const int64_t r = e / nch, k0 = 8 * (e % nch);
+        const float* x = X + r * ldx + k0;
+        float v[8];
+        if (vec && k0 + 8 <= K) {
+            const float4 a = *(const float4*)x, b = *(const float4*)(x + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = (k0 + q < K) ? x[q] : 0.f;
+        }
+        split3_store8(v, P + r * ldp + k0, plane);
+    }
+}
+
+// The same from S[r][k] = X[k * ldx + r] (X stored [K][R]), through a 64 x 64
+// LDS tile; grid (cdiv(R, 64), kp / 64), kp % 64 == 0.
+__global__ __launch_bounds__(256) void split3_cols_kernel(const float* __restrict__ X, int64_t ldx, int64_t R,
+                                                          int64_t K, uint16_t* __restrict__ P, int64_t ldp,
+                                                          int64_t plane) {
+    __shared__ float tile[64][65];
+    const int64_t r0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int kk = i >> 6, rr = i & 63;
+        tile[kk][rr] = (k0 + kk < K && r0 + rr < R) ? X[(k0 + kk) * ldx + r0 + rr] : 0.f;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+        const int rr = i >> 3, c = i & 7;
+        if (r0 + rr >= R) continue;
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = tile[8 * c + q][rr];
+        split3_store8(v, P + (r0 + rr) * ldp + k0 + 8 * c, plane);
+    }
+}
+
+int64_t split3_ld(int64_t K) { return cdiv(K, 64) * 64 + 64; }
+
+// planes of op(X) [R, K] (trans: X stored [K][R])
+int launch_split3(const float* X, int64_t ldx, bool trans, int64_t R, int64_t K, uint16_t* P, hipStream_t st) {
+    const int64_t kp = cdiv(K, 64) * 64, ldp = split3_ld(K), plane = R * ldp;
+    if (trans) {
+        hipLaunchKernelGGL(split3_cols_kernel, dim3((unsigned)cdiv(R, 64), (unsigned)(kp / 64)), dim3(256), 0, st, X,
+                           ldx, R, K, P, ldp, plane);
+    } else {
+        const int vec = (((uintptr_t)X & 15u) == 0) && (ldx % 4 == 0);
+        const int64_t items = R * (kp / 8);
+        hipLaunchKernelGGL(split3_rows_kernel, dim3((unsigned)std::min<int64_t>(cdiv(items, 256), 16384)), dim3(256),
+                           0, st, X, ldx, R, K, vec, P, ldp, kp, plane);
+    }
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
+}  // namespace
+
+size_t gemm_f32_split3_elems(int64_t rows, int64_t K) { return (size_t)(3 * rows * split3_ld(K)); }
+
+int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStream_t st) {
+    if (a.M <= 0 || a.N <= 0) return PTQ_OK;
+    if (a.K <= 0) return launch_gemm_f32(a, st);
+    const int64_t kp = cdiv(a.K, 64) * 64, ldp = split3_ld(a.K);
+    const bool same = a.A == a.B && a.lda == a.ldb && a.M == a.N &&
+                      ((a.layout_a == A_MK && a.layout_b == B_NK) || (a.layout_a == A_KM && a.layout_b == B_KN));
+    PTQ_TRY(launch_split3(a.A, a.lda, a.layout_a == A_KM, a.M, a.K, pa, st));
+    if (!same) PTQ_TRY(launch_split3(a.B, a.ldb, a.layout_b == B_KN, a.N, a.K, pb, st));
+    Bf16GemmArgs g{};
+    g.Ap = pa; g.Bp = same ? pa : pb;
+    g.a_plane = a.M * ldp; g.b_plane = a.N * ldp;
+    g.lda = ldp; g.ldb = ldp;
+    g.K1 = kp; g.K2 = 0;
+    g.M = a.M; g.N = a.N;
+    g.C = a.C; g.ldc = a.ldc;
+    g.alpha = a.alpha; g.beta_one = a.beta_one; g.tri = a.tri; g.upper_only = a.upper_only;
+    g.tiles_m = cdiv(a.M, 256); g.tiles_n = cdiv(a.N, 256);
+    const unsigned grid = (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n
+                                                       : g.tiles_m * g.tiles_n);
+    prof_begin(PROF_SPLIT3_GEMM, st);
+    const int rc = launch_direct<256, EPI_GEMM, 64>(g, 0, grid, 1, st);
+    prof_end(PROF_SPLIT3_GEMM, st);
+    PTQ_TRY(rc);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
+namespace {
 
 // Xt[c][r] = X[r0 + r][c] for r < nr; entries nr <= r < kt of each Xt row are
 // zeroed (the row stride ldt may be larger; that tail is never read).
