@@ -169,13 +169,15 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
 #pragma unroll
                 for (int q = 0; q < 4; ++q) s[dj][q] = Uj[q];
             }
+            if (i0 < j) {   // rows >= j are final (Ri = 0): whole waves skip the update as j falls
 #pragma unroll
-            for (int di = 0; di < 4; ++di)
+                for (int di = 0; di < 4; ++di)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    a[di][q] -= Ri[di] * Rk[q];
-                    s[di][q] -= Ri[di] * Uj[q];
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        a[di][q] -= Ri[di] * Rk[q];
+                        s[di][q] -= Ri[di] * Uj[q];
+                    }
+            }
             if (j > 0) {   // publish column j-1 of A and row j-1 of S (final after this update)
                 const int djn = (dj + 3) & 3;
                 const int jn = j - 1, jbn = jn >> 2;
