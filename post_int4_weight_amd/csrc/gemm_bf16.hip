@@ -149,8 +149,17 @@ __device__ __forceinline__ void store_panel(unsigned char* S, const uint4 (&v)[B
     }
 }
 
-template <int BMX, int EPI>
-__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[BMX / 64][BMX / 64], int64_t i0,
+// Wave layout of a BMX x BMX tile over NW waves: NW / 2 rows x 2 columns of
+// waves, each a (WA x 32) x (WB x 32) block of 32x32 MFMA accumulators.
+template <int BMX, int NW>
+struct WaveTile {
+    static constexpr int TM = BMX / (NW / 2), TN = BMX / 2;
+    static constexpr int WA = TM / 32, WB = TN / 32;
+};
+
+template <int BMX, int EPI, int NW = 4>
+__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g,
+                                           f32x16 (&acc)[WaveTile<BMX, NW>::WA][WaveTile<BMX, NW>::WB], int64_t i0,
                                            int64_t j0, bool diag, int64_t L, unsigned char* smem);
 
 // Register-staged variant: any shape (bounds-checked loads, zero fill).
@@ -255,13 +264,15 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
 
 // Tile epilogue. 32x32 accumulator layout: lane l, register r -> row
 // 8*(r/4) + 4*(l/32) + r%4, column l%32. `smem` is free scratch by now.
-template <int BMX, int EPI>
-__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[BMX / 64][BMX / 64], int64_t i0,
+template <int BMX, int EPI, int NW>
+__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g,
+                                           f32x16 (&acc)[WaveTile<BMX, NW>::WA][WaveTile<BMX, NW>::WB], int64_t i0,
                                            int64_t j0, bool diag, int64_t L, unsigned char* smem) {
-    constexpr int WT = BMX / 64;
+    using WTL = WaveTile<BMX, NW>;
+    constexpr int WA = WTL::WA, WB = WTL::WB;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * (BMX / 2), wn = (wave & 1) * (BMX / 2);
+    const int wm = (wave >> 1) * WTL::TM, wn = (wave & 1) * WTL::TN;
     const int li = lane & 31, lh = lane >> 5;
     if (EPI == EPI_HESSIAN) {
         const int mi = (int)std::min<int64_t>(BMX, g.M - i0);   // valid rows / columns of this tile
@@ -270,9 +281,9 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[
         float* Hm = g.H + j0 * g.ldh + i0;                      // mirror origin
         const int ld = (int)g.ldh;
 #pragma unroll
-        for (int a = 0; a < WT; ++a)
+        for (int a = 0; a < WA; ++a)
 #pragma unroll
-            for (int b = 0; b < WT; ++b) {
+            for (int b = 0; b < WB; ++b) {
                 const int jj = wn + 32 * b + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -290,9 +301,9 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[
         const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
         float* Ct = g.C + i0 * g.ldc + j0;
 #pragma unroll
-        for (int a = 0; a < WT; ++a)
+        for (int a = 0; a < WA; ++a)
 #pragma unroll
-            for (int b = 0; b < WT; ++b) {
+            for (int b = 0; b < WB; ++b) {
                 const int jj = wn + 32 * b + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -309,9 +320,9 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[
         const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
         double s = 0.0;
 #pragma unroll
-        for (int a = 0; a < WT; ++a)
+        for (int a = 0; a < WA; ++a)
 #pragma unroll
-            for (int b = 0; b < WT; ++b) {
+            for (int b = 0; b < WB; ++b) {
                 float part = 0.f;
                 const int jj = wn + 32 * b + li;
 #pragma unroll
@@ -328,8 +339,12 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g, f32x16 (&acc)[
         double* red = (double*)smem;
         if (lane == 0) red[wave] = s;
         __syncthreads();
-        if (t == 0)
-            g.partial[(int64_t)blockIdx.y * g.ntiles + L] = ((red[0] + red[1]) + (red[2] + red[3]));
+        if (t == 0) {
+            double tot = 0.0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) tot += red[w];
+            g.partial[(int64_t)blockIdx.y * g.ntiles + L] = tot;
+        }
     }
 }
 
@@ -372,14 +387,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8));
 }
 
-template <int BMX, int EPI, int DKT, int NST>
-__global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g, int64_t nwork) {
+template <int BMX, int EPI, int DKT, int NST, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g, int64_t nwork) {
     using S = DStage<DKT>;
+    using WTL = WaveTile<BMX, NW>;
     constexpr int ROWB = S::ROWB, KSUB = S::KSUB;
-    constexpr int WT = BMX / 64;
-    constexpr int PER = BMX * S::CH / (64 * 4);   // load instructions per wave per panel per stage
-    constexpr int PANEL = BMX * ROWB;              // bytes of one operand panel per stage
-    static_assert(NST >= 2 && KSUB % 2 == 0 && PER % WT == 0, "pipeline shape");
+    constexpr int WA = WTL::WA, WB = WTL::WB;          // accumulator blocks per wave (rows, columns)
+    constexpr int NM = WA * WB, NR = WA + WB;          // MFMAs and fragment reads per k-step
+    constexpr int PER = BMX * S::CH / (64 * NW);       // load instructions per wave per panel per stage
+    constexpr int PANEL = BMX * ROWB;                  // bytes of one operand panel per stage
+    static_assert(NST >= 2 && KSUB % 2 == 0 && NM >= NR && PER >= 1, "pipeline shape");
     int64_t i0, j0, L = 0;
     bool diag = false;
     if (EPI == EPI_HESSIAN) {
@@ -420,7 +437,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * (BMX / 2), wn = (wave & 1) * (BMX / 2);
+    const int wm = (wave >> 1) * WTL::TM, wn = (wave & 1) * WTL::TN;
     const int li = lane & 31, lh = lane >> 5;
 
     // element offsets (from the operand base) of the chunks this lane moves
@@ -480,11 +497,11 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
         for (int q = 0; q < 2 * PER; ++q) load_one(s, buf, q);
     };
 
-    f32x16 acc[WT][WT];
+    f32x16 acc[WA][WB];
 #pragma unroll
-    for (int a = 0; a < WT; ++a)
+    for (int a = 0; a < WA; ++a)
 #pragma unroll
-        for (int b = 0; b < WT; ++b)
+        for (int b = 0; b < WB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
@@ -499,7 +516,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
     // stage is visible to all waves and this stage's buffer is free, and the
     // copies of stage s + NST go into it.
     const int fsw = S::sw(li);   // fragment swizzle term, lane-only (row = wm + 32 a + li)
-    bf16x8 fa[2][WT], fb[2][WT];
+    bf16x8 fa[2][WA], fb[2][WB];
     // k-step kk reads chunk 2 kk + lh of its rows
     auto fragp = [&](int64_t s, int kk) { return smem + (s % NST) * (2 * PANEL) + 16 * ((2 * kk + lh) ^ fsw); };
     // fragment q of a k-step, in the order the MFMAs (a-major) consume them:
@@ -507,31 +524,31 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
     auto read_one = [&](int64_t s, int kk, int slot, int q) {
         const unsigned char* As = fragp(s, kk);
         if (q == 0) fa[slot][0] = *(const bf16x8*)(As + (wm + li) * ROWB);
-        else if (q <= WT) fb[slot][q - 1] = *(const bf16x8*)(As + PANEL + (wn + 32 * (q - 1) + li) * ROWB);
-        else fa[slot][q - WT] = *(const bf16x8*)(As + (wm + 32 * (q - WT) + li) * ROWB);
+        else if (q <= WB) fb[slot][q - 1] = *(const bf16x8*)(As + PANEL + (wn + 32 * (q - 1) + li) * ROWB);
+        else fa[slot][q - WB] = *(const bf16x8*)(As + (wm + 32 * (q - WB) + li) * ROWB);
     };
     auto frags = [&](int64_t s, int kk, int slot) {
 #pragma unroll
-        for (int q = 0; q < 2 * WT; ++q) read_one(s, kk, slot, q);
+        for (int q = 0; q < NR; ++q) read_one(s, kk, slot, q);
     };
     auto mfma_one = [&](int slot, int idx) {
-        const int a = idx / WT, b = idx % WT;
+        const int a = idx / WB, b = idx % WB;
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][a], fb[slot][b], acc[a][b], 0, 0, 0);
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
-        for (int i = 0; i < WT * WT; ++i) mfma_one(slot, i);
+        for (int i = 0; i < NM; ++i) mfma_one(slot, i);
     };
-    // The reads of the next k-step ride under the first 2 WT MFMAs of the
+    // The NR reads of the next k-step ride under the first NR MFMAs of the
     // current one, one per MFMA, so the last of them has the remaining
-    // WT^2 - 2 WT MFMAs' time to return before the next k-step needs it.
+    // NM - NR MFMAs' time to return before the next k-step needs it.
     auto interleave = [&]() {
 #pragma unroll
-        for (int i = 0; i < 2 * WT; ++i) {
+        for (int i = 0; i < NR; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        if constexpr (WT * WT > 2 * WT) __builtin_amdgcn_sched_group_barrier(0x008, WT * WT - 2 * WT, 0);
+        if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
     };
 
     // Past the last stage the issue repeats the last stage into the free
@@ -559,16 +576,16 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
             {
                 // After the barrier: the last k-step's MFMAs, the next
                 // stage's first fragment reads (one after each of the first
-                // 2 WT MFMAs) and the 2 PER copies of stage s + NST spread
+                // NR MFMAs) and the 2 PER copies of stage s + NST spread
                 // evenly over the MFMAs, pinned in that order: a copy that
                 // waits for the address unit stalls at most one MFMA's issue.
                 const int64_t sl = std::min<int64_t>(s + NST, nst - 1);
                 const int bl = (int)(s % NST);
-                constexpr int NL = 2 * PER, NM = WT * WT;
+                constexpr int NL = 2 * PER;
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
                     mfma_one(1, m);
-                    if (m < 2 * WT) read_one(s + 1, 0, 0, m);
+                    if (m < NR) read_one(s + 1, 0, 0, m);
 #pragma unroll
                     for (int l = m * NL / NM; l < (m + 1) * NL / NM; ++l) load_one(sl, bl, l);
                     __builtin_amdgcn_sched_barrier(0);
@@ -580,16 +597,16 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArg
     }
     wait_vmcnt<0, true>();
     __syncthreads();
-    store_tile<BMX, EPI>(g, acc, i0, j0, diag, L, smem);
+    store_tile<BMX, EPI, NW>(g, acc, i0, j0, diag, L, smem);
 }
 
 // Opt a kernel into more than 64 KB of dynamic LDS (once per instantiation).
-template <int BMX, int EPI, int DKT>
+template <int BMX, int EPI, int DKT, int NW = 4>
 int prepare_kernel() {
     static bool done = false;
     if (!done) {
         if constexpr (DKT > 0)
-            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, DNST<DKT>>,
+            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, DNST<DKT>, NW>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         dsmem_bytes<BMX, DKT, DNST<DKT>>()));
         else
@@ -600,15 +617,20 @@ int prepare_kernel() {
     return PTQ_OK;
 }
 
-template <int BMX, int EPI, int DKT>
+template <int BMX, int EPI, int DKT, int NW = 4>
 int launch_direct(const Bf16GemmArgs& g, int64_t nwork, unsigned grid, unsigned grid_y, hipStream_t st) {
     constexpr int nst = DNST<DKT>;
     constexpr int lds = dsmem_bytes<BMX, DKT, nst>();
-    PTQ_TRY((prepare_kernel<BMX, EPI, DKT>()));
-    hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, nst>), dim3(grid, grid_y), dim3(NTH), lds, st, g,
-                       nwork);
+    PTQ_TRY((prepare_kernel<BMX, EPI, DKT, NW>()));
+    hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, nst, NW>), dim3(grid, grid_y), dim3(64 * NW), lds,
+                       st, g, nwork);
     return PTQ_OK;
 }
+
+// waves per workgroup of the direct kernel at 64-deep stages and 256-wide tiles:
+// eight (two per SIMD, 64 x 128 accumulators each) let one wave issue MFMAs
+// while the other waits on a fragment read, a copy or the barrier
+constexpr int DNW = 8;
 
 // Launch the direct variant when both K segments are multiples of its stage
 // depth (64, else 32), the register-staged one otherwise.
@@ -616,7 +638,7 @@ template <int BMX, int EPI>
 int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t st) {
     const unsigned grid = (unsigned)(EPI == EPI_HESSIAN ? 256 * hessian_rounds(g.T) : cdiv(nwork, NXCD) * NXCD);
     if (g.M > 0 && g.N > 0 && g.K1 % 64 == 0 && g.K2 % 64 == 0) {
-        PTQ_TRY((launch_direct<BMX, EPI, 64>(g, nwork, grid, grid_y, st)));
+        PTQ_TRY((launch_direct<BMX, EPI, 64, BMX == 256 ? DNW : 4>(g, nwork, grid, grid_y, st)));
     } else if (g.M > 0 && g.N > 0 && g.K1 % 32 == 0 && g.K2 % 32 == 0) {
         PTQ_TRY((launch_direct<BMX, EPI, 32>(g, nwork, grid, grid_y, st)));
     } else {
