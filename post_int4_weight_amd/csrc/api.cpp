@@ -417,6 +417,7 @@ int dequantize_int4(const uint32_t* packed, const float* scales, const int32_t* 
                     int64_t out, int64_t in, int group_size, int out_dtype, void* What, int64_t ldo, void* stream) {
     const char* fn = "dequantize_int4";
     if (out < 0 || in < 0) return fail(PTQ_EINVAL, "%s: negative size", fn);
+    if (in > ((int64_t)1 << 30)) return fail(PTQ_EINVAL, "%s: in = %lld too large", fn, (long long)in);
     if (in % 8) return fail(PTQ_EINVAL, "%s: in = %lld must be a multiple of 8", fn, (long long)in);
     if (group_size < 1) return fail(PTQ_EINVAL, "%s: group_size = %d < 1", fn, group_size);
     if (!dtype_ok(out_dtype)) return fail(PTQ_EINVAL, "%s: out_dtype = %d", fn, out_dtype);

@@ -61,42 +61,83 @@ __device__ __forceinline__ uint16_t from_float<uint16_t>(float v) { return float
 // What[r][c] = code(r, c) * scales[r][gi(c)], gi(c) = g_idx[c] (or c / g);
 // with zeros: unsigned nibbles, What = (code - zeros[r][gi(c)]) * scale.
 // A group index outside [0, ngroups) yields NaN for that column.
+// Grid: x over the words of a row, y over rows (a row's scales and zeros then
+// stay in cache for the whole block). With g % 8 == 0 and no g_idx the 8
+// columns of a word share one group: one scale (and zero) load per word.
 template <typename T>
-__global__ void dequant_int4_kernel(const uint32_t* __restrict__ packed, const float* __restrict__ scales,
-                                    const int32_t* __restrict__ g_idx, const int8_t* __restrict__ zeros,
-                                    int64_t out, int64_t in, int g,
-                                    int64_t ngroups, T* __restrict__ What, int64_t ldo) {
-    const int64_t wpr = in / 8;                       // words per row
-    const int64_t nwords = out * wpr;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nwords; w += stride) {
-        const int64_t r = w / wpr, c0 = 8 * (w % wpr);
-        const uint32_t word = packed[w];
+__global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ packed,
+                                                           const float* __restrict__ scales,
+                                                           const int32_t* __restrict__ g_idx,
+                                                           const int8_t* __restrict__ zeros, int64_t out, int in,
+                                                           int g, int ngroups, int gvec, T* __restrict__ What,
+                                                           int64_t ldo) {
+    const int wpr = in / 8;   // words per row
+    for (int64_t r = blockIdx.y; r < out; r += gridDim.y) {
+        const uint32_t* prow = packed + r * wpr;
         const float* srow = scales + r * ngroups;
-        T v[8];
+        const int8_t* zrow = zeros ? zeros + r * ngroups : nullptr;
+        T* orow = What + r * ldo;
+        // one packed word (8 columns)
+        auto word8 = [&](int w, uint32_t word) {
+            const int c0 = 8 * w;
+            int gi[8];
+            if (g_idx) {
+                if (gvec) {
+                    const int4 a = *(const int4*)(g_idx + c0), b = *(const int4*)(g_idx + c0 + 4);
+                    gi[0] = a.x; gi[1] = a.y; gi[2] = a.z; gi[3] = a.w;
+                    gi[4] = b.x; gi[5] = b.y; gi[6] = b.z; gi[7] = b.w;
+                } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int64_t gi = g_idx ? (int64_t)g_idx[c0 + k] : (c0 + k) / g;
-            const int nib = (int)((word >> (4 * k)) & 0xFu);
-            const bool ok = gi >= 0 && gi < ngroups;
-            const int64_t gs = ok ? gi : 0;
-            const float s = srow[gs];
-            const int code = zeros ? nib - (int)zeros[r * ngroups + gs] : nib - ((nib & 8) ? 16 : 0);
-            v[k] = from_float<T>(ok ? (float)code * s : __builtin_nanf(""));
-        }
-        T* dst = What + r * ldo + c0;
-        if constexpr (sizeof(T) == 4) {
-            *(float4*)dst = make_float4(*(float*)&v[0], *(float*)&v[1], *(float*)&v[2], *(float*)&v[3]);
-            *(float4*)(dst + 4) = make_float4(*(float*)&v[4], *(float*)&v[5], *(float*)&v[6], *(float*)&v[7]);
-        } else {
-            uint4 o;
-            const uint16_t* h = (const uint16_t*)v;
-            o.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-            o.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-            o.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
-            o.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
-            *(uint4*)dst = o;
-        }
+                    for (int k = 0; k < 8; ++k) gi[k] = g_idx[c0 + k];
+                }
+            } else if (g % 8 == 0) {
+                const int q = c0 / g;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) gi[k] = q;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) gi[k] = (c0 + k) / g;
+            }
+            T v[8];
+            bool one = true;   // all 8 columns in one valid group: one scale / zero load
+#pragma unroll
+            for (int k = 1; k < 8; ++k) one = one && gi[k] == gi[0];
+            one = one && gi[0] >= 0 && gi[0] < ngroups;
+            if (one) {
+                const float sc = srow[gi[0]];
+                const int z = zrow ? (int)zrow[gi[0]] : 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int nib = (int)((word >> (4 * k)) & 0xFu);
+                    const int code = zrow ? nib - z : nib - ((nib & 8) ? 16 : 0);
+                    v[k] = from_float<T>((float)code * sc);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int nib = (int)((word >> (4 * k)) & 0xFu);
+                    const bool ok = gi[k] >= 0 && gi[k] < ngroups;
+                    const int gs = ok ? gi[k] : 0;
+                    const float sc = srow[gs];
+                    const int code = zrow ? nib - (int)zrow[gs] : nib - ((nib & 8) ? 16 : 0);
+                    v[k] = from_float<T>(ok ? (float)code * sc : __builtin_nanf(""));
+                }
+            }
+            T* dst = orow + c0;
+            if constexpr (sizeof(T) == 4) {
+                *(float4*)dst = make_float4(*(float*)&v[0], *(float*)&v[1], *(float*)&v[2], *(float*)&v[3]);
+                *(float4*)(dst + 4) = make_float4(*(float*)&v[4], *(float*)&v[5], *(float*)&v[6], *(float*)&v[7]);
+            } else {
+                uint4 o;
+                const uint16_t* h = (const uint16_t*)v;
+                o.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                o.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                o.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
+                o.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
+                *(uint4*)dst = o;
+            }
+        };
+        for (int w = blockIdx.x * 256 + threadIdx.x; w < wpr; w += gridDim.x * 256) word8(w, prow[w]);
     }
 }
 
@@ -119,13 +160,16 @@ int launch_dequant_int4(const uint32_t* packed, const float* scales, const int32
                         int64_t out, int64_t in, int g, int out_dtype, void* What, int64_t ldo, hipStream_t st) {
     const int64_t nwords = out * (in / 8);
     if (nwords == 0) return PTQ_OK;
-    const int64_t ngroups = cdiv(in, g);
+    const int ngroups = (int)cdiv(in, g);
+    const int gvec = g_idx && (((uintptr_t)g_idx & 15u) == 0);
+    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(in / 8, 256), 64)),
+                    (unsigned)std::min<int64_t>(out, 65535));
     if (out_dtype == PTQ_F32)
-        hipLaunchKernelGGL(dequant_int4_kernel<float>, dim3(stream_grid(nwords)), dim3(256), 0, st, packed, scales,
-                           g_idx, zeros, out, in, g, ngroups, (float*)What, ldo);
+        hipLaunchKernelGGL(dequant_int4_kernel<float>, grid, dim3(256), 0, st, packed, scales, g_idx, zeros, out,
+                           (int)in, g, ngroups, gvec, (float*)What, ldo);
     else
-        hipLaunchKernelGGL(dequant_int4_kernel<uint16_t>, dim3(stream_grid(nwords)), dim3(256), 0, st, packed,
-                           scales, g_idx, zeros, out, in, g, ngroups, (uint16_t*)What, ldo);
+        hipLaunchKernelGGL(dequant_int4_kernel<uint16_t>, grid, dim3(256), 0, st, packed, scales, g_idx, zeros, out,
+                           (int)in, g, ngroups, gvec, (uint16_t*)What, ldo);
     PTQ_LAUNCH_CHECK();
     return PTQ_OK;
 }
