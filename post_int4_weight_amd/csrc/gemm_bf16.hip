@@ -149,18 +149,46 @@ __device__ __forceinline__ void store_panel(unsigned char* S, const uint4 (&v)[B
     }
 }
 
-// Wave layout of a BMX x BMX tile over NW waves: NW / 2 rows x 2 columns of
-// waves, each a (WA x 32) x (WB x 32) block of 32x32 MFMA accumulators.
-template <int BMX, int NW>
-struct WaveTile {
-    static constexpr int TM = BMX / (NW / 2), TN = BMX / 2;
-    static constexpr int WA = TM / 32, WB = TN / 32;
+// The two bf16 MFMA shapes. Operands: lane l supplies row l % MF of its
+// block and the 8 consecutive k at 8 * (l / MF) of the k-step (KDEP deep).
+// Accumulator register r of lane l holds row row(l, r), column col(l).
+template <int MF>
+struct MfmaShape;
+template <>
+struct MfmaShape<32> {   // v_mfma_f32_32x32x16_bf16
+    using acc_t = f32x16;
+    static constexpr int NACC = 16, KDEP = 16;
+    __device__ static __forceinline__ int row(int l, int r) { return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3); }
+    __device__ static __forceinline__ int col(int l) { return l & 31; }
+    __device__ static __forceinline__ acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct MfmaShape<16> {   // v_mfma_f32_16x16x32_bf16
+    using acc_t = f32x4;
+    static constexpr int NACC = 4, KDEP = 32;
+    __device__ static __forceinline__ int row(int l, int r) { return 4 * (l >> 4) + r; }
+    __device__ static __forceinline__ int col(int l) { return l & 15; }
+    __device__ static __forceinline__ acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
 };
 
-template <int BMX, int EPI, int NW = 4>
-__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g,
-                                           f32x16 (&acc)[WaveTile<BMX, NW>::WA][WaveTile<BMX, NW>::WB], int64_t i0,
-                                           int64_t j0, bool diag, int64_t L, unsigned char* smem);
+// Wave layout of a BMX x BMX tile over NW waves: NW / 2 rows x 2 columns of
+// waves, each a (WA x MF) x (WB x MF) block of MF x MF MFMA accumulators.
+template <int BMX, int NW, int MF = 32>
+struct WaveTile {
+    static constexpr int TM = BMX / (NW / 2), TN = BMX / 2;
+    static constexpr int WA = TM / MF, WB = TN / MF;
+    using acc_t = typename MfmaShape<MF>::acc_t;
+};
+
+template <int BMX, int EPI, int NW = 4, int MF = 32>
+__device__ __forceinline__ void store_tile(
+    const Bf16GemmArgs& g,
+    typename WaveTile<BMX, NW, MF>::acc_t (&acc)[WaveTile<BMX, NW, MF>::WA][WaveTile<BMX, NW, MF>::WB], int64_t i0,
+    int64_t j0, bool diag, int64_t L, unsigned char* smem);
 
 // Register-staged variant: any shape (bounds-checked loads, zero fill).
 template <int BMX, int EPI>
@@ -262,21 +290,21 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
     store_tile<BMX, EPI>(g, acc, i0, j0, diag, L, smem);
 }
 
-// Tile epilogue. 32x32 accumulator layout: lane l, register r -> row
-// 8*(r/4) + 4*(l/32) + r%4, column l%32. `smem` is free scratch by now.
-template <int BMX, int EPI, int NW>
-__device__ __forceinline__ void store_tile(const Bf16GemmArgs& g,
-                                           f32x16 (&acc)[WaveTile<BMX, NW>::WA][WaveTile<BMX, NW>::WB], int64_t i0,
-                                           int64_t j0, bool diag, int64_t L, unsigned char* smem) {
-    using WTL = WaveTile<BMX, NW>;
-    constexpr int WA = WTL::WA, WB = WTL::WB;
+// Tile epilogue (accumulator layout in MfmaShape). `smem` is free scratch by now.
+template <int BMX, int EPI, int NW, int MF>
+__device__ __forceinline__ void store_tile(
+    const Bf16GemmArgs& g,
+    typename WaveTile<BMX, NW, MF>::acc_t (&acc)[WaveTile<BMX, NW, MF>::WA][WaveTile<BMX, NW, MF>::WB], int64_t i0,
+    int64_t j0, bool diag, int64_t L, unsigned char* smem) {
+    using WTL = WaveTile<BMX, NW, MF>;
+    using Sh = MfmaShape<MF>;
+    constexpr int WA = WTL::WA, WB = WTL::WB, NACC = Sh::NACC;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = (wave >> 1) * WTL::TM, wn = (wave & 1) * WTL::TN;
-    const int li = lane & 31, lh = lane >> 5;
+    const int mi = (int)std::min<int64_t>(BMX, g.M - i0);   // valid rows / columns of this tile
+    const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
     if (EPI == EPI_HESSIAN) {
-        const int mi = (int)std::min<int64_t>(BMX, g.M - i0);   // valid rows / columns of this tile
-        const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
         float* Ht = g.H + i0 * g.ldh + j0;                      // tile origin
         float* Hm = g.H + j0 * g.ldh + i0;                      // mirror origin
         const int ld = (int)g.ldh;
@@ -284,10 +312,10 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g,
         for (int a = 0; a < WA; ++a)
 #pragma unroll
             for (int b = 0; b < WB; ++b) {
-                const int jj = wn + 32 * b + li;
+                const int jj = wn + MF * b + Sh::col(lane);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ii = wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                for (int r = 0; r < NACC; ++r) {
+                    const int ii = wm + MF * a + Sh::row(lane, r);
                     if (ii < mi && jj < nj) {
                         float* p = Ht + (int64_t)ii * ld + jj;
                         const float v = g.store_not_add ? acc[a][b][r] : (*p + acc[a][b][r]);
@@ -297,17 +325,15 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g,
                 }
             }
     } else if (EPI == EPI_GEMM) {
-        const int mi = (int)std::min<int64_t>(BMX, g.M - i0);
-        const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
         float* Ct = g.C + i0 * g.ldc + j0;
 #pragma unroll
         for (int a = 0; a < WA; ++a)
 #pragma unroll
             for (int b = 0; b < WB; ++b) {
-                const int jj = wn + 32 * b + li;
+                const int jj = wn + MF * b + Sh::col(lane);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ii = wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                for (int r = 0; r < NACC; ++r) {
+                    const int ii = wm + MF * a + Sh::row(lane, r);
                     if (ii < mi && jj < nj) {
                         float* p = Ct + (int64_t)ii * g.ldc + jj;
                         const float v = g.alpha * acc[a][b][r];
@@ -316,24 +342,22 @@ __device__ __forceinline__ void store_tile(const Bf16GemmArgs& g,
                 }
             }
     } else {
-        const int mi = (int)std::min<int64_t>(BMX, g.M - i0);
-        const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
         double s = 0.0;
 #pragma unroll
         for (int a = 0; a < WA; ++a)
 #pragma unroll
             for (int b = 0; b < WB; ++b) {
                 float part = 0.f;
-                const int jj = wn + 32 * b + li;
+                const int jj = wn + MF * b + Sh::col(lane);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ii = wm + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                for (int r = 0; r < NACC; ++r) {
+                    const int ii = wm + MF * a + Sh::row(lane, r);
                     const float v = (ii < mi && jj < nj) ? acc[a][b][r] : 0.f;
                     part = fmaf(v, v, part);
                 }
                 s += (double)part;
             }
-        // wave reduction (fixed order), then across the 4 waves through LDS
+        // wave reduction (fixed order), then across the waves through LDS
         // (the staging buffers are free after the last barrier)
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
         double* red = (double*)smem;
@@ -387,11 +411,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8));
 }
 
-template <int BMX, int EPI, int DKT, int NST, int NW>
+template <int BMX, int EPI, int DKT, int NST, int NW, int MF>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g, int64_t nwork) {
     using S = DStage<DKT>;
-    using WTL = WaveTile<BMX, NW>;
-    constexpr int ROWB = S::ROWB, KSUB = S::KSUB;
+    using WTL = WaveTile<BMX, NW, MF>;
+    using Sh = MfmaShape<MF>;
+    constexpr int ROWB = S::ROWB, KSUB = DKT / Sh::KDEP;
     constexpr int WA = WTL::WA, WB = WTL::WB;          // accumulator blocks per wave (rows, columns)
     constexpr int NM = WA * WB, NR = WA + WB;          // MFMAs and fragment reads per k-step
     constexpr int PER = BMX * S::CH / (64 * NW);       // load instructions per wave per panel per stage
@@ -497,13 +522,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         for (int q = 0; q < 2 * PER; ++q) load_one(s, buf, q);
     };
 
-    f32x16 acc[WA][WB];
+    typename WTL::acc_t acc[WA][WB];
 #pragma unroll
     for (int a = 0; a < WA; ++a)
 #pragma unroll
         for (int b = 0; b < WB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+            for (int r = 0; r < Sh::NACC; ++r) acc[a][b][r] = 0.f;
 
     // Software pipeline over k-steps (16 deep): the fragment reads of the next
     // k-step are interleaved with the MFMAs of the current one, so after the
@@ -515,17 +540,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     // barrier (no memory fence, which would drain every prefetch) the next
     // stage is visible to all waves and this stage's buffer is free, and the
     // copies of stage s + NST go into it.
-    const int fsw = S::sw(li);   // fragment swizzle term, lane-only (row = wm + 32 a + li)
+    const int fr = lane % MF;     // operand row of this lane within a block
+    const int fsw = S::sw(fr);    // fragment swizzle term, lane-only (row = wm + MF a + fr)
     bf16x8 fa[2][WA], fb[2][WB];
-    // k-step kk reads chunk 2 kk + lh of its rows
-    auto fragp = [&](int64_t s, int kk) { return smem + (s % NST) * (2 * PANEL) + 16 * ((2 * kk + lh) ^ fsw); };
+    // k-step kk reads chunk (KDEP / 8) kk + lane / MF of its rows
+    auto fragp = [&](int64_t s, int kk) {
+        return smem + (s % NST) * (2 * PANEL) + 16 * (((Sh::KDEP / 8) * kk + lane / MF) ^ fsw);
+    };
     // fragment q of a k-step, in the order the MFMAs (a-major) consume them:
     // A block 0, the B blocks, then the other A blocks
     auto read_one = [&](int64_t s, int kk, int slot, int q) {
         const unsigned char* As = fragp(s, kk);
-        if (q == 0) fa[slot][0] = *(const bf16x8*)(As + (wm + li) * ROWB);
-        else if (q <= WB) fb[slot][q - 1] = *(const bf16x8*)(As + PANEL + (wn + 32 * (q - 1) + li) * ROWB);
-        else fa[slot][q - WB] = *(const bf16x8*)(As + (wm + 32 * (q - WB) + li) * ROWB);
+        if (q == 0) fa[slot][0] = *(const bf16x8*)(As + (wm + fr) * ROWB);
+        else if (q <= WB) fb[slot][q - 1] = *(const bf16x8*)(As + PANEL + (wn + MF * (q - 1) + fr) * ROWB);
+        else fa[slot][q - WB] = *(const bf16x8*)(As + (wm + MF * (q - WB) + fr) * ROWB);
     };
     auto frags = [&](int64_t s, int kk, int slot) {
 #pragma unroll
@@ -533,7 +561,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     };
     auto mfma_one = [&](int slot, int idx) {
         const int a = idx / WB, b = idx % WB;
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][a], fb[slot][b], acc[a][b], 0, 0, 0);
+        acc[a][b] = Sh::mfma(fa[slot][a], fb[slot][b], acc[a][b]);
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
@@ -597,16 +625,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     }
     wait_vmcnt<0, true>();
     __syncthreads();
-    store_tile<BMX, EPI, NW>(g, acc, i0, j0, diag, L, smem);
+    store_tile<BMX, EPI, NW, MF>(g, acc, i0, j0, diag, L, smem);
 }
 
 // Opt a kernel into more than 64 KB of dynamic LDS (once per instantiation).
-template <int BMX, int EPI, int DKT, int NW = 4>
+template <int BMX, int EPI, int DKT, int NW = 4, int MF = 32>
 int prepare_kernel() {
     static bool done = false;
     if (!done) {
         if constexpr (DKT > 0)
-            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, DNST<DKT>, NW>,
+            PTQ_HIP(hipFuncSetAttribute((const void*)gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, DNST<DKT>, NW, MF>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         dsmem_bytes<BMX, DKT, DNST<DKT>>()));
         else
@@ -617,20 +645,24 @@ int prepare_kernel() {
     return PTQ_OK;
 }
 
-template <int BMX, int EPI, int DKT, int NW = 4>
+template <int BMX, int EPI, int DKT, int NW = 4, int MF = 32>
 int launch_direct(const Bf16GemmArgs& g, int64_t nwork, unsigned grid, unsigned grid_y, hipStream_t st) {
     constexpr int nst = DNST<DKT>;
     constexpr int lds = dsmem_bytes<BMX, DKT, nst>();
-    PTQ_TRY((prepare_kernel<BMX, EPI, DKT, NW>()));
-    hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, nst, NW>), dim3(grid, grid_y), dim3(64 * NW), lds,
-                       st, g, nwork);
+    PTQ_TRY((prepare_kernel<BMX, EPI, DKT, NW, MF>()));
+    hipLaunchKernelGGL((gemm_bf16_nt_direct_kernel<BMX, EPI, DKT, nst, NW, MF>), dim3(grid, grid_y), dim3(64 * NW),
+                       lds, st, g, nwork);
     return PTQ_OK;
 }
 
-// waves per workgroup of the direct kernel at 64-deep stages and 256-wide tiles:
-// eight (two per SIMD, 64 x 128 accumulators each) let one wave issue MFMAs
-// while the other waits on a fragment read, a copy or the barrier
+// Direct kernel at 64-deep stages and 256-wide tiles: eight waves (two per
+// SIMD, 64 x 128 accumulators each) let one wave issue MFMAs while the other
+// waits on a fragment read, a copy or the barrier; 16x16x32 MFMAs (16 cycles
+// each, 4 accumulator registers) interleave those waits at half the grain of
+// 32x32x16 ones. Measured on X^T X per 65536-row chunk: 4 waves / 32x32
+// 51.3 ms, 8 / 32x32 50.1, 8 / 16x16 46.1, 4 / 16x16 58.9.
 constexpr int DNW = 8;
+constexpr int DMF = 16;
 
 // Launch the direct variant when both K segments are multiples of its stage
 // depth (64, else 32), the register-staged one otherwise.
@@ -638,7 +670,7 @@ template <int BMX, int EPI>
 int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t st) {
     const unsigned grid = (unsigned)(EPI == EPI_HESSIAN ? 256 * hessian_rounds(g.T) : cdiv(nwork, NXCD) * NXCD);
     if (g.M > 0 && g.N > 0 && g.K1 % 64 == 0 && g.K2 % 64 == 0) {
-        PTQ_TRY((launch_direct<BMX, EPI, 64, BMX == 256 ? DNW : 4>(g, nwork, grid, grid_y, st)));
+        PTQ_TRY((launch_direct<BMX, EPI, 64, BMX == 256 ? DNW : 4, BMX == 256 ? DMF : 32>(g, nwork, grid, grid_y, st)));
     } else if (g.M > 0 && g.N > 0 && g.K1 % 32 == 0 && g.K2 % 32 == 0) {
         PTQ_TRY((launch_direct<BMX, EPI, 32>(g, nwork, grid, grid_y, st)));
     } else {
@@ -770,7 +802,7 @@ int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStr
     const unsigned grid = (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n
                                                        : g.tiles_m * g.tiles_n);
     prof_begin(PROF_SPLIT3_GEMM, st);
-    const int rc = launch_direct<256, EPI_GEMM, 64>(g, 0, grid, 1, st);
+    const int rc = launch_direct<256, EPI_GEMM, 64, DNW, DMF>(g, 0, grid, 1, st);
     prof_end(PROF_SPLIT3_GEMM, st);
     PTQ_TRY(rc);
     PTQ_LAUNCH_CHECK();
