@@ -305,10 +305,15 @@ __global__ void sum_rows_kernel(const double* row_out, int64_t out, double* tot)
 
 __global__ void zero_int_kernel(int* p) { *p = 0; }
 
+// Trailing updates with at least this many rows and columns run on the bf16
+// MFMA from three-term bf16 splits of E and U's rows (fp32 accuracy,
+// gemm_bf16.hip); smaller ones on the fp32 MFMA GEMM.
+constexpr int64_t TRAIL_SPLIT3_MIN = 2048;
+
 template <int B, bool ZP>
 int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float qmax, const int32_t* perm,
                int8_t* codes, float* scales, int8_t* zeros, int64_t ngroups, float* gmaxes, float* E, float* err2,
-               int64_t nblocks, int* flag, hipStream_t st) {
+               int64_t nblocks, int* flag, uint16_t* Pa, uint16_t* Pb, hipStream_t st) {
     constexpr int RPW = NTH / (B / CPL);
     const unsigned grid = (unsigned)cdiv(out, RPW);
     // W_cur[:, c1:] -= Err[:, 0:K] U[k0:k0+K, c1:c2]
@@ -326,8 +331,9 @@ int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float q
         a.B = U + k0 * n + c1; a.ldb = n; a.layout_b = B_KN;
         a.C = Wc + c1; a.ldc = n;
         a.alpha = -1.f; a.beta_one = 1; a.tri = TRI_NONE; a.upper_only = 0;
+        const bool split = Pa && kernel == PROF_TRAIL_GEMM && a.M >= TRAIL_SPLIT3_MIN && a.N >= TRAIL_SPLIT3_MIN;
         prof_begin(kernel, st);
-        const int s = launch_gemm_f32(a, st);
+        const int s = split ? launch_gemm_f32_split3(a, Pa, Pb, st) : launch_gemm_f32(a, st);
         prof_end(kernel, st);
         return s;
     };
@@ -361,6 +367,10 @@ size_t columns_workspace_bytes(int64_t out, int64_t n, int block) {
     z.take<double>((size_t)out * 2);         // per-row stats
     z.take<double>(2);                       // totals
     z.take<int>(1);                          // flag
+    if (out >= TRAIL_SPLIT3_MIN && n >= TRAIL_SPLIT3_MIN) {   // split planes of E and of U's rows
+        z.take<uint16_t>(gemm_f32_split3_elems(out, SB_COLS));
+        z.take<uint16_t>(gemm_f32_split3_elems(n, SB_COLS));
+    }
     return z.bytes();
 }
 
@@ -378,7 +388,10 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
     double* rowst = ar.take<double>((size_t)out * 2);
     double* tot = ar.take<double>(2);
     int* flag = ar.take<int>(1);
-    if (!Wc || !E || !err2 || !gmaxes || !rowst || !tot || !flag) {
+    const bool split = out >= TRAIL_SPLIT3_MIN && n >= TRAIL_SPLIT3_MIN;
+    uint16_t* Pa = split ? ar.take<uint16_t>(gemm_f32_split3_elems(out, SB_COLS)) : nullptr;
+    uint16_t* Pb = split ? ar.take<uint16_t>(gemm_f32_split3_elems(n, SB_COLS)) : nullptr;
+    if (!Wc || !E || !err2 || !gmaxes || !rowst || !tot || !flag || (split && (!Pa || !Pb))) {
         set_error("gptq_quantize_columns: workspace of %zu bytes, %zu needed", ws_bytes,
                   columns_workspace_bytes(out, n, block));
         return PTQ_EWORKSPACE;
@@ -400,12 +413,12 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
             constexpr bool Z = decltype(zp)::value;
             if (block == 128)
                 return run_blocks<128, Z>(Wc, out, n, U, g, qmax, perm, codes, scales, zeros, ngroups, gmaxes, E, err2,
-                                          nblocks, flag, st);
+                                          nblocks, flag, Pa, Pb, st);
             if (block == 64)
                 return run_blocks<64, Z>(Wc, out, n, U, g, qmax, perm, codes, scales, zeros, ngroups, gmaxes, E, err2,
-                                         nblocks, flag, st);
+                                         nblocks, flag, Pa, Pb, st);
             return run_blocks<32, Z>(Wc, out, n, U, g, qmax, perm, codes, scales, zeros, ngroups, gmaxes, E, err2,
-                                     nblocks, flag, st);
+                                     nblocks, flag, Pa, Pb, st);
         };
         if (zeros) PTQ_TRY(blocks(std::true_type{}));
         else PTQ_TRY(blocks(std::false_type{}));
