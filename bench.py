@@ -178,7 +178,7 @@ def main():
     achieved = flops_per_launch / avg_launch_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                "kernel": "gemm_bf16_nt_direct_kernel<256, 0, 64, 2, 8> (X^T X tiles, one launch per 65536-row chunk)",
+                "kernel": "gemm_bf16_nt_direct_kernel<256, 0, 64, 2, 8, 16> (X^T X tiles, one launch per 65536-row chunk)",
                 "avg_launch_ms": round(avg_launch_s * 1e3, 3), "launches": xtx_launches}
 
     breakdown = None
