@@ -26,8 +26,10 @@ def _compare(res, ref, alphas):
         assert np.allclose(res["s"].cpu().double().numpy(), ref["s"], rtol=1e-6)
 
 
+# n = 1056 (a multiple of 32, not of 64) takes the 32-deep ring of the direct
+# kernel; 520 the register-staged kernel; 1024 the 64-deep ring
 @pytest.mark.parametrize("dtype,out,n,rows", [("f32", 256, 512, 2048), ("bf16", 300, 1024, 1000),
-                                              ("bf16", 128, 520, 700)])
+                                              ("bf16", 128, 520, 700), ("bf16", 260, 1056, 600)])
 def test_awq_small(gpu, dtype, out, n, rows):
     from post_int4_weight_amd import api
     announce(f"awq {dtype} out={out} n={n} rows={rows}")
