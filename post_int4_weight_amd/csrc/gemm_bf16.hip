@@ -1,8 +1,9 @@
-// bf16 "NT" GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16):
+// bf16 "NT" GEMM on CDNA4 matrix cores (v_mfma_f32_16x16x32_bf16 or
+// v_mfma_f32_32x32x16_bf16):
 //
 //   C[i][j] = sum_k A[i][k] B[j][k]      A [M, K], B [N, K], both K-contiguous
 //
-// Two uses, selected by the epilogue:
+// Three uses, selected by the epilogue:
 //  * the proxy Hessian H (+)= X^T X ("GPTQ versus AWQ objectives", "A strong
 //    answer"), run on a transposed chunk of the calibration rows, Xt [in,
 //    rows], with A = B = Xt: only tiles on or above the diagonal are
@@ -11,16 +12,20 @@
 //    with A = X [rows, in] and B = dW [out, in] split into a bf16 high part and
 //    a bf16 residual (dW = hi + lo to ~16 significant bits): the K loop runs
 //    over both halves with the same A, and the epilogue reduces the tile's
-//    sum of squares to one fp64 partial per workgroup (E is never written).
+//    sum of squares to one fp64 partial per workgroup (E is never written);
+//  * fp32 GEMMs C = alpha A B (+ C) whose operands arrive as three-term bf16
+//    splits (the large products of the U recursion and the GPTQ trailing
+//    updates; see launch_gemm_f32_split3 below).
 //
-// Tile 256 x 256 (or 128 x 128) per workgroup of 256 threads, 4 wave64s in
-// 2 x 2, each wave a (BM/2)^2 block of 32x32 MFMA accumulators. Two main
-// loops: the direct-to-LDS one (K segments multiples of 64, or of 32, which
-// covers every call on the path) described further down, and a
-// register-staged one for any K: 16-byte
-// chunks go through registers into 128-byte LDS rows whose chunk index is
-// XOR-swizzled by (row >> 1) & 7, so the staging writes and the ds_read_b128
-// operand fetches are free of bank conflicts.
+// Tile 256 x 256 (or 128 x 128) per workgroup of NW wave64s in NW/2 x 2
+// (WaveTile), each wave a block of MF x MF MFMA accumulators (MfmaShape):
+// 256-wide tiles use 8 waves of 16x16x32, 128-wide ones 4 waves of 32x32x16.
+// Two main loops: the direct-to-LDS one (K segments multiples of 64, or of
+// 32, which covers every call on the path) described further down, and a
+// register-staged one for any K (4 waves of 32x32x16): 16-byte chunks go
+// through registers into 128-byte LDS rows whose chunk index is XOR-swizzled
+// by (row >> 1) & 7, so the staging writes and the ds_read_b128 operand
+// fetches are free of bank conflicts.
 //
 // Workgroup order is XCD-aware (blockIdx b runs on XCD b % 8): Hessian tiles
 // go in rounds of 16 x 16 super-blocks split into one 4 x 8 sub-block per XCD
@@ -691,7 +696,7 @@ int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t
 // drops those of order 2^-24 and below; each term product is exact and all
 // six accumulate in the same fp32 MFMA accumulators, so the result carries
 // fp32 GEMM accuracy at six bf16 MFMAs (16 x the fp32 MFMA's rate each) per
-// 32 x 32 x 16 block.
+// block and k-step.
 __device__ __forceinline__ void split3(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
     if (!(fabsf(x) <= 3.3e38f)) {   // NaN / Inf (or a value bf16 rounding would overflow): keep hi only
         h = (uint16_t)(__float_as_uint(x) >> 16) | (uint16_t)((x != x) ? 0x40 : 0);
