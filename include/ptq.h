@@ -69,9 +69,10 @@ int ptq_abi_version(void);
  * class k is bracketed by two hipEvents recorded on its launch stream:
  *   0 X^T X bf16 MFMA tiles        1 fp32 GEMMs of the U recursion
  *   2 diagonal-block factor/inverse 3 GPTQ in-block column loop
- *   4 GPTQ trailing fp32 GEMM       5 AWQ error GEMM
+ *   4 GPTQ trailing GEMM            5 AWQ error GEMM
  *   6 GPTQ fp32 update inside a super-block of columns
- *   7 fp32 GEMMs run as bf16 MFMAs on three-term bf16 splits (inside 1)
+ *   7 fp32 GEMMs run as bf16 MFMAs on three-term bf16 splits (the large
+ *     ones inside 1 and 4; main loop only)
  * Enabling (any mask, 0 included) discards earlier records. ptq_profile_read
  * waits for the recorded events of class `kernel` and returns the sum of
  * their elapsed times (ms) and the number of launches. Process-wide; calls
@@ -132,8 +133,10 @@ int gptq_inverse_factor(const float* H, const double* d, int64_t in, double damp
  * clip(round_half_even(w / scale), -qmax-1, qmax) (scale 0 gives code 0);
  * err = (w - code*scale) / U_jj is subtracted from the later columns through
  * row j of U. Updates are batched over blocks of `block_size` columns (the
- * page's lazy batch): in-block updates in registers, then one fp32 MFMA GEMM
- * W_cur[:, b1:] -= E U[b0:b1, b1:] per block; the arithmetic is the same.
+ * page's lazy batch): in-block updates in registers, then one GEMM
+ * W_cur[:, b1:] -= E U[b0:b1, b1:] per block (fp32 MFMA, or for large ones
+ * bf16 MFMAs on three-term bf16 splits of E and U at fp32 accuracy); the
+ * arithmetic is the same up to the order of the fp32 sums.
  *
  * W (not modified) in ORIGINAL column order; U from gptq_inverse_factor (in
  * the processing basis); perm as returned there (NULL = identity).
