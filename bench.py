@@ -204,6 +204,32 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def awq_stage(api, torch, dev):
+    """AWQ's alpha search on the q/k/v-shaped layer (W [8192, 8192], its first
+    4096 calibration rows, the 20-point grid): whole call and error-GEMM time.
+    Algorithmic work 20 * 2 * rows * in * out flops; the error GEMM executes
+    twice that (dW as a bf16 high part plus residual)."""
+    import inputs
+    cfg = inputs.CONFIGS["llama70b_qkv_proj"]
+    Wq, Xq, _ = inputs.layer(cfg, device=dev, rows=inputs.AWQ_CAL_ROWS)
+    alphas = list(inputs.AWQ_ALPHAS)
+    ws = torch.empty(api.awq_workspace_bytes(cfg.out, cfg.inp, inputs.AWQ_CAL_ROWS, len(alphas)),
+                     dtype=torch.uint8, device=dev)
+    api.awq_search_alpha(Wq, Xq, alphas, bits=4, group_size=128, workspace=ws)   # warm
+    api.profile_enable(["awq_gemm"])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    api.awq_search_alpha(Wq, Xq, alphas, bits=4, group_size=128, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    ms, _ = api.profile_read("awq_gemm")
+    api.profile_enable([])
+    f = len(alphas) * 2.0 * inputs.AWQ_CAL_ROWS * cfg.inp * cfg.out
+    return {"awq_qkv_s": round(t, 4), "awq_tflops": round(f / t / 1e12, 1), "awq_gemm_ms": round(ms, 3),
+            "awq_gemm_frac_bf16_peak": round(2 * f / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def stage_breakdown(api, torch, cfg, W, X, H, d, codes, scales, g_idx, perm, ws_h, ws_g, bits, g, block):
     """One extra instrumented step: stage times from torch events on the current
     stream (the library launches on it), kernel-class totals from the library's
@@ -250,6 +276,7 @@ def stage_breakdown(api, torch, cfg, W, X, H, d, codes, scales, g_idx, perm, ws_
         if cnt:
             kern[k] = {"total_ms": round(ms, 3), "launches": cnt}
     api.profile_enable([])
+    awq = awq_stage(api, torch, X.device)
     f_xtx = N * n * (n + 1)
     f_u = 2.0 * n ** 3 / 3.0
     nb = (n + block - 1) // block
@@ -264,6 +291,7 @@ def stage_breakdown(api, torch, cfg, W, X, H, d, codes, scales, g_idx, perm, ws_
         "int4_dequant_bf16_ms": round(t_deq * 1e3, 4),
         "int4_dequant_frac_hbm": round(b_deq / t_deq / 1e9 / PEAK_HBM_GBS, 4),
     }
+    out.update(awq)
     if "xtx_gemm" in kern:
         out["xtx_kernel_frac_bf16_peak"] = round(f_xtx / (kern["xtx_gemm"]["total_ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)
     if "factor_gemm" in kern:

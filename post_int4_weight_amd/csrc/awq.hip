@@ -93,36 +93,47 @@ __device__ __forceinline__ double awq_group(const T* W, int64_t row_off, int64_t
     return scale;
 }
 
-// One thread per (alpha, row, group): RTN of the scaled group, then either the
-// hi/lo split of dW = W - Q(W diag s) diag(s)^-1 (search) or the codes and
-// scales of W diag(s) (final).
+// One wave per (alpha, row, group), lanes across the group's columns (so
+// loads and stores are coalesced): the group max of |W diag(s)| by a wave
+// reduction, then the RTN of every column, decided in fp64 with the same
+// operations as awq_group; either the hi/lo split of dW = W - Q(W diag s)
+// diag(s)^-1 (search) or the codes and scales of W diag(s) (final).
 template <typename T>
-__global__ void awq_quant_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n, int g, float qmax,
-                                 const double* __restrict__ s_all, int na, uint16_t* __restrict__ hi,
-                                 uint16_t* __restrict__ lo, int8_t* __restrict__ codes, float* __restrict__ scales,
-                                 int64_t ngroups) {
+__global__ __launch_bounds__(256) void awq_quant_kernel(const T* __restrict__ W, int64_t ldw, int64_t out, int64_t n,
+                                                        int g, float qmax, const double* __restrict__ s_all, int na,
+                                                        uint16_t* __restrict__ hi, uint16_t* __restrict__ lo,
+                                                        int8_t* __restrict__ codes, float* __restrict__ scales,
+                                                        int64_t ngroups) {
+    const int lane = threadIdx.x & 63;
     const int64_t per_a = out * ngroups;
-    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= per_a * na) return;
+    const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (id >= per_a * na) return;   // whole waves
     const int a = (int)(id / per_a);
     const int64_t rem = id % per_a;
     const int64_t r = rem / ngroups, grp = rem % ngroups;
     const double* s = s_all + (int64_t)a * n;
     const int64_t c0 = grp * g, c1 = std::min<int64_t>(n, c0 + g);
-    const double scale = awq_group<T>(W, r * ldw, c0, c1, s, (double)qmax, [&](int64_t c, double w, double q,
-                                                                                 double sc) {
+    const double qm = (double)qmax;
+    double mx = 0.0;
+    for (int64_t c = c0 + lane; c < c1; c += 64)
+        mx = fmax(mx, fabs((double)load_as_float<T>(W, r * ldw + c) * s[c]));
+    for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off, 64));
+    const double scale = mx / qm;
+    for (int64_t c = c0 + lane; c < c1; c += 64) {
+        const double w = (double)load_as_float<T>(W, r * ldw + c);
+        double q = 0.0;
+        if (scale > 0.0) q = fmin(fmax(rint((w * s[c]) / scale), -qm - 1.0), qm);
         if (codes) {
             codes[r * n + c] = (int8_t)(int)q;
         } else {
-            const float dw = (float)(w - (q * sc) / s[c]);
+            const float dw = (float)(w - (q * scale) / s[c]);
             const uint16_t h = float_to_bf16_bits(dw);
-            const float l = dw - bf16_bits_to_float(h);
             const int64_t o = (int64_t)a * out * n + r * n + c;
             hi[o] = h;
-            lo[o] = float_to_bf16_bits(l);
+            lo[o] = float_to_bf16_bits(dw - bf16_bits_to_float(h));
         }
-    });
-    if (scales) scales[r * ngroups + grp] = (float)scale;
+    }
+    if (scales && lane == 0) scales[r * ngroups + grp] = (float)scale;
 }
 
 // fp32 path: dW as fp32 for one alpha (no split)
@@ -292,7 +303,7 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
     }
 
     if (bf) {
-        const int64_t nth = out * ngroups * n_alpha;
+        const int64_t nth = cdiv(out * ngroups * n_alpha, 4) * 256;   // one wave per (alpha, row, group)
         if (w_dtype == PTQ_BF16)
             hipLaunchKernelGGL(awq_quant_kernel<uint16_t>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st,
                                (const uint16_t*)W, ldw, out, n, g, qmax, s_all, n_alpha, hi, lo, (int8_t*)nullptr,
@@ -348,7 +359,7 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
         hipLaunchKernelGGL(s_to_f32_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, sb, n, s_out);
         PTQ_LAUNCH_CHECK();
     }
-    const int64_t nth = out * ngroups;
+    const int64_t nth = cdiv(out * ngroups, 4) * 256;
     if (w_dtype == PTQ_BF16)
         hipLaunchKernelGGL(awq_quant_kernel<uint16_t>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st,
                            (const uint16_t*)W, ldw, out, n, g, qmax, sb, 1, (uint16_t*)nullptr, (uint16_t*)nullptr,
