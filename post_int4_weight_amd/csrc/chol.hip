@@ -92,6 +92,22 @@ __global__ void build_damped_kernel(const float* __restrict__ H, const int32_t* 
     }
 }
 
+// The same without a permutation, 16 bytes per thread (n % 4 == 0).
+__global__ void build_damped_vec_kernel(const float4* __restrict__ H, int64_t n4, const double* lam,
+                                        float4* __restrict__ A) {
+    const int64_t i = blockIdx.y;
+    const float l = (float)*lam;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (int64_t)gridDim.x * blockDim.x) {
+        float4 v = H[i * n4 + q];
+        const int64_t d = i - 4 * q;   // position of the diagonal inside this float4, if any
+        if (d == 0) v.x = (float)((double)v.x + (double)l);
+        if (d == 1) v.y = (float)((double)v.y + (double)l);
+        if (d == 2) v.z = (float)((double)v.z + (double)l);
+        if (d == 3) v.w = (float)((double)v.w + (double)l);
+        A[i * n4 + q] = v;
+    }
+}
+
 __global__ void fill_zero_kernel(float* p, int64_t count) {
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
          e += (int64_t)gridDim.x * blockDim.x)
@@ -313,8 +329,12 @@ int run_inverse_factor(const float* H, const double* d, int64_t n, double damp, 
         hipLaunchKernelGGL(identity_perm_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, p, n);
     }
     PTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(build_damped_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)n),
-                       dim3(256), 0, st, H, act_order ? p : nullptr, n, lam, c.A);
+    if (!act_order && n % 4 == 0 && ((uintptr_t)H & 15u) == 0)
+        hipLaunchKernelGGL(build_damped_vec_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n / 4, 256), 64), (unsigned)n),
+                           dim3(256), 0, st, (const float4*)H, n / 4, lam, (float4*)c.A);
+    else
+        hipLaunchKernelGGL(build_damped_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)n),
+                           dim3(256), 0, st, H, act_order ? p : nullptr, n, lam, c.A);
     PTQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, st, U, n * n);
     PTQ_LAUNCH_CHECK();
