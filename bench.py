@@ -175,11 +175,20 @@ def main():
     rows_per_launch = N / launches_per_step
     flops_per_launch = rows_per_launch * n * (n + 1)
     avg_launch_s = xtx_ms / 1e3 / max(1, xtx_launches)
-    achieved = flops_per_launch / avg_launch_s / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                "kernel": "gemm_bf16_nt_direct_kernel<256, 0, 64, 2, 8, 16> (X^T X tiles, one launch per 65536-row chunk)",
-                "avg_launch_ms": round(avg_launch_s * 1e3, 3), "launches": xtx_launches}
+    # bf16 X: the direct kernel on 256-wide tiles (128-wide below in = 2048);
+    # fp32 X goes through the fp32 GEMM, which this field does not cover
+    if xtx_launches and n >= 2048:
+        kname = "gemm_bf16_nt_direct_kernel<256, 0, 64, 2, 8, 16>"
+    elif xtx_launches:
+        kname = "gemm_bf16_nt_direct_kernel<128, 0, 64, 2, 4, 32>"
+    else:
+        kname = None
+    achieved = flops_per_launch / avg_launch_s / 1e12 if xtx_launches else None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2) if achieved else None, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+                "traffic": measured_traffic() if args.workload == "llama70b_down_proj" else None,
+                "kernel": f"{kname} (X^T X tiles, one launch per 65536-row chunk)" if kname else None,
+                "avg_launch_ms": round(avg_launch_s * 1e3, 3) if xtx_launches else None, "launches": xtx_launches}
 
     breakdown = None
     if not args.no_breakdown:

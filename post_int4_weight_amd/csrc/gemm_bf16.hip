@@ -51,19 +51,39 @@ template <int BMX>
 constexpr int smem_bytes() { return 4 * BMX * ROWB; }   // A and B, two stages each
 
 // Hessian tiles (upper triangle of a T x T tile grid) in rounds of 256
-// workgroups; workgroup b runs on XCD b % 8. Round r is the r-th SB x SB
-// super-block (P <= Q, row-major) and XCD x takes its 4 x 8 sub-block (rows
-// 4 (x / 2).., columns 8 (x % 2)..): the 256 tiles of a round, which start
-// together and move through k together, read 32 panels (16 on the diagonal),
-// so the die-shared last-level cache serves most of what one XCD's L2
-// misses, and the 32 tiles of one XCD read 12 panels through its own L2.
-// Slots outside the triangle or the grid return at once.
+// workgroups; workgroup b runs on XCD b % 8 and the XCD with the most tiles
+// sets the launch time, so every round deals its tiles evenly over the XCDs.
+// Round r is the r-th SB x SB super-block (P <= Q, row-major), cut into eight
+// 4 x 8 sub-blocks (rows 4 (s / 2).., columns 8 (s % 2)..). Its v valid tiles
+// (inside the grid, on or above the diagonal) are listed sub-block by
+// sub-block, row-major inside each, and XCD x takes the x-th run of
+// ceil(v / 8) of them. A full off-diagonal super-block gives each XCD one
+// whole sub-block: its 32 tiles read 12 panels through the XCD's own L2, and
+// the 256 tiles of the round, which start together and move through k
+// together, read 32 panels between them, so the die-shared last-level cache
+// serves most of what the L2s miss. On a diagonal super-block the sub-blocks
+// go in the order (0, 2, 1, 3, 4..7), left triangle, right square, right
+// triangle, so that each XCD's run of 17 stays compact. Slots past a run
+// return at once.
 constexpr int SB = 16;
 __host__ __device__ inline int64_t hessian_rounds(int T) {
     const int64_t nb = cdiv(T, SB);
     return nb * (nb + 1) / 2;
 }
-__device__ __forceinline__ bool hessian_tile(int64_t b, int T, int& ti, int& tj) {
+// valid tiles of row ti among the 8 columns from c0
+__host__ __device__ inline int hessian_row_tiles(int ti, int c0, int T) {
+    if (ti >= T) return 0;
+    const int hi = c0 + 8 < T ? c0 + 8 : T, lo = c0 > ti ? c0 : ti;
+    return hi > lo ? hi - lo : 0;
+}
+// valid tiles of super-block (P, Q)
+__host__ __device__ inline int hessian_round_tiles(int P, int Q, int T) {
+    int v = 0;
+    for (int s = 0; s < 8; ++s)
+        for (int a = 0; a < 4; ++a) v += hessian_row_tiles(SB * P + 4 * (s >> 1) + a, SB * Q + 8 * (s & 1), T);
+    return v;
+}
+__host__ __device__ inline bool hessian_tile(int64_t b, int T, int& ti, int& tj) {
     const int nb = (int)cdiv(T, SB);
     int64_t r = b / 256;
     const int w = (int)(b % 256), x = w % NXCD, i = w / NXCD;
@@ -73,9 +93,23 @@ __device__ __forceinline__ bool hessian_tile(int64_t b, int T, int& ti, int& tj)
         ++P;
     }
     const int Q = P + (int)r;
-    ti = SB * P + 4 * (x >> 1) + (i >> 3);
-    tj = SB * Q + 8 * (x & 1) + (i & 7);
-    return ti < T && tj < T && ti <= tj;
+    const int v = hessian_round_tiles(P, Q, T), per = (v + NXCD - 1) / NXCD;
+    int c = x * per + i;
+    if (i >= per || c >= v) return false;
+    for (int k = 0; k < 8; ++k) {
+        const int s = (k == 1) ? 2 : (k == 2) ? 1 : k;
+        const int c0 = SB * Q + 8 * (s & 1);
+        for (int a = 0; a < 4; ++a) {
+            const int row = SB * P + 4 * (s >> 1) + a, m = hessian_row_tiles(row, c0, T);
+            if (c < m) {
+                ti = row;
+                tj = (c0 > row ? c0 : row) + c;
+                return true;
+            }
+            c -= m;
+        }
+    }
+    return false;
 }
 
 struct Bf16GemmArgs {
@@ -85,7 +119,10 @@ struct Bf16GemmArgs {
     int64_t K1, K2;
     int64_t lda, ldb;
     int64_t M, N;
-    int64_t b_batch_stride;    // EPI_SUMSQ: B offset per blockIdx.y
+    int64_t b_batch_stride;    // EPI_SUMSQ / EPI_HESSIAN: B offset per blockIdx.y
+    // EPI_HESSIAN split over depth: blockIdx.y takes depth [y K1, min(ktot, (y+1) K1)) of A1/B1 (A1 and B1
+    // advance by a_batch_stride / b_batch_stride) and writes its own partial H at H + y * h_batch_stride
+    int64_t a_batch_stride, h_batch_stride, ktot;
     // EPI_HESSIAN
     float* H; int64_t ldh; int mirror; int T; int store_not_add;
     // EPI_SUMSQ
@@ -154,6 +191,13 @@ __device__ __forceinline__ void store_panel(unsigned char* S, const uint4 (&v)[B
     }
 }
 
+// Depth of the first operand segment for this workgroup's blockIdx.y (split
+// over depth when ktot > 0, else K1).
+__device__ __forceinline__ int64_t split_depth(const Bf16GemmArgs& g) {
+    if (g.ktot <= 0) return g.K1;
+    return std::max<int64_t>(0, std::min<int64_t>(g.K1, g.ktot - (int64_t)blockIdx.y * g.K1));
+}
+
 // The two bf16 MFMA shapes. Operands: lane l supplies row l % MF of its
 // block and the 8 consecutive k at 8 * (l / MF) of the k-step (KDEP deep).
 // Accumulator register r of lane l holds row row(l, r), column col(l).
@@ -215,6 +259,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
         i0 = (L / g.tiles_n) * BMX;
         j0 = (L % g.tiles_n) * BMX;
     }
+    const uint16_t* A1 = g.A1 + (int64_t)blockIdx.y * g.a_batch_stride;
     const uint16_t* B1 = g.B1 + (int64_t)blockIdx.y * g.b_batch_stride;
     const uint16_t* B2 = g.B2 ? g.B2 + (int64_t)blockIdx.y * g.b_batch_stride : nullptr;
 
@@ -234,15 +279,16 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    const int64_t n1 = cdiv(g.K1, KT), n2 = cdiv(g.K2, KT);
+    const int64_t K1 = split_depth(g);
+    const int64_t n1 = cdiv(K1, KT), n2 = cdiv(g.K2, KT);
     const int64_t nst = n1 + n2;
     Stg<BMX> rg;
     const bool rows_full = (i0 + BMX <= g.M) && (j0 + BMX <= g.N);
     auto gload = [&](int64_t s) {
         const bool seg1 = s < n1;
-        const uint16_t* A = seg1 ? g.A1 : g.A2;
+        const uint16_t* A = seg1 ? A1 : g.A2;
         const uint16_t* B = seg1 ? B1 : B2;
-        const int64_t K = seg1 ? g.K1 : g.K2;
+        const int64_t K = seg1 ? K1 : g.K2;
         const int64_t k0 = (seg1 ? s : s - n1) * KT;
         if (rows_full && k0 + KT <= K) {
             load_panel<BMX, false>(rg.a, A, g.lda, i0, g.M, k0, K, t);
@@ -310,8 +356,9 @@ __device__ __forceinline__ void store_tile(
     const int mi = (int)std::min<int64_t>(BMX, g.M - i0);   // valid rows / columns of this tile
     const int nj = (int)std::min<int64_t>(BMX, g.N - j0);
     if (EPI == EPI_HESSIAN) {
-        float* Ht = g.H + i0 * g.ldh + j0;                      // tile origin
-        float* Hm = g.H + j0 * g.ldh + i0;                      // mirror origin
+        float* Hy = g.H + (int64_t)blockIdx.y * g.h_batch_stride;
+        float* Ht = Hy + i0 * g.ldh + j0;                       // tile origin
+        float* Hm = Hy + j0 * g.ldh + i0;                       // mirror origin
         const int ld = (int)g.ldh;
 #pragma unroll
         for (int a = 0; a < WA; ++a)
@@ -461,6 +508,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         i0 = (L / g.tiles_n) * BMX;
         j0 = (L % g.tiles_n) * BMX;
     }
+    const uint16_t* A1 = g.A1 + (int64_t)blockIdx.y * g.a_batch_stride;
     const uint16_t* B1 = g.B1 + (int64_t)blockIdx.y * g.b_batch_stride;
     const uint16_t* B2 = g.B2 ? g.B2 + (int64_t)blockIdx.y * g.b_batch_stride : nullptr;
 
@@ -482,7 +530,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         offA[q] = ra * g.lda + 8 * c;
         offB[q] = rb * g.ldb + 8 * c;
     }
-    int64_t n1 = g.K1 / DKT, nst = n1 + g.K2 / DKT;
+    int64_t n1 = split_depth(g) / DKT, nst = n1 + g.K2 / DKT;
     int64_t kb = 0;
     if (EPI == EPI_GEMM) {
         // depth range of the tile (triangular operands skip their zero
@@ -501,7 +549,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
             const int pq = (int)(s - 6 * kc);
             return g.Ap + ((0x120100 >> (4 * pq)) & 15) * g.a_plane + kb + kc * DKT;
         } else {
-            return s < n1 ? g.A1 + s * DKT : g.A2 + (s - n1) * DKT;
+            return s < n1 ? A1 + s * DKT : g.A2 + (s - n1) * DKT;
         }
     };
     auto stage_b = [&](int64_t s) -> const uint16_t* {
@@ -676,6 +724,10 @@ int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t
     const unsigned grid = (unsigned)(EPI == EPI_HESSIAN ? 256 * hessian_rounds(g.T) : cdiv(nwork, NXCD) * NXCD);
     if (g.M > 0 && g.N > 0 && g.K1 % 64 == 0 && g.K2 % 64 == 0) {
         PTQ_TRY((launch_direct<BMX, EPI, 64, BMX == 256 ? DNW : 4, BMX == 256 ? DMF : 32>(g, nwork, grid, grid_y, st)));
+    } else if constexpr (EPI == EPI_HESSIAN) {
+        // X^T X pads every chunk's depth to a multiple of 64
+        set_error("X^T X tiles: depth %lld is not a multiple of 64", (long long)g.K1);
+        return PTQ_EINVAL;
     } else if (g.M > 0 && g.N > 0 && g.K1 % 32 == 0 && g.K2 % 32 == 0) {
         PTQ_TRY((launch_direct<BMX, EPI, 32>(g, nwork, grid, grid_y, st)));
     } else {
@@ -917,17 +969,18 @@ __global__ void mirror_diag_blocks_kernel(float* H, int64_t n, int bm) {
 }
 
 // H[i][j] += sum_s part[s][i][j] over the upper triangle, mirrored.
+// H[i][j] += sum over the splits of part[s][i][j] on and above the diagonal
+// (in split order); one row per blockIdx.y. The lower triangle is mirrored
+// once after the last chunk.
 __global__ void reduce_partials_kernel(float* H, const float* part, int nsplit, int64_t n) {
     const int64_t nn = n * n;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = e / n, j = e % n;
-        if (i > j) continue;
-        float v = H[e];
-        for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * nn + e];
-        H[e] = v;
-        if (i != j) H[j * n + i] = v;
-    }
+    for (int64_t i = blockIdx.y; i < n; i += gridDim.y)
+        for (int64_t j = i + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t e = i * n + j;
+            float v = H[e];
+            for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * nn + e];
+            H[e] = v;
+        }
 }
 
 // fp64 column sums of squares over one slab of rows; 2 columns per thread.
@@ -967,6 +1020,7 @@ __global__ void reduce_slabs_kernel(double* d, const double* part, int nslab, in
 constexpr int64_t SLAB_ROWS = 2048;
 constexpr int MAX_SLABS = 256;
 constexpr int64_t CHUNK_ROWS_MAX = 65536;   // calibration rows per transposed chunk
+constexpr int64_t SPLIT_ROWS_MIN = 2048;    // depth of one split of a chunk's XtX launch, at least
 // Row stride of the transposed chunk = its depth + XT_PAD elements: a
 // power-of-two stride (65536 bf16 = 128 KB) would send the 256 rows of a
 // panel slice to the same L2 channel and set.
@@ -994,9 +1048,20 @@ XtxPlan plan_xtx(int64_t n, int64_t rows) {
     p.bm = (n >= 2048) ? 256 : 128;
     p.T = (int)cdiv(n, p.bm);
     p.chunk = std::min<int64_t>(CHUNK_ROWS_MAX, cdiv(std::max<int64_t>(rows, 1), 64) * 64);
+    // Split the depth of a launch so that its tile jobs fill the CUs evenly:
+    // the busiest XCD runs its jobs in waves of 32 (one per CU) and sets the
+    // launch time. Take the smallest power of two whose jobs keep 90% of the
+    // slots busy (at most 16, each split at least SPLIT_ROWS_MIN rows deep).
     const int64_t ntiles = (int64_t)p.T * (p.T + 1) / 2;
+    const int nb = (int)cdiv(p.T, SB);
+    int64_t per_xcd = 0;   // tiles of the busiest XCD in one launch without splitting
+    for (int P = 0; P < nb; ++P)
+        for (int Q = P; Q < nb; ++Q) per_xcd += cdiv(hessian_round_tiles(P, Q, p.T), NXCD);
+    auto busy = [&](int64_t s) {
+        return (double)(ntiles * s) / (double)(256 * cdiv(per_xcd * s, 256 / NXCD));
+    };
     int s = 1;
-    while (ntiles * s < 1024 && p.chunk / (2 * s) >= 4096 && s < 16) s *= 2;
+    while (busy(s) < 0.9 && p.chunk / (2 * s) >= SPLIT_ROWS_MIN && s < 16) s *= 2;
     p.nsplit = s;
     p.slab_rows = std::max<int64_t>(SLAB_ROWS, cdiv(cdiv(rows, MAX_SLABS), 64) * 64);
     p.nslab = (int)std::max<int64_t>(1, cdiv(rows, p.slab_rows));
@@ -1072,25 +1137,29 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
         }
         PTQ_LAUNCH_CHECK();
         const bool last = r0 + p.chunk >= rows;
-        const int ns = (p.nsplit > 1 && nr >= p.nsplit * 4096) ? p.nsplit : 1;
+        const int ns = (p.nsplit > 1 && nr >= p.nsplit * SPLIT_ROWS_MIN) ? p.nsplit : 1;
         const int64_t kper = cdiv(cdiv(kt, ns), KT) * KT;
-        for (int s = 0; s < ns; ++s) {
-            const int64_t kb = s * kper, ke = std::min<int64_t>(kt, kb + kper);
+        {
+            // one launch: blockIdx.y = s takes depth [s kper, min(kt, (s+1) kper))
             Bf16GemmArgs g{};
-            g.A1 = Xt + kb; g.B1 = Xt + kb; g.A2 = nullptr; g.B2 = nullptr;
-            g.K1 = std::max<int64_t>(0, ke - kb); g.K2 = 0;
-            g.lda = ldt; g.ldb = ldt; g.M = n; g.N = n; g.b_batch_stride = 0;
-            g.H = (ns > 1) ? hpart + (int64_t)s * n * n : H;
+            g.A1 = Xt; g.B1 = Xt; g.A2 = nullptr; g.B2 = nullptr;
+            g.K1 = kper; g.K2 = 0; g.ktot = kt;
+            g.a_batch_stride = kper; g.b_batch_stride = kper;
+            g.lda = ldt; g.ldb = ldt; g.M = n; g.N = n;
+            g.H = (ns > 1) ? hpart : H;
+            g.h_batch_stride = n * n;
             g.ldh = n; g.mirror = (ns == 1 && last) ? 1 : 0; g.T = p.T; g.store_not_add = (ns > 1) ? 1 : 0;
             prof_begin(PROF_XTX_GEMM, st);
-            const int rc = (p.bm == 256) ? launch_nt<256, EPI_HESSIAN>(g, ntiles, 1, st)
-                                         : launch_nt<128, EPI_HESSIAN>(g, ntiles, 1, st);
+            const int rc = (p.bm == 256) ? launch_nt<256, EPI_HESSIAN>(g, ntiles, (unsigned)ns, st)
+                                         : launch_nt<128, EPI_HESSIAN>(g, ntiles, (unsigned)ns, st);
             prof_end(PROF_XTX_GEMM, st);
             PTQ_TRY(rc);
         }
         if (ns > 1) {
-            // reduce the split partials into H (upper triangle, mirrored)
-            hipLaunchKernelGGL(reduce_partials_kernel, dim3(2048), dim3(256), 0, st, H, hpart, ns, n);
+            // reduce the split partials into H (upper triangle; mirrored after the last chunk)
+            hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 32),
+                                                            (unsigned)std::min<int64_t>(n, 65535)),
+                               dim3(256), 0, st, H, hpart, ns, n);
             PTQ_LAUNCH_CHECK();
         } else if (last) {
             hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(64, (unsigned)p.T), dim3(256), 0, st, H, n, p.bm);

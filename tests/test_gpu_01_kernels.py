@@ -95,7 +95,8 @@ def test_gemm_f32_upper_only(gpu, k):
 
 
 @pytest.mark.parametrize("rows,n,dtype", [(1000, 520, "bf16"), (2048, 512, "f32"), (3000, 2056, "bf16"),
-                                          (32768, 1024, "bf16"), (70000, 256, "bf16"), (64, 8, "bf16")])
+                                          (32768, 1024, "bf16"), (70000, 256, "bf16"), (40000, 640, "bf16"),
+                                          (64, 8, "bf16")])
 def test_hessian_vs_oracle(gpu, rows, n, dtype):
     """H relative Frobenius error <= 1e-5, exact symmetry, d to fp64 rounding."""
     import inputs
