@@ -123,6 +123,8 @@ struct Bf16GemmArgs {
     // EPI_HESSIAN split over depth: blockIdx.y takes depth [y K1, min(ktot, (y+1) K1)) of A1/B1 (A1 and B1
     // advance by a_batch_stride / b_batch_stride) and writes its own partial H at H + y * h_batch_stride
     int64_t a_batch_stride, h_batch_stride, ktot;
+    // EPI_HESSIAN operands are panel-blocked (xt_offset): pstride elements per panel of BMX rows
+    int64_t pstride;
     // EPI_HESSIAN
     float* H; int64_t ldh; int mirror; int T; int store_not_add;
     // EPI_SUMSQ
@@ -471,9 +473,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     constexpr int ROWB = S::ROWB, KSUB = DKT / Sh::KDEP;
     constexpr int WA = WTL::WA, WB = WTL::WB;          // accumulator blocks per wave (rows, columns)
     constexpr int NM = WA * WB, NR = WA + WB;          // MFMAs and fragment reads per k-step
-    constexpr int PER = BMX * S::CH / (64 * NW);       // load instructions per wave per panel per stage
+    // X^T X: only the first wave of each SIMD (waves 0 .. NW/2 - 1) issues
+    // the copies, so a copy that stalls at issue holds one of the SIMD's two
+    // waves while the other keeps the MFMA pipe busy (2% on the down_proj
+    // shape against copies from every wave).
+    constexpr int CWV = (EPI == EPI_HESSIAN) ? NW / 2 : NW;   // waves that issue copies
+    constexpr int PER = BMX * S::CH / (64 * CWV);      // copies per copying wave per panel per stage
     constexpr int PANEL = BMX * ROWB;                  // bytes of one operand panel per stage
     static_assert(NST >= 2 && KSUB % 2 == 0 && NM >= NR && PER >= 1, "pipeline shape");
+    static_assert(EPI != EPI_HESSIAN || (DKT == 64 && PER % 2 == 0), "X^T X copy layout");
     int64_t i0, j0, L = 0;
     bool diag = false;
     if (EPI == EPI_HESSIAN) {
@@ -514,21 +522,35 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
+    // X^T X keeps the wave index in an SGPR (scalar copy addressing and branch)
+    const int lane = t & 63, wave = (EPI == EPI_HESSIAN) ? __builtin_amdgcn_readfirstlane(t >> 6) : t >> 6;
     const int wm = (wave >> 1) * WTL::TM, wn = (wave & 1) * WTL::TN;
+    const int cw = wave % CWV;                           // copy slot of this wave
+    const bool copier = CWV == NW || wave < CWV;
     const int li = lane & 31, lh = lane >> 5;
 
-    // element offsets (from the operand base) of the chunks this lane moves
+    // Copy q of a wave moves the 16-byte granules p = 64 (cw PER + q) + lane
+    // of a panel's stage: row r = p / CH, chunk (p % CH) ^ sw(r).
+    // X^T X (panel-blocked Xt, xt_offset; a stage of a panel is a contiguous
+    // BMX x 64 block): with q' = cw PER + q, r = 8 q' + lane / 8 and
+    // sw(r) = (4 (q' & 1) + lane / 16) & 7, so the element offset within the
+    // block is 512 q' plus one of two lane terms by the parity of q'.
+    const int64_t hA = (i0 / BMX) * g.pstride, hB = (j0 / BMX) * g.pstride;
+    const int lo0 = (lane >> 3) * 64 + 8 * ((lane & 7) ^ (lane >> 4));
+    const int lo1 = (lane >> 3) * 64 + 8 * ((lane & 7) ^ (4 + (lane >> 4)));
+    // other products: element offsets from the operand base, rows clamped to the operand
     int64_t offA[PER], offB[PER];
+    if constexpr (EPI != EPI_HESSIAN) {
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int p = (wave * PER + q) * 64 + lane;      // 16-byte granule of the panel slab
-        const int r = p / S::CH;
-        const int c = (p % S::CH) ^ S::sw(r);
-        const int64_t ra = std::min<int64_t>(i0 + r, g.M - 1);
-        const int64_t rb = std::min<int64_t>(j0 + r, g.N - 1);
-        offA[q] = ra * g.lda + 8 * c;
-        offB[q] = rb * g.ldb + 8 * c;
+        for (int q = 0; q < PER; ++q) {
+            const int p = (cw * PER + q) * 64 + lane;
+            const int r = p / S::CH;
+            const int c = (p % S::CH) ^ S::sw(r);
+            const int64_t ra = std::min<int64_t>(i0 + r, g.M - 1);
+            const int64_t rb = std::min<int64_t>(j0 + r, g.N - 1);
+            offA[q] = ra * g.lda + 8 * c;
+            offB[q] = rb * g.ldb + 8 * c;
+        }
     }
     int64_t n1 = split_depth(g) / DKT, nst = n1 + g.K2 / DKT;
     int64_t kb = 0;
@@ -548,6 +570,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
             const int64_t kc = s / 6;
             const int pq = (int)(s - 6 * kc);
             return g.Ap + ((0x120100 >> (4 * pq)) & 15) * g.a_plane + kb + kc * DKT;
+        } else if constexpr (EPI == EPI_HESSIAN) {
+            return A1 + s * (BMX * DKT);
         } else {
             return s < n1 ? A1 + s * DKT : g.A2 + (s - n1) * DKT;
         }
@@ -557,6 +581,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
             const int64_t kc = s / 6;
             const int pq = (int)(s - 6 * kc);
             return g.Bp + ((0x102010 >> (4 * pq)) & 15) * g.b_plane + kb + kc * DKT;
+        } else if constexpr (EPI == EPI_HESSIAN) {
+            return B1 + s * (BMX * DKT);
         } else {
             return s < n1 ? B1 + s * DKT : B2 + (s - n1) * DKT;
         }
@@ -566,8 +592,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     auto load_one = [&](int64_t s, int buf, int q) {
         const bool isa = q < PER;
         const int qq = isa ? q : q - PER;
-        const uint16_t* P = isa ? stage_a(s) + offA[qq] : stage_b(s) + offB[qq];
-        unsigned char* dst = smem + buf * (2 * PANEL) + (isa ? 0 : PANEL) + (wave * PER + qq) * 1024;
+        const uint16_t* P;
+        if constexpr (EPI == EPI_HESSIAN) {
+            // PER is even, so q' and qq have the same parity
+            P = (isa ? stage_a(s) + hA : stage_b(s) + hB) + 512 * (cw * PER + qq) + ((qq & 1) ? lo1 : lo0);
+        } else {
+            P = isa ? stage_a(s) + offA[qq] : stage_b(s) + offB[qq];
+        }
+        unsigned char* dst = smem + buf * (2 * PANEL) + (isa ? 0 : PANEL) + (cw * PER + qq) * 1024;
         __builtin_amdgcn_global_load_lds((const void*)P, (lds_ptr_t)dst, 16, 0, 0);
     };
     auto issue = [&](int64_t s, int buf) {
@@ -636,8 +668,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     // buffer, so the counts (and the waits) are the same on every iteration
     // and the loop has no joins that would force a full lgkmcnt drain.
     if (nst > 0) {
+        if (copier) {
 #pragma unroll
-        for (int s = 0; s < NST; ++s) issue(std::min<int64_t>(s, nst - 1), s);
+            for (int s = 0; s < NST; ++s) issue(std::min<int64_t>(s, nst - 1), s);
+        }
         wait_vmcnt<(NST - 1) * 2 * PER, false>();
         __builtin_amdgcn_s_barrier();
         frags(0, 0, 0);
@@ -667,8 +701,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
                 for (int m = 0; m < NM; ++m) {
                     mfma_one(1, m);
                     if (m < NR) read_one(s + 1, 0, 0, m);
+                    if (copier) {
 #pragma unroll
-                    for (int l = m * NL / NM; l < (m + 1) * NL / NM; ++l) load_one(sl, bl, l);
+                        for (int l = m * NL / NM; l < (m + 1) * NL / NM; ++l) load_one(sl, bl, l);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -868,10 +904,23 @@ int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStr
 
 namespace {
 
-// Xt[c][r] = X[r0 + r][c] for r < nr; entries nr <= r < kt of each Xt row are
-// zeroed (the row stride ldt may be larger; that tail is never read).
+// The transposed chunk Xt (row c of Xt = column c of X) is panel-blocked for
+// the X^T X tiles: rows c of panel c / bm are stored one stage (64 chunk rows)
+// at a time, so element (c, r) sits at
+//   (c / bm) * pstride + (r / 64) * bm * 64 + (c % bm) * 64 + r % 64
+// and one stage of one panel is a contiguous bm x 64 block (32 KB at bm = 256):
+// a tile's 16-byte copies read whole 1 KB runs. Panels are padded to bm rows
+// with zeros, and pstride = bm * (chunk + 64): one spare stage per panel keeps
+// the panels from starting at power-of-two distances, where the same stage of
+// every panel would fall into the same L2 sets.
+__host__ __device__ inline int64_t xt_offset(int64_t c, int64_t r, int bm, int64_t pstride) {
+    return (c / bm) * pstride + (r >> 6) * ((int64_t)bm * 64) + (c % bm) * 64 + (r & 63);
+}
+
+// Xt(c, r) = X[r0 + r][c] for r < nr and c < n; zero for nr <= r < kt or
+// n <= c < npad (grid: npad / 64 x kt / 64).
 __global__ void transpose_rows_kernel(const uint16_t* __restrict__ X, int64_t ldx, int64_t n, int64_t r0,
-                                      int64_t nr, uint16_t* __restrict__ Xt, int64_t ldt, int64_t kt) {
+                                      int64_t nr, uint16_t* __restrict__ Xt, int bm, int64_t pstride, int64_t kt) {
     __shared__ uint16_t tile[64][66];
     const int64_t cb = (int64_t)blockIdx.x * 64, rb = (int64_t)blockIdx.y * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 256 threads: 64 x 4
@@ -882,21 +931,21 @@ __global__ void transpose_rows_kernel(const uint16_t* __restrict__ X, int64_t ld
     __syncthreads();
     for (int y = ty; y < 64; y += 4) {
         const int64_t c = cb + y, r = rb + tx;
-        if (c < n && r < kt) Xt[c * ldt + r] = tile[tx][y];
+        if (r < kt) Xt[xt_offset(c, r, bm, pstride)] = tile[tx][y];
     }
 }
 
-// Xt[c][r] = X[r0 + r][c] for r < nr (zero for nr <= r < kt) with 16-byte
+// Xt(c, r) = X[r0 + r][c] (zero for nr <= r < kt or n <= c) with 16-byte
 // accesses on both sides: a workgroup moves a 64-column strip over TR_ROWS
 // rows of the chunk through a 64 x 64 LDS tile. With dpart, it also adds up
 // the fp64 squares of the strip's values over those rows, one partial per
 // (row group, column) in dpart[blockIdx.y][c] (X is read once for both).
-// Requires n % 8 == 0 and 16-byte aligned rows of X.
+// Requires n % 8 == 0 and 16-byte aligned rows of X; grid x = npad / 64.
 constexpr int TR_ROWS = 1024;
 __global__ __launch_bounds__(256) void transpose_sumsq_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                               int64_t n, int64_t r0, int64_t nr,
-                                                              uint16_t* __restrict__ Xt, int64_t ldt, int64_t kt,
-                                                              double* __restrict__ dpart) {
+                                                              uint16_t* __restrict__ Xt, int bm, int64_t pstride,
+                                                              int64_t kt, double* __restrict__ dpart) {
     __shared__ uint32_t tile[64][33];        // 64 rows x 64 bf16 (as 32 words) + 1 word of padding
     __shared__ double red[32][65];
     const int t = threadIdx.x;
@@ -936,13 +985,13 @@ __global__ __launch_bounds__(256) void transpose_sumsq_kernel(const uint16_t* __
                 const uint32_t word = tile[rw + j][c >> 1];
                 e[j] = (uint16_t)((c & 1) ? (word >> 16) : (word & 0xFFFFu));
             }
-            if (c0 + c < n && rb + rw < kt) {
+            if (rb + rw < kt) {
                 uint4 o;
                 o.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
                 o.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
                 o.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
                 o.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
-                *(uint4*)(Xt + (c0 + c) * ldt + rb + rw) = o;
+                *(uint4*)(Xt + xt_offset(c0 + c, rb + rw, bm, pstride)) = o;
             }
         }
         __syncthreads();
@@ -968,7 +1017,6 @@ __global__ void mirror_diag_blocks_kernel(float* H, int64_t n, int bm) {
     }
 }
 
-// H[i][j] += sum_s part[s][i][j] over the upper triangle, mirrored.
 // H[i][j] += sum over the splits of part[s][i][j] on and above the diagonal
 // (in split order); one row per blockIdx.y. The lower triangle is mirrored
 // once after the last chunk.
@@ -1021,10 +1069,7 @@ constexpr int64_t SLAB_ROWS = 2048;
 constexpr int MAX_SLABS = 256;
 constexpr int64_t CHUNK_ROWS_MAX = 65536;   // calibration rows per transposed chunk
 constexpr int64_t SPLIT_ROWS_MIN = 2048;    // depth of one split of a chunk's XtX launch, at least
-// Row stride of the transposed chunk = its depth + XT_PAD elements: a
-// power-of-two stride (65536 bf16 = 128 KB) would send the 256 rows of a
-// panel slice to the same L2 channel and set.
-constexpr int64_t XT_PAD = 64;
+constexpr int64_t XT_PAD = 64;             // spare chunk rows per Xt panel (xt_offset)
 
 struct XtxPlan {
     int bm, T, nsplit;
@@ -1037,7 +1082,7 @@ struct XtxPlan {
 size_t plan_bytes(const XtxPlan& p, int64_t n) {
     Sizer z;
     if (p.nslab > 1) z.take<double>((size_t)p.nslab * n);
-    z.take<uint16_t>((size_t)n * (p.chunk + XT_PAD));
+    z.take<uint16_t>((size_t)p.T * p.bm * (p.chunk + XT_PAD));
     if (p.nsplit > 1) z.take<float>((size_t)p.nsplit * n * n);
     z.take<double>((size_t)p.ngroups * n);
     return z.bytes();
@@ -1116,7 +1161,8 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
         return PTQ_OK;
     }
 
-    uint16_t* Xt = ar.take<uint16_t>((size_t)n * (p.chunk + XT_PAD));
+    uint16_t* Xt = ar.take<uint16_t>((size_t)p.T * p.bm * (p.chunk + XT_PAD));
+    const int64_t npad = (int64_t)p.T * p.bm, pstride = (int64_t)p.bm * (p.chunk + XT_PAD);
     float* hpart = (p.nsplit > 1) ? ar.take<float>((size_t)p.nsplit * n * n) : nullptr;
     double* dsum = ar.take<double>((size_t)p.ngroups * n);
     const int64_t ntiles = (int64_t)p.T * (p.T + 1) / 2;
@@ -1124,16 +1170,15 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
     for (int64_t r0 = 0; r0 < rows; r0 += p.chunk) {
         const int64_t nr = std::min<int64_t>(p.chunk, rows - r0);
         const int64_t kt = cdiv(nr, 64) * 64;     // contraction depth of this chunk (zero-padded rows)
-        const int64_t ldt = kt + XT_PAD;
         if (vec) {
             const int64_t ng = cdiv(kt, TR_ROWS);
-            hipLaunchKernelGGL(transpose_sumsq_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)ng), dim3(256), 0,
-                               st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt, kt,
+            hipLaunchKernelGGL(transpose_sumsq_kernel, dim3((unsigned)(npad / 64), (unsigned)ng), dim3(256), 0,
+                               st, (const uint16_t*)X, ldx, n, r0, nr, Xt, p.bm, pstride, kt,
                                d ? dsum + gofs * n : (double*)nullptr);
             gofs += ng;
         } else {
-            hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)cdiv(n, 64), (unsigned)(kt / 64)),
-                               dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, ldt, kt);
+            hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)(npad / 64), (unsigned)(kt / 64)),
+                               dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, p.bm, pstride, kt);
         }
         PTQ_LAUNCH_CHECK();
         const bool last = r0 + p.chunk >= rows;
@@ -1144,8 +1189,8 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
             Bf16GemmArgs g{};
             g.A1 = Xt; g.B1 = Xt; g.A2 = nullptr; g.B2 = nullptr;
             g.K1 = kper; g.K2 = 0; g.ktot = kt;
-            g.a_batch_stride = kper; g.b_batch_stride = kper;
-            g.lda = ldt; g.ldb = ldt; g.M = n; g.N = n;
+            g.a_batch_stride = (kper / 64) * p.bm * 64; g.b_batch_stride = g.a_batch_stride;
+            g.pstride = pstride; g.lda = 64; g.ldb = 64; g.M = n; g.N = n;
             g.H = (ns > 1) ? hpart : H;
             g.h_batch_stride = n * n;
             g.ldh = n; g.mirror = (ns == 1 && last) ? 1 : 0; g.T = p.T; g.store_not_add = (ns > 1) ? 1 : 0;
