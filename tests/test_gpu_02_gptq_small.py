@@ -93,6 +93,8 @@ def test_columns_stage_alone_with_oracle_U(gpu):
     (33, 640, 1500, 4, 256, 64, True, "bf16"),
     (17, 256, 512, 4, 32, 32, False, "f32"),
     (5, 1040, 3000, 3, 128, 128, True, "bf16"),       # several U recursion levels, ragged
+    (24, 2600, 3000, 4, 128, 128, True, "bf16"),      # two lazy-batch super-blocks (the second ragged)
+    (20, 2200, 2500, 4, 384, 128, False, "f32"),      # wide groups that do not divide a super-block
 ])
 def test_layer_shapes(gpu, out, n, rows, bits, g, block, act, dtype):
     from post_int4_weight_amd import api
