@@ -118,17 +118,23 @@ __global__ void fill_int_kernel(int* p, int v) { *p = v; }
 
 // Base case on an m x m diagonal block (m <= BASE, m % 4 == 0): the
 // reversed-order Cholesky A = R R^T (R upper) and U = R^-1 in one right-looking
-// sweep over j = m-1 .. 0. Each of the (BASE/4)^2 threads keeps a 4 x 4 tile of the
-// (symmetric) trailing matrix A and of S = I - R[:, >j] U[>j, :] in registers;
-// at step j only column j of A and row j of S go through LDS:
+// sweep over j = m-1 .. 0, with the (symmetric) trailing matrix A and
+// S = I - R[:, >j] U[>j, :]:
 //
 //   R[i][j] = A[i][j] / sqrt(A[j][j])       (i < j)
 //   U[j][c] = S[j][c] / sqrt(A[j][j])       (row j of R U = I, final now)
 //   A[i][k] -= R[i][j] R[k][j],  S[i][c] -= R[i][j] U[j][c]    (i, k < j)
 //
-// so a step is one barrier, three 16-byte LDS reads and 32 FMAs per thread.
-// Outside m the block is padded with the identity. U is written to the block
-// (zeros below its diagonal). Bit 0 of *flag: non-positive pivot; bit 1: NaN.
+// Column k of A is last needed at step k + 1 (it holds column k of R), and
+// column c of S stays the identity's until step c (U[j][c] = 0 for c < j), so
+// one 4 x 4 register tile per thread holds M[i][k] = A[i][k] for k < j and
+// S[i][k] for k >= j: at step j column j turns into the identity's column,
+// and the step's update is the single M[i][k] -= R[i][j] V[k] with
+// V[k] = R[k][j] (k < j) or U[j][k] (k >= j). Only column j of A and row j of
+// S go through LDS, so a step is one barrier, three 16-byte LDS reads and 16
+// FMAs per thread (rows already final skip the update). Outside m the block
+// is padded with the identity. U is written to the block (zeros below its
+// diagonal). Bit 0 of *flag: non-positive pivot; bit 1: NaN.
 __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float* __restrict__ A,
                                                                       float* __restrict__ U, int m, int64_t ld,
                                                                       int* flag) {
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
     const int t = threadIdx.x;
     const int ib = t / TB, kb = t % TB;        // this thread's tile: rows 4*ib.., columns 4*kb..
     const int i0 = 4 * ib, k0 = 4 * kb;
-    float a[4][4], s[4][4];
+    float a[4][4];                             // M: A left of the current column, S from it on
 #pragma unroll
     for (int di = 0; di < 4; ++di)
 #pragma unroll
@@ -146,17 +152,12 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
             const int i = i0 + di, k = k0 + dk;
             const int r = min(min(i, k), m - 1), c = min(max(i, k), m - 1);   // upper triangle only
             a[di][dk] = A[(int64_t)r * ld + c];
-        }
-#pragma unroll
-    for (int di = 0; di < 4; ++di)
-#pragma unroll
-        for (int dk = 0; dk < 4; ++dk) {
-            const int i = i0 + di, k = k0 + dk;
             if (i >= m || k >= m) a[di][dk] = (i == k) ? 1.f : 0.f;
-            s[di][dk] = (i == k) ? 1.f : 0.f;
         }
+    // row BASE - 1 of S is the identity's
     if (kb == TB - 1) *(float4*)&colb[BASE - 1][i0] = make_float4(a[0][3], a[1][3], a[2][3], a[3][3]);
-    if (ib == TB - 1) *(float4*)&rowb[BASE - 1][k0] = make_float4(s[3][0], s[3][1], s[3][2], s[3][3]);
+    if (ib == TB - 1)
+        *(float4*)&rowb[BASE - 1][k0] = make_float4(0.f, 0.f, 0.f, (kb == TB - 1) ? 1.f : 0.f);
     for (int jb = TB - 1; jb >= 0; --jb) {
 #pragma unroll
         for (int dj = 3; dj >= 0; --dj) {
@@ -174,33 +175,39 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
             const float civ[4] = {ci.x, ci.y, ci.z, ci.w};
             const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
             const float rjv[4] = {rj.x, rj.y, rj.z, rj.w};
-            float Ri[4], Rk[4], Uj[4];
+            float Ri[4], V[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 Ri[q] = (i0 + q < j) ? civ[q] * r : 0.f;
-                Rk[q] = (k0 + q < j) ? ckv[q] * r : 0.f;
-                Uj[q] = rjv[q] * r;
+                V[q] = (k0 + q < j) ? ckv[q] * r : rjv[q] * r;
             }
-            if (ib == jb) {
+            if (kb == jb) {   // column j of A is spent: it becomes column j of S (the identity's)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) s[dj][q] = Uj[q];
+                for (int di = 0; di < 4; ++di) a[di][dj] = (i0 + di == j) ? 1.f : 0.f;
+            }
+            if (ib == jb) {   // row j of S is final: U[j][k] for k >= j
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (k0 + q >= j) a[dj][q] = V[q];
             }
             if (i0 < j) {   // rows >= j are final (Ri = 0): whole waves skip the update as j falls
 #pragma unroll
                 for (int di = 0; di < 4; ++di)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        a[di][q] -= Ri[di] * Rk[q];
-                        s[di][q] -= Ri[di] * Uj[q];
-                    }
+                    for (int q = 0; q < 4; ++q) a[di][q] -= Ri[di] * V[q];
             }
             if (j > 0) {   // publish column j-1 of A and row j-1 of S (final after this update)
                 const int djn = (dj + 3) & 3;
                 const int jn = j - 1, jbn = jn >> 2;
                 if (kb == jbn)
                     *(float4*)&colb[jn][i0] = make_float4(a[0][djn], a[1][djn], a[2][djn], a[3][djn]);
-                if (ib == jbn)
-                    *(float4*)&rowb[jn][k0] = make_float4(s[djn][0], s[djn][1], s[djn][2], s[djn][3]);
+                if (ib == jbn) {
+                    // S[jn][k]: the identity's left of column j, M from column j on
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = (k0 + q < j) ? ((k0 + q == jn) ? 1.f : 0.f) : a[djn][q];
+                    *(float4*)&rowb[jn][k0] = make_float4(v[0], v[1], v[2], v[3]);
+                }
             }
         }
     }
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
 #pragma unroll
         for (int dk = 0; dk < 4; ++dk) {
             const int i = i0 + di, k = k0 + dk;
-            if (i < m && k < m) U[(int64_t)i * ld + k] = s[di][dk];
+            if (i < m && k < m) U[(int64_t)i * ld + k] = a[di][dk];
         }
 }
 
