@@ -171,7 +171,11 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
                 if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
                 piv = 1.f;
             }
-            const float r = 1.f / sqrtf(piv);
+            // 1 / sqrt(piv): the hardware reciprocal square root and one Newton
+            // step (within about an ulp, as IEEE sqrt then divide; their dozens
+            // of dependent instructions sat on every step's critical path)
+            const float r0 = __builtin_amdgcn_rsqf(piv);
+            const float r = r0 * fmaf(-0.5f * piv, r0 * r0, 1.5f);
             const float civ[4] = {ci.x, ci.y, ci.z, ci.w};
             const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
             const float rjv[4] = {rj.x, rj.y, rj.z, rj.w};
