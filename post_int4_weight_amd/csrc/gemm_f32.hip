@@ -12,7 +12,10 @@
 // 2 x 2, each wave 64 x 64 = 2 x 2 MFMA 32x32 blocks):
 //
 //  * gemm_f32_direct_kernel (below) for A K-contiguous and K, leading
-//    dimensions a multiple of 4: every product on the hot path;
+//    dimensions a multiple of 4: every product on the hot path. Products
+//    with fewer than 128 such tiles run it on 64 x 64 tiles instead (each
+//    wave one 32 x 32 block), so the small products deep in the U recursion
+//    spread over four times as many CUs;
 //  * gemm_f32_kernel, the general fallback (any layout, any K): K staged
 //    through LDS 32 at a time, double buffered through registers, k-major LDS
 //    tiles (K-contiguous operands transposed while staging) read with one
@@ -231,8 +234,8 @@ constexpr int DNST_LONG = 4;            // ring stages for long contractions
 constexpr int DNST_SHORT = 3;           // K <= 1024: a smaller ring fits three workgroups per CU
 constexpr int SHORT_K = 1024;
 constexpr int DWG = 2;                  // workgroups per CU the kernel is built for
-constexpr int DSTAGE_BYTES = 2 * BM * DBK * 4;   // A and B tiles of one stage
-constexpr int DQ = BM * DBK * 4 / 1024 / 4;     // 1 KB copies per wave per operand per stage
+template <int BT>
+constexpr int DSTAGE_BYTES = 2 * BT * DBK * 4;   // A and B tiles of one stage (BT x BT tiles)
 constexpr int DJ = DBK / 8;                      // 8-deep MFMA steps per stage
 constexpr int DCH = DBK / 4;                     // 16-byte chunks per K-contiguous LDS row
 constexpr int XCDS = 8;                          // accelerator complex dies, one L2 each
@@ -254,9 +257,16 @@ __device__ __forceinline__ void f32_wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool B_KMAJOR, int DNST>
+// BT = 128 (4 waves of 64 x 64 = 2 x 2 MFMA blocks) or 64 (4 waves of one
+// 32 x 32 block each): the small tile quadruples the workgroups of the small
+// products deep in the U recursion, which otherwise run on a few CUs.
+template <bool B_KMAJOR, int DNST, int BT>
 __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
     static_assert(DNST >= 3, "the ring needs three stages");
+    static_assert(BT == 128 || BT == 64, "tile");
+    constexpr int WB = BT / 64;                          // 32 x 32 blocks per wave and dimension
+    constexpr int DQ = BT * DBK * 4 / 1024 / 4;         // 1 KB copies per wave per operand per stage
+    constexpr int SB = DSTAGE_BYTES<BT>;
     // Tile order. blockIdx b runs on XCD b % 8. With at least 8 tile rows,
     // XCD x takes the whole rows x, x + 8, x + 16, ... in row-major order:
     // the tiles one XCD runs side by side share A panels (and B panels across
@@ -275,19 +285,19 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
         tn = blockIdx.x % tiles_n;
     }
     if (g.upper_only && tm > tn) return;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int64_t m0 = tm * BT, n0 = tn * BT;
 
     int64_t kb = 0, ke = g.K;
     if (g.tri == TRI_A_UPPER) kb = m0;
     else if (g.tri == TRI_B_UPPER_NK) kb = n0;
-    else if (g.tri == TRI_B_UPPER_KN) ke = min(g.K, n0 + BN);
+    else if (g.tri == TRI_B_UPPER_KN) ke = min(g.K, n0 + BT);
     kb = (kb / DBK) * DBK;
     const int64_t nst = (ke > kb) ? cdiv(ke - kb, DBK) : 0;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char dsm[];
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int wm = (wave >> 1) * (BT / 2), wn = (wave & 1) * (BT / 2);
     const int li = lane & 31, lh = lane >> 5;
 
     // per-lane global offsets (elements) of the chunks this lane moves, at k = 0
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
             offB[q] = row * g.ldb;
             kcB[q] = 4 * c;
         } else {
-            const int kr = p >> 5, pc = p & 31;
+            const int kr = p / (BT / 4), pc = p % (BT / 4);
             const int c = pc ^ (8 * ((kr >> 2) & 1));
             const int64_t col = min(n0 + 4 * c, g.N - 4);
             offB[q] = col;
@@ -320,8 +330,8 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
 
     auto issue = [&](int64_t s, int buf) {
         const int64_t k0 = kb + s * DBK;
-        unsigned char* sa = dsm + buf * DSTAGE_BYTES;
-        unsigned char* sb = sa + BM * DBK * 4;
+        unsigned char* sa = dsm + buf * SB;
+        unsigned char* sb = sa + BT * DBK * 4;
 #pragma unroll
         for (int q = 0; q < DQ; ++q) {
             const int64_t k = min(k0 + kcA[q], g.K - 4);
@@ -343,35 +353,35 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[WB][WB];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < WB; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < WB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     // fragments of one 8-deep step j: fa[a] = A[row][8j + 4lh .. +3], fb likewise
-    f32x4 fa[2][2], fb[2][2];
+    f32x4 fa[2][WB], fb[2][WB];
     const int aswz = kswz(li);
     auto frags = [&](int64_t s, int j, int slot, bool mask) {
-        const unsigned char* As = dsm + (s % DNST) * DSTAGE_BYTES;
-        const unsigned char* Bs = As + BM * DBK * 4;
+        const unsigned char* As = dsm + (s % DNST) * SB;
+        const unsigned char* Bs = As + BT * DBK * 4;
         const int c = (2 * j + lh) ^ aswz;
 #pragma unroll
-        for (int a = 0; a < 2; ++a) fa[slot][a] = *(const f32x4*)(As + (wm + 32 * a + li) * (DBK * 4) + 16 * c);
+        for (int a = 0; a < WB; ++a) fa[slot][a] = *(const f32x4*)(As + (wm + 32 * a + li) * (DBK * 4) + 16 * c);
         if (!B_KMAJOR) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b) fb[slot][b] = *(const f32x4*)(Bs + (wn + 32 * b + li) * (DBK * 4) + 16 * c);
+            for (int b = 0; b < WB; ++b) fb[slot][b] = *(const f32x4*)(Bs + (wn + 32 * b + li) * (DBK * 4) + 16 * c);
         } else {
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < WB; ++b) {
                 const int n = wn + 32 * b + li;
                 const int pc = (n >> 2) ^ (8 * lh);     // ((k >> 2) & 1) == lh for k = 8j + 4lh + e
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int k = 8 * j + 4 * lh + e;
-                    fb[slot][b][e] = *(const float*)(Bs + k * (BN * 4) + 16 * pc + 4 * (n & 3));
+                    fb[slot][b][e] = *(const float*)(Bs + k * (BT * 4) + 16 * pc + 4 * (n & 3));
                 }
             }
         }
@@ -381,9 +391,9 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
             for (int e = 0; e < 4; ++e) {
                 const bool ok = kbase + e < g.K;
 #pragma unroll
-                for (int a = 0; a < 2; ++a) fa[slot][a][e] = ok ? fa[slot][a][e] : 0.f;
+                for (int a = 0; a < WB; ++a) fa[slot][a][e] = ok ? fa[slot][a][e] : 0.f;
 #pragma unroll
-                for (int b = 0; b < 2; ++b) fb[slot][b][e] = ok ? fb[slot][b][e] : 0.f;
+                for (int b = 0; b < WB; ++b) fb[slot][b][e] = ok ? fb[slot][b][e] : 0.f;
             }
         }
     };
@@ -391,20 +401,23 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < WB; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < WB; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[slot][a][e], fb[slot][b][e], acc[a][b], 0, 0,
                                                                     0);
     };
-    constexpr int NREAD = B_KMAJOR ? 10 : 4;     // LDS reads per fragment set
+    constexpr int NREAD = WB * (B_KMAJOR ? 5 : 2);   // LDS reads per fragment set
+    constexpr int NMF = 4 * WB * WB;                  // MFMAs per step
+    constexpr int NPAIR = NREAD < NMF ? NREAD : NMF;
     auto interleave = [&]() {
 #pragma unroll
-        for (int i = 0; i < NREAD; ++i) {
+        for (int i = 0; i < NPAIR; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16 - NREAD, 0);
+        if constexpr (NMF > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NPAIR, 0);
+        if constexpr (NREAD > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
     };
 
     if (nst > 0) {
@@ -441,12 +454,12 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
     }
 
     // epilogue (same accumulator layout as above)
-    const int mi = (int)min((int64_t)BM, g.M - m0), nj = (int)min((int64_t)BN, g.N - n0);
+    const int mi = (int)min((int64_t)BT, g.M - m0), nj = (int)min((int64_t)BT, g.N - n0);
     float* Ct = g.C + m0 * g.ldc + n0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < WB; ++j) {
             const int jj = wn + 32 * j + li;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -460,29 +473,34 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
         }
 }
 
-template <bool B_KMAJOR, int DNST>
+template <bool B_KMAJOR, int DNST, int BT>
 int launch_direct_ring(const GemmArgs& a, hipStream_t st) {
     static bool ready = false;
     if (!ready) {
-        PTQ_HIP(hipFuncSetAttribute((const void*)gemm_f32_direct_kernel<B_KMAJOR, DNST>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, DNST * DSTAGE_BYTES));
+        PTQ_HIP(hipFuncSetAttribute((const void*)gemm_f32_direct_kernel<B_KMAJOR, DNST, BT>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, DNST * DSTAGE_BYTES<BT>));
         ready = true;
     }
-    const int64_t tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    const int64_t tm = cdiv(a.M, BT), tn = cdiv(a.N, BT);
     const unsigned grid = (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
-    hipLaunchKernelGGL((gemm_f32_direct_kernel<B_KMAJOR, DNST>), dim3(grid), dim3(NT), DNST * DSTAGE_BYTES, st, a,
-                       tm, tn);
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<B_KMAJOR, DNST, BT>), dim3(grid), dim3(NT), DNST * DSTAGE_BYTES<BT>,
+                       st, a, tm, tn);
     PTQ_LAUNCH_CHECK();
     return PTQ_OK;
 }
 
 // Short contractions (the trailing updates) are dominated by the tile's
 // prologue and C read-modify-write: a 3-stage ring (48 KB) lets a third
-// workgroup per CU cover them; long ones keep the deeper ring.
+// workgroup per CU cover them; long ones keep the deeper ring. Products
+// with fewer than SMALL_TILES 128 x 128 tiles run on 64 x 64 tiles.
+constexpr int64_t SMALL_TILES = 128;
 template <bool B_KMAJOR>
 int launch_direct(const GemmArgs& a, hipStream_t st) {
-    return a.K <= SHORT_K ? launch_direct_ring<B_KMAJOR, DNST_SHORT>(a, st)
-                          : launch_direct_ring<B_KMAJOR, DNST_LONG>(a, st);
+    if (cdiv(a.M, BM) * cdiv(a.N, BN) < SMALL_TILES)
+        return a.K <= SHORT_K ? launch_direct_ring<B_KMAJOR, DNST_SHORT, 64>(a, st)
+                              : launch_direct_ring<B_KMAJOR, DNST_LONG, 64>(a, st);
+    return a.K <= SHORT_K ? launch_direct_ring<B_KMAJOR, DNST_SHORT, 128>(a, st)
+                          : launch_direct_ring<B_KMAJOR, DNST_LONG, 128>(a, st);
 }
 
 bool direct_ok(const GemmArgs& a) {

@@ -15,8 +15,9 @@ from gpu_util import announce, rel_fro, to64, zeros_h
 pytestmark = pytest.mark.gpu
 
 
+# below 128 tiles of 128 x 128 the direct kernel runs 64 x 64 tiles; (1700, 1540, 200) has 182
 @pytest.mark.parametrize("M,N,K", [(200, 130, 77), (128, 128, 16), (300, 260, 300), (5, 9, 3), (260, 388, 1000),
-                                   (37, 4, 36)])
+                                   (37, 4, 36), (1700, 1540, 200)])
 @pytest.mark.parametrize("la,lb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_gemm_f32_layouts(gpu, M, N, K, la, lb):
     from post_int4_weight_amd import api
@@ -44,11 +45,11 @@ def test_gemm_f32_layouts(gpu, M, N, K, la, lb):
         assert rel_fro(got.numpy(), want.numpy()) < 1e-5
 
 
+@pytest.mark.parametrize("n,m", [(384, 272), (2048, 1100)])      # 64 x 64 and 128 x 128 tiles
 @pytest.mark.parametrize("tri", [1, 2, 3])
-def test_gemm_f32_triangles(gpu, tri):
+def test_gemm_f32_triangles(gpu, tri, n, m):
     from post_int4_weight_amd import api
-    announce(f"gemm_f32 triangle mode {tri}")
-    n, m = 384, 272
+    announce(f"gemm_f32 triangle mode {tri} n={n} m={m}")
     g = torch.Generator().manual_seed(tri)
     T = torch.triu(torch.randn(n, n, generator=g))
     if tri == 1:      # C[n, m] = T[n, n] X[n, m], A upper
@@ -69,11 +70,12 @@ def test_gemm_f32_triangles(gpu, tri):
     assert rel_fro(C.cpu().double().numpy(), ref.numpy()) < 1e-5
 
 
+@pytest.mark.parametrize("n", [300, 1800])                        # 64 x 64 and 128 x 128 tiles
 @pytest.mark.parametrize("k", [50, 64])
-def test_gemm_f32_upper_only(gpu, k):
+def test_gemm_f32_upper_only(gpu, k, n):
+    """Every entry on or above the diagonal is updated; 128-blocks below it are untouched."""
     from post_int4_weight_amd import api
-    announce(f"gemm_f32 upper_only k={k}")
-    n = 300
+    announce(f"gemm_f32 upper_only k={k} n={n}")
     g = torch.Generator().manual_seed(7)
     P = torch.randn(n, k, generator=g)
     C0 = torch.randn(n, n, generator=g)
@@ -85,11 +87,15 @@ def test_gemm_f32_upper_only(gpu, k):
     torch.cuda.synchronize()
     ref = C0.double() - P.double() @ P.double().T
     got = C.cpu().double()
-    for ti in range(3):
-        for tj in range(3):
+    nb = (n + 127) // 128
+    for ti in range(nb):
+        for tj in range(nb):
             blk = (slice(128 * ti, min(n, 128 * ti + 128)), slice(128 * tj, min(n, 128 * tj + 128)))
-            if ti <= tj:
+            if ti < tj:
                 assert rel_fro(got[blk].numpy(), ref[blk].numpy()) < 1e-5
+            elif ti == tj:
+                up = np.triu(np.ones(got[blk].shape, dtype=bool))
+                assert rel_fro(got[blk].numpy()[up], ref[blk].numpy()[up]) < 1e-5
             else:
                 assert torch.equal(got[blk], C0.double()[blk])
 
