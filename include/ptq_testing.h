@@ -12,7 +12,7 @@
  * skipped per row tile); 2 B upper (layout 0, B[k][j] = 0 for k > j);
  * 3 B upper stored [N][K] (entries with k < j are zero). upper_only: only
  * output tiles on or above the diagonal are written (128 x 128 tiles, or
- * 64 x 64 when the product has fewer than 128 of 128 x 128): every entry
+ * 64 x 64 when the product has fewer than 1024 of 128 x 128): every entry
  * on or above the diagonal is, entries below it only inside diagonal tiles.
  * Device pointers; lda, ldb multiples of 4; asynchronous on `stream`.
  * Returns PTQ_OK, PTQ_EINVAL or PTQ_EHIP.

@@ -13,9 +13,8 @@
 //
 //  * gemm_f32_direct_kernel (below) for A K-contiguous and K, leading
 //    dimensions a multiple of 4: every product on the hot path. Products
-//    with fewer than 128 such tiles run it on 64 x 64 tiles instead (each
-//    wave one 32 x 32 block), so the small products deep in the U recursion
-//    spread over four times as many CUs;
+//    with fewer than 1024 such tiles run it on 64 x 64 tiles instead (each
+//    wave one 32 x 32 block), so they spread over four times as many CUs;
 //  * gemm_f32_kernel, the general fallback (any layout, any K): K staged
 //    through LDS 32 at a time, double buffered through registers, k-major LDS
 //    tiles (K-contiguous operands transposed while staging) read with one
@@ -492,8 +491,11 @@ int launch_direct_ring(const GemmArgs& a, hipStream_t st) {
 // Short contractions (the trailing updates) are dominated by the tile's
 // prologue and C read-modify-write: a 3-stage ring (48 KB) lets a third
 // workgroup per CU cover them; long ones keep the deeper ring. Products
-// with fewer than SMALL_TILES 128 x 128 tiles run on 64 x 64 tiles.
-constexpr int64_t SMALL_TILES = 128;
+// with fewer than SMALL_TILES 128 x 128 tiles run on 64 x 64 tiles: the U
+// recursion's fp32 products (n = 28672: 121.9 ms at a threshold of 128 tiles,
+// 120.7 at 512 or more) and the in-super-block updates of the column stage
+// (60.3 -> 56.5 ms); the larger ones keep the denser tile.
+constexpr int64_t SMALL_TILES = 1024;
 template <bool B_KMAJOR>
 int launch_direct(const GemmArgs& a, hipStream_t st) {
     if (cdiv(a.M, BM) * cdiv(a.N, BN) < SMALL_TILES)

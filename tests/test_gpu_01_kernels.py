@@ -15,9 +15,9 @@ from gpu_util import announce, rel_fro, to64, zeros_h
 pytestmark = pytest.mark.gpu
 
 
-# below 128 tiles of 128 x 128 the direct kernel runs 64 x 64 tiles; (1700, 1540, 200) has 182
+# below 1024 tiles of 128 x 128 the direct kernel runs 64 x 64 tiles; (4200, 4100, 64) has 1089
 @pytest.mark.parametrize("M,N,K", [(200, 130, 77), (128, 128, 16), (300, 260, 300), (5, 9, 3), (260, 388, 1000),
-                                   (37, 4, 36), (1700, 1540, 200)])
+                                   (37, 4, 36), (1700, 1540, 200), (4200, 4100, 64)])
 @pytest.mark.parametrize("la,lb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_gemm_f32_layouts(gpu, M, N, K, la, lb):
     from post_int4_weight_amd import api
@@ -45,7 +45,7 @@ def test_gemm_f32_layouts(gpu, M, N, K, la, lb):
         assert rel_fro(got.numpy(), want.numpy()) < 1e-5
 
 
-@pytest.mark.parametrize("n,m", [(384, 272), (2048, 1100)])      # 64 x 64 and 128 x 128 tiles
+@pytest.mark.parametrize("n,m", [(384, 272), (2048, 1100)])
 @pytest.mark.parametrize("tri", [1, 2, 3])
 def test_gemm_f32_triangles(gpu, tri, n, m):
     from post_int4_weight_amd import api
@@ -70,7 +70,7 @@ def test_gemm_f32_triangles(gpu, tri, n, m):
     assert rel_fro(C.cpu().double().numpy(), ref.numpy()) < 1e-5
 
 
-@pytest.mark.parametrize("n", [300, 1800])                        # 64 x 64 and 128 x 128 tiles
+@pytest.mark.parametrize("n", [300, 1800])
 @pytest.mark.parametrize("k", [50, 64])
 def test_gemm_f32_upper_only(gpu, k, n):
     """Every entry on or above the diagonal is updated; 128-blocks below it are untouched."""
