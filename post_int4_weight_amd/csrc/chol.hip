@@ -226,8 +226,10 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
 
 // GEMMs with all of M, N, K at least this large run on the bf16 MFMA from
 // three-term splits of their operands (fp32 accuracy, gemm_bf16.hip); the
-// smaller ones, deep in the recursion, on the fp32 MFMA GEMM.
-constexpr int64_t SPLIT3_MIN = 2048;
+// smaller ones, deep in the recursion, on the fp32 MFMA GEMM (at n = 8192 its
+// 2048-sized products are faster there: factor 11.3 ms at a threshold of
+// 2048, 10.3 at 3072).
+constexpr int64_t SPLIT3_MIN = 3072;
 
 struct Ctx {
     float* A;      // damped (permuted) H, destroyed
