@@ -505,6 +505,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
             tm = blockIdx.x / g.tiles_n;
             tn = blockIdx.x % g.tiles_n;
         }
+        // B upper triangular [K][N]: a tile's depth grows with its column,
+        // so columns go in descending order and the deepest tiles start first
+        // (the last tiles to start are then the shortest)
+        if (g.tri == TRI_B_UPPER_KN) tn = g.tiles_n - 1 - tn;
         if (g.upper_only && tm > tn) return;
         i0 = tm * BMX;
         j0 = tn * BMX;

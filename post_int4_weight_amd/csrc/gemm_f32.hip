@@ -283,6 +283,10 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
         tm = blockIdx.x / tiles_n;
         tn = blockIdx.x % tiles_n;
     }
+    // B upper triangular [K][N]: a tile's depth grows with its column, so
+    // columns go in descending order and the deepest tiles start first (the
+    // last tiles to start are then the shortest)
+    if (g.tri == TRI_B_UPPER_KN) tn = tiles_n - 1 - tn;
     if (g.upper_only && tm > tn) return;
     const int64_t m0 = tm * BT, n0 = tn * BT;
 
