@@ -491,13 +491,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         j0 = (int64_t)tj * BMX;
         diag = (ti == tj);
     } else if (EPI == EPI_GEMM) {
-        // With at least 8 tile rows, XCD x takes the whole rows x, x + 8, ...
-        // (its tiles share A panels in its L2, and the rows' alternation
-        // balances triangular work over the XCDs); else plain row-major.
+        // With at least 8 tile rows, XCD x takes whole rows (its tiles share
+        // A panels in its L2): its k-th is row 8k + x for even k and
+        // 8k + 7 - x for odd k, a zigzag that balances over the XCDs the
+        // triangular products whose row work falls with the row (A upper,
+        // upper_only). Else plain row-major.
         int64_t tm, tn;
         if (g.tiles_m >= NXCD) {
-            const int64_t x = blockIdx.x % NXCD, i = blockIdx.x / NXCD;
-            tm = x + NXCD * (i / g.tiles_n);
+            const int64_t x = blockIdx.x % NXCD, i = blockIdx.x / NXCD, k = i / g.tiles_n;
+            tm = NXCD * k + ((k & 1) ? NXCD - 1 - x : x);
             tn = i % g.tiles_n;
             if (tm >= g.tiles_m) return;
         } else {

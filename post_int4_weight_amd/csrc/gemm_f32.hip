@@ -267,15 +267,16 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
     constexpr int DQ = BT * DBK * 4 / 1024 / 4;         // 1 KB copies per wave per operand per stage
     constexpr int SB = DSTAGE_BYTES<BT>;
     // Tile order. blockIdx b runs on XCD b % 8. With at least 8 tile rows,
-    // XCD x takes the whole rows x, x + 8, x + 16, ... in row-major order:
-    // the tiles one XCD runs side by side share A panels (and B panels across
-    // its rows) in its own L2, and the rows' alternation keeps the triangular
-    // products (A upper, upper_only), whose work varies by row, balanced over
-    // the XCDs. Fewer rows: plain row-major order over all XCDs.
+    // XCD x takes whole rows in row-major order, its k-th being row 8k + x
+    // for even k and 8k + 7 - x for odd k: the tiles one XCD runs side by
+    // side share A panels (and B panels across its rows) in its own L2, and
+    // the zigzag keeps the triangular products (A upper, upper_only), whose
+    // work falls with the row, balanced over the XCDs. Fewer rows: plain
+    // row-major order over all XCDs.
     int64_t tm, tn;
     if (tiles_m >= XCDS) {
-        const int64_t x = blockIdx.x % XCDS, i = blockIdx.x / XCDS;
-        tm = x + XCDS * (i / tiles_n);
+        const int64_t x = blockIdx.x % XCDS, i = blockIdx.x / XCDS, k = i / tiles_n;
+        tm = XCDS * k + ((k & 1) ? XCDS - 1 - x : x);
         tn = i % tiles_n;
         if (tm >= tiles_m) return;
     } else {
