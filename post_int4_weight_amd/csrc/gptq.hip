@@ -74,22 +74,33 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
                                                           int64_t ngroups, float* __restrict__ gmaxes,
                                                           float* __restrict__ E, int lde,
                                                           float* __restrict__ err2, int64_t nblocks,
-                                                          int* __restrict__ flag) {
+                                                          int* __restrict__ flag, uint64_t gs_lo, uint64_t gs_hi) {
+    // gs_lo / gs_hi: bit j (j < 64 / j - 64) set where a group of g <= B
+    // columns starts at block column j (no bits when groups span blocks)
     constexpr int LPR = B / CPL;          // lanes per row
     constexpr int RPW = NTH / LPR;        // rows per workgroup
     __shared__ float Us[B][B + 4];
-    __shared__ float diag[B];
+    __shared__ float rdiag[B];            // 1 / U[j][j]
 
     const int t = threadIdx.x;
-    // stage U[b0:b0+bc, b0:b0+bc] (upper; zero elsewhere and outside bc)
-    for (int e = t; e < B * B; e += NTH) {
-        const int i = e / B, j = e % B;
-        float v = 0.f;
-        if (i < bc && j < bc && j >= i) v = U[(b0 + i) * n + (b0 + j)];
-        Us[i][j] = v;
+    // stage U[b0:b0+bc, b0:b0+bc] (upper; zero elsewhere and outside bc):
+    // all of this thread's loads in flight before the first LDS store
+    {
+        constexpr int PT = B * B / NTH;
+        float sv[PT];
+#pragma unroll
+        for (int q = 0; q < PT; ++q) {
+            const int e = t + q * NTH, i = e / B, j = e % B;
+            sv[q] = (i < bc && j < bc && j >= i) ? U[(b0 + i) * n + (b0 + j)] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < PT; ++q) {
+            const int e = t + q * NTH;
+            Us[e / B][e % B] = sv[q];
+        }
     }
     __syncthreads();
-    if (t < B) diag[t] = (t < bc) ? Us[t][t] : 1.f;
+    if (t < B) rdiag[t] = 1.f / ((t < bc) ? Us[t][t] : 1.f);
     __syncthreads();
 
     const int lr = t % LPR;                       // lane within row
@@ -108,6 +119,7 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
     const int lane = t & 63;
     const int row_lane0 = lane - lr;              // first lane of this row in the wave
     float scale = 0.f;
+    float rscale = 0.f;     // 1 / scale (0 while scale is 0)
     float gmax = 0.f;       // symmetric: the group's max |w| (scale = gmax / qmax); zero-point: hi
     float glo = 0.f;        // zero-point: lo
     float zero = 0.f;       // zero-point: the group's zero
@@ -139,6 +151,7 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             glo = mn;
             if (ZP) zp_params(mx, mn, qmax, scale, zero);
             else scale = mx / qmax;
+            rscale = (scale > 0.f) ? 1.f / scale : 0.f;
             if (live && lr == 0) {
                 scales[r * ngroups + b0 / g] = scale;
                 gmaxes[2 * (r * ngroups + b0 / g)] = mx;
@@ -150,13 +163,14 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             gmax = gmaxes[2 * (r * ngroups + b0 / g)];
             glo = gmaxes[2 * (r * ngroups + b0 / g) + 1];
             if (ZP) zero = (float)zeros[r * ngroups + b0 / g];
+            rscale = (scale > 0.f) ? 1.f / scale : 0.f;
         }
     }
 
 #pragma unroll
     for (int j = 0; j < B; ++j) {
         if (j < bc) {
-            if (g <= B && (j % g) == 0) {
+            if (((j < 64 ? (gs_lo >> (j & 63)) : (gs_hi >> (j & 63))) & 1) != 0) {
                 // the group [j, j+g) lies inside this block: lanes whose columns fall in it
                 float loc = 0.f, lmn = 0.f;
 #pragma unroll
@@ -180,6 +194,7 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
                 glo = lmn;
                 if (ZP) zp_params(loc, lmn, qmax, scale, zero);
                 else scale = loc / qmax;
+                rscale = (scale > 0.f) ? 1.f / scale : 0.f;
                 if (live && lr == 0) {
                     scales[r * ngroups + (b0 + j) / g] = scale;
                     if (ZP) zeros[r * ngroups + (b0 + j) / g] = (int8_t)(int)zero;
@@ -187,12 +202,13 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             }
             // round this lane's copy of column j (the owner's copy is the real one).
             // The rounding decision is the fp64 one, x / (gmax / qmax) in double:
-            // the fp32 quotient is within 2 ulp of it, so only quotients that
-            // close to a half-integer are recomputed in fp64.
+            // the fp32 x * (1 / scale) is within 3 ulp of it, so only quotients
+            // that close to a half-integer (TIE_BAND, far wider) are recomputed
+            // in fp64.
             const float x = w[j % CPL];
             float q = 0.f;
             if (scale > 0.f) {
-                const float t = x / scale;
+                const float t = x * rscale;
                 float rq = rintf(t);
                 if (fabsf(fabsf(t - rq) - 0.5f) < TIE_BAND) {
                     const double s64 = ZP ? ((double)gmax - (double)glo) / (double)qmax : (double)gmax / (double)qmax;
@@ -200,14 +216,13 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
                 }
                 q = ZP ? fminf(fmaxf(rq + zero, 0.f), qmax) : fminf(fmaxf(rq, -qmax - 1.f), qmax);
             }
-            const float e = (x - (q - zero) * scale) / diag[j];
+            const float e = (x - (q - zero) * scale) * rdiag[j];
             const int owner = j / CPL;
             const float eb = __shfl(e, row_lane0 + owner, 64);
-            if (lr == owner) {
-                cq[j % CPL] = q;
-                ce[j % CPL] = e;
-                e2 = fmaf(e, e, e2);
-            }
+            const bool own = lr == owner;
+            cq[j % CPL] = own ? q : cq[j % CPL];
+            ce[j % CPL] = own ? e : ce[j % CPL];
+            e2 = own ? fmaf(e, e, e2) : e2;
             const float4 u0 = *(const float4*)&Us[j][c0];
             const float4 u1 = *(const float4*)&Us[j][c0 + 4];
             w[0] = fmaf(-eb, u0.x, w[0]);
@@ -346,9 +361,12 @@ int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float q
         for (int64_t b0 = s0; b0 < s1; b0 += B) {
             const int bc = (int)std::min<int64_t>(B, s1 - b0);
             prof_begin(PROF_BLOCK_LOOP, st);
+            uint64_t gs[2] = {0, 0};   // group starts inside the block (groups of g <= B)
+            if (g <= B)
+                for (int j = 0; j < bc; j += g) gs[j >> 6] |= (uint64_t)1 << (j & 63);
             hipLaunchKernelGGL((gptq_block_kernel<B, ZP>), dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc, g,
                                qmax, perm, codes, scales, zeros, ngroups, gmaxes, E + (b0 - s0), (int)SB, err2,
-                               nblocks, flag);
+                               nblocks, flag, gs[0], gs[1]);
             prof_end(PROF_BLOCK_LOOP, st);
             PTQ_LAUNCH_CHECK();
             const int64_t b1 = b0 + bc;
