@@ -5,9 +5,11 @@
 //
 // Three uses, selected by the epilogue:
 //  * the proxy Hessian H (+)= X^T X ("GPTQ versus AWQ objectives", "A strong
-//    answer"), run on a transposed chunk of the calibration rows, Xt [in,
-//    rows], with A = B = Xt: only tiles on or above the diagonal are
-//    computed; the tile is added into H (fp32) and, on request, mirrored;
+//    answer"), run on a transposed, panel-blocked chunk of the calibration
+//    rows (xt_offset) with A = B = Xt: only tiles on or above the diagonal
+//    are computed; the tile is added into H (fp32) and, on request,
+//    mirrored, or, when a chunk is split over depth (grid.y), stored into the
+//    split's own partial H;
 //  * AWQ's calibration output error ||X dW^T||^2 (same page, AWQ paragraph),
 //    with A = X [rows, in] and B = dW [out, in] split into a bf16 high part and
 //    a bf16 residual (dW = hi + lo to ~16 significant bits): the K loop runs
@@ -28,9 +30,11 @@
 // fetches are free of bank conflicts.
 //
 // Workgroup order is XCD-aware (blockIdx b runs on XCD b % 8): Hessian tiles
-// go in rounds of 16 x 16 super-blocks split into one 4 x 8 sub-block per XCD
-// (see hessian_tile); AWQ tiles in contiguous runs per XCD.
+// go in rounds of 16 x 16 super-blocks dealt evenly over the XCDs (see
+// hessian_tile); GEMM tile rows go to the XCDs in a zigzag; AWQ tiles in
+// contiguous runs per XCD.
 #include "common.hpp"
+#include "tile_order.hpp"
 
 #include <algorithm>
 
@@ -50,67 +54,10 @@ __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + 16 * (c ^ (
 template <int BMX>
 constexpr int smem_bytes() { return 4 * BMX * ROWB; }   // A and B, two stages each
 
-// Hessian tiles (upper triangle of a T x T tile grid) in rounds of 256
-// workgroups; workgroup b runs on XCD b % 8 and the XCD with the most tiles
-// sets the launch time, so every round deals its tiles evenly over the XCDs.
-// Round r is the r-th SB x SB super-block (P <= Q, row-major), cut into eight
-// 4 x 8 sub-blocks (rows 4 (s / 2).., columns 8 (s % 2)..). Its v valid tiles
-// (inside the grid, on or above the diagonal) are listed sub-block by
-// sub-block, row-major inside each, and XCD x takes the x-th run of
-// ceil(v / 8) of them. A full off-diagonal super-block gives each XCD one
-// whole sub-block: its 32 tiles read 12 panels through the XCD's own L2, and
-// the 256 tiles of the round, which start together and move through k
-// together, read 32 panels between them, so the die-shared last-level cache
-// serves most of what the L2s miss. On a diagonal super-block the sub-blocks
-// go in the order (0, 2, 1, 3, 4..7), left triangle, right square, right
-// triangle, so that each XCD's run of 17 stays compact. Slots past a run
-// return at once.
-constexpr int SB = 16;
-__host__ __device__ inline int64_t hessian_rounds(int T) {
-    const int64_t nb = cdiv(T, SB);
-    return nb * (nb + 1) / 2;
-}
-// valid tiles of row ti among the 8 columns from c0
-__host__ __device__ inline int hessian_row_tiles(int ti, int c0, int T) {
-    if (ti >= T) return 0;
-    const int hi = c0 + 8 < T ? c0 + 8 : T, lo = c0 > ti ? c0 : ti;
-    return hi > lo ? hi - lo : 0;
-}
-// valid tiles of super-block (P, Q)
-__host__ __device__ inline int hessian_round_tiles(int P, int Q, int T) {
-    int v = 0;
-    for (int s = 0; s < 8; ++s)
-        for (int a = 0; a < 4; ++a) v += hessian_row_tiles(SB * P + 4 * (s >> 1) + a, SB * Q + 8 * (s & 1), T);
-    return v;
-}
-__host__ __device__ inline bool hessian_tile(int64_t b, int T, int& ti, int& tj) {
-    const int nb = (int)cdiv(T, SB);
-    int64_t r = b / 256;
-    const int w = (int)(b % 256), x = w % NXCD, i = w / NXCD;
-    int P = 0;
-    while (r >= nb - P) {
-        r -= nb - P;
-        ++P;
-    }
-    const int Q = P + (int)r;
-    const int v = hessian_round_tiles(P, Q, T), per = (v + NXCD - 1) / NXCD;
-    int c = x * per + i;
-    if (i >= per || c >= v) return false;
-    for (int k = 0; k < 8; ++k) {
-        const int s = (k == 1) ? 2 : (k == 2) ? 1 : k;
-        const int c0 = SB * Q + 8 * (s & 1);
-        for (int a = 0; a < 4; ++a) {
-            const int row = SB * P + 4 * (s >> 1) + a, m = hessian_row_tiles(row, c0, T);
-            if (c < m) {
-                ti = row;
-                tj = (c0 > row ? c0 : row) + c;
-                return true;
-            }
-            c -= m;
-        }
-    }
-    return false;
-}
+using tile_order::SB;
+using tile_order::hessian_rounds;
+using tile_order::hessian_round_tiles;
+using tile_order::hessian_tile;
 
 struct Bf16GemmArgs {
     // operand segments: k in [0, K1) uses (A1, B1); k in [K1, K1 + K2) uses (A2, B2) at k - K1
