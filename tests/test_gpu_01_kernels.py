@@ -102,7 +102,7 @@ def test_gemm_f32_upper_only(gpu, k, n):
 
 @pytest.mark.parametrize("rows,n,dtype", [(1000, 520, "bf16"), (2048, 512, "f32"), (3000, 2056, "bf16"),
                                           (32768, 1024, "bf16"), (70000, 256, "bf16"), (40000, 640, "bf16"),
-                                          (64, 8, "bf16")])
+                                          (64, 8, "bf16"), (1500, 300, "bf16")])     # in % 8 != 0: scalar transpose
 def test_hessian_vs_oracle(gpu, rows, n, dtype):
     """H relative Frobenius error <= 1e-5, exact symmetry, d to fp64 rounding."""
     import inputs
@@ -110,6 +110,11 @@ def test_hessian_vs_oracle(gpu, rows, n, dtype):
     announce(f"hessian rows={rows} n={n} {dtype}")
     W, X = inputs.custom(8, n, rows, seed=rows + n, dtype=dtype, device="cpu")
     Xd = X.to(gpu)
+    if n % 8:
+        # rows padded to 16 bytes (the ABI's ldx rule); in % 8 != 0 takes the scalar transpose
+        Xp = torch.zeros(rows, (n + 7) // 8 * 8, dtype=Xd.dtype, device=gpu)
+        Xp[:, :n] = Xd
+        Xd = Xp[:, :n]
     H, d = zeros_h(n, gpu)
     api.hessian_accumulate(H, d, Xd)
     torch.cuda.synchronize()
