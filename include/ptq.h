@@ -133,10 +133,13 @@ int gptq_inverse_factor(const float* H, const double* d, int64_t in, double damp
  * clip(round_half_even(w / scale), -qmax-1, qmax) (scale 0 gives code 0);
  * err = (w - code*scale) / U_jj is subtracted from the later columns through
  * row j of U. Updates are batched over blocks of `block_size` columns (the
- * page's lazy batch): in-block updates in registers, then one GEMM
- * W_cur[:, b1:] -= E U[b0:b1, b1:] per block (fp32 MFMA, or for large ones
- * bf16 MFMAs on three-term bf16 splits of E and U at fp32 accuracy); the
- * arithmetic is the same up to the order of the fp32 sums.
+ * page's lazy batch) and again over 2048-column super-blocks: in-block
+ * updates in registers, then W_cur[:, b1:s1] -= E U[b0:b1, b1:s1] for the
+ * rest of the block's super-block [s0, s1) (fp32 MFMA), and after each
+ * super-block one GEMM W_cur[:, s1:] -= E U[s0:s1, s1:] with K = s1 - s0
+ * (bf16 MFMAs on three-term bf16 splits of E and U at fp32 accuracy when
+ * large, else fp32 MFMA); the arithmetic is the same up to the order of the
+ * fp32 sums.
  *
  * W (not modified) in ORIGINAL column order; U from gptq_inverse_factor (in
  * the processing basis); perm as returned there (NULL = identity).
