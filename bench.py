@@ -47,7 +47,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "xtx_gemm_down_proj_traffic.md")
-TRAFFIC_SOURCES = ["post_int4_weight_amd/csrc/gemm_bf16.hip"]
+TRAFFIC_SOURCES = ["post_int4_weight_amd/csrc/gemm_bf16.hip", "post_int4_weight_amd/csrc/tile_order.hpp"]
 
 
 def kernel_source_digest() -> str:
