@@ -29,6 +29,7 @@ int launch_awq_error_gemm(const uint16_t* X, int64_t ldx, int64_t rows, int64_t 
 namespace {
 
 constexpr double MEAN_ABS_FLOOR = 1e-12;
+constexpr int AWQ_ROWS = 2;   // rows per wave of the batched search kernel
 
 // m_j (+)= sum over a slab of rows of |x_ij| (fp64); slabs reduced later.
 template <typename T>
@@ -64,11 +65,15 @@ __global__ void mean_abs_finish_kernel(const double* part, int nslab, int64_t n,
 }
 
 // s[a][j] = m_j ^ alpha_a in fp64 (the rounding decisions below are taken in
-// fp64, the precision of the pages' NumPy reference)
-__global__ void scales_kernel(const double* m, int64_t n, const float* alphas, int na, double* s) {
+// fp64, the precision of the pages' NumPy reference), and 1 / s[a][j]
+__global__ void scales_kernel(const double* m, int64_t n, const float* alphas, int na, double* s, double* rs) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int a = blockIdx.y;
-    if (c < n && a < na) s[(int64_t)a * n + c] = pow(m[c], (double)alphas[a]);
+    if (c < n && a < na) {
+        const double v = pow(m[c], (double)alphas[a]);
+        s[(int64_t)a * n + c] = v;
+        rs[(int64_t)a * n + c] = 1.0 / v;
+    }
 }
 
 __global__ void s_to_f32_kernel(const double* s64, int64_t n, float* s) {
@@ -134,6 +139,120 @@ __global__ __launch_bounds__(256) void awq_quant_kernel(const T* __restrict__ W,
         }
     }
     if (scales && lane == 0) scales[r * ngroups + grp] = (float)scale;
+}
+
+// Distance from a half-integer below which the product w s (1/scale) is
+// re-decided by the division: that product lies within 2^-52 relative of the
+// exact quotient, |quotient| <= 128 for bits <= 8, so 1e-12 covers it.
+constexpr double TIE_EPS = 1e-12;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Search-mode RTN for every alpha in one pass over W. Each lane owns 8
+// consecutive columns (one 16-byte load of bf16 W), L = g/8 lanes form a
+// group and a wave covers 64/L groups of R rows. W stays in registers across
+// the alpha loop, so only s and 1/s are re-read (from L2), and every store is
+// 16 bytes. The decisions are those of awq_group: the group max of |w s| and
+// scale = max / qmax in fp64, and q = rint(w s / scale), taken here as
+// rint((w s) (1/scale)) unless that product lies within TIE_EPS of a
+// half-integer, where the exact division decides. dW = w - q scale (1/s)
+// differs from w - q scale / s by an fp64 rounding, far below its bf16
+// hi + lo representation.
+template <typename T, int L, int R>
+__global__ __launch_bounds__(256) void awq_dw_batch_kernel(const T* __restrict__ W, int64_t ldw, int64_t out,
+                                                           int64_t n, float qmax, const double* __restrict__ s_all,
+                                                           const double* __restrict__ rs_all, int na,
+                                                           uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+    constexpr int COLS = 512;   // columns per wave: 64 lanes x 8
+    const int lane = threadIdx.x & 63;
+    const int64_t csets = cdiv(n, (int64_t)COLS);
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t r0 = (wid / csets) * R;
+    if (r0 >= out) return;   // whole waves
+    const int64_t c = (wid % csets) * COLS + (int64_t)lane * 8;
+    const bool live = c < n;   // n is a multiple of 8: a lane is all in or all out
+    const double qm = (double)qmax;
+    float wv[R][8];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (live && r0 + j < out) {
+            load8<T>(W + (r0 + j) * ldw + c, wv[j]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) wv[j][k] = 0.0f;
+        }
+    }
+    for (int a = 0; a < na; ++a) {
+        double sv[8], rv[8];
+        if (live) {
+            const double2* sp = reinterpret_cast<const double2*>(s_all + (int64_t)a * n + c);
+            const double2* rp = reinterpret_cast<const double2*>(rs_all + (int64_t)a * n + c);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const double2 x = sp[k], y = rp[k];
+                sv[2 * k] = x.x; sv[2 * k + 1] = x.y;
+                rv[2 * k] = y.x; rv[2 * k + 1] = y.y;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sv[k] = rv[k] = 0.0;
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int64_t r = r0 + j;
+            double mx = 0.0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) mx = fmax(mx, fabs((double)wv[j][k] * sv[k]));
+#pragma unroll
+            for (int off = L / 2; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off, 64));
+            const double scale = mx / qm;
+            const double rsc = scale > 0.0 ? 1.0 / scale : 0.0;
+            uint32_t hp[4], lp[4];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const double w = (double)wv[j][k];
+                const double ws = w * sv[k];
+                const double t = ws * rsc;
+                double q = rint(t);
+                const double u = fabs(t);
+                if (fabs(u - floor(u) - 0.5) < TIE_EPS && scale > 0.0) q = rint(ws / scale);
+                q = fmin(fmax(q, -qm - 1.0), qm);
+                const float dw = (float)(w - (q * scale) * rv[k]);
+                const uint32_t h = float_to_bf16_bits(dw);
+                const uint32_t l = float_to_bf16_bits(dw - bf16_bits_to_float((uint16_t)h));
+                if (k & 1) {
+                    hp[k >> 1] |= h << 16;
+                    lp[k >> 1] |= l << 16;
+                } else {
+                    hp[k >> 1] = h;
+                    lp[k >> 1] = l;
+                }
+            }
+            if (live && r < out) {
+                const int64_t o = (int64_t)a * out * n + r * n + c;
+                *reinterpret_cast<uint4*>(hi + o) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+                *reinterpret_cast<uint4*>(lo + o) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+            }
+        }
+    }
 }
 
 // fp32 path: dW as fp32 for one alpha (no split)
@@ -237,6 +356,7 @@ size_t awq_ws_bytes(int64_t out, int64_t n, int64_t rows, int n_alpha) {
     z.take<double>((size_t)l.nslab * n);        // column |x| partials
     z.take<double>((size_t)n);                  // m
     z.take<double>((size_t)n_alpha * n);        // s per alpha (fp64)
+    z.take<double>((size_t)n_alpha * n);        // 1 / s per alpha
     z.take<float>((size_t)n_alpha);             // alphas (device copy)
     z.take<double>((size_t)n_alpha);            // err
     // bf16 path: hi + lo for every alpha, one partial per tile and alpha
@@ -261,6 +381,7 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
     double* cpart = ar.take<double>((size_t)l.nslab * n);
     double* m = ar.take<double>((size_t)n);
     double* s_all = ar.take<double>((size_t)n_alpha * n);
+    double* rs_all = ar.take<double>((size_t)n_alpha * n);
     float* al_dev = ar.take<float>((size_t)n_alpha);
     double* err = ar.take<double>((size_t)n_alpha);
     const int64_t ngroups = cdiv(n, g);
@@ -278,7 +399,7 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
         E = ar.take<float>((size_t)rows * out);
         partial = ar.take<double>((size_t)cdiv(rows * out, F32_SLICE) + 1);
     }
-    if (!cpart || !m || !s_all || !al_dev || !err || !partial || (bf && (!hi || !lo)) || (!bf && (!dW || !E))) {
+    if (!cpart || !m || !s_all || !rs_all || !al_dev || !err || !partial || (bf && (!hi || !lo)) || (!bf && (!dW || !E))) {
         set_error("awq_search_alpha: workspace of %zu bytes, %zu needed", ws_bytes,
                   awq_ws_bytes(out, n, rows, n_alpha));
         return PTQ_EWORKSPACE;
@@ -298,13 +419,38 @@ int run_awq(const void* W, int w_dtype, int64_t out, int64_t n, int64_t ldw, con
         hipLaunchKernelGGL(mean_abs_finish_kernel, dim3(1), dim3(256), 0, st, cpart, (int)l.nslab, n, rows, m);
         PTQ_LAUNCH_CHECK();
         hipLaunchKernelGGL(scales_kernel, dim3((unsigned)cdiv(n, 256), (unsigned)n_alpha), dim3(256), 0, st, m, n,
-                           al_dev, n_alpha, s_all);
+                           al_dev, n_alpha, s_all, rs_all);
         PTQ_LAUNCH_CHECK();
     }
 
     if (bf) {
         const int64_t nth = cdiv(out * ngroups * n_alpha, 4) * 256;   // one wave per (alpha, row, group)
-        if (w_dtype == PTQ_BF16)
+        const int wbytes = w_dtype == PTQ_BF16 ? 2 : 4;
+        const bool vec = g % 8 == 0 && g >= 32 && g <= 512 && (g & (g - 1)) == 0 && n % 8 == 0 &&
+                         (ldw * wbytes) % 16 == 0 && ((uintptr_t)W & 15) == 0;
+        if (vec) {
+            constexpr int R = AWQ_ROWS;
+            const int64_t waves = cdiv(out, (int64_t)R) * cdiv(n, (int64_t)512);
+            const dim3 grid((unsigned)cdiv(waves, 4));
+#define PTQ_AWQ_VEC(T, LL)                                                                                          \
+    hipLaunchKernelGGL((awq_dw_batch_kernel<T, LL, R>), grid, dim3(256), 0, st, (const T*)W, ldw, out, n, qmax,   \
+                       s_all, rs_all, n_alpha, hi, lo)
+#define PTQ_AWQ_VEC_T(T)              \
+    switch (g / 8) {                  \
+        case 4: PTQ_AWQ_VEC(T, 4); break;   \
+        case 8: PTQ_AWQ_VEC(T, 8); break;   \
+        case 16: PTQ_AWQ_VEC(T, 16); break; \
+        case 32: PTQ_AWQ_VEC(T, 32); break; \
+        default: PTQ_AWQ_VEC(T, 64); break; \
+    }
+            if (w_dtype == PTQ_BF16) {
+                PTQ_AWQ_VEC_T(uint16_t)
+            } else {
+                PTQ_AWQ_VEC_T(float)
+            }
+#undef PTQ_AWQ_VEC_T
+#undef PTQ_AWQ_VEC
+        } else if (w_dtype == PTQ_BF16)
             hipLaunchKernelGGL(awq_quant_kernel<uint16_t>, dim3((unsigned)cdiv(nth, 256)), dim3(256), 0, st,
                                (const uint16_t*)W, ldw, out, n, g, qmax, s_all, n_alpha, hi, lo, (int8_t*)nullptr,
                                (float*)nullptr, ngroups);

@@ -27,17 +27,21 @@ def _compare(res, ref, alphas):
 
 
 # n = 1056 (a multiple of 32, not of 64) takes the 32-deep ring of the direct
-# kernel; 520 the register-staged kernel; 1024 the 64-deep ring
-@pytest.mark.parametrize("dtype,out,n,rows", [("f32", 256, 512, 2048), ("bf16", 300, 1024, 1000),
-                                              ("bf16", 128, 520, 700), ("bf16", 260, 1056, 600)])
-def test_awq_small(gpu, dtype, out, n, rows):
+# kernel; 520 the register-staged kernel; 1024 the 64-deep ring. Group sizes
+# 32..512 take the batched 8-columns-per-lane search kernel (ragged last
+# groups at n = 520, 1056, 776, 1096), g = 24 the one-wave-per-group one.
+@pytest.mark.parametrize("dtype,out,n,rows,g", [("f32", 256, 512, 2048, 128), ("bf16", 300, 1024, 1000, 128),
+                                                ("bf16", 128, 520, 700, 128), ("bf16", 260, 1056, 600, 128),
+                                                ("bf16", 201, 776, 500, 32), ("bf16", 96, 1536, 400, 512),
+                                                ("bf16", 130, 1096, 300, 64), ("bf16", 70, 960, 300, 24)])
+def test_awq_small(gpu, dtype, out, n, rows, g):
     from post_int4_weight_amd import api
-    announce(f"awq {dtype} out={out} n={n} rows={rows}")
+    announce(f"awq {dtype} out={out} n={n} rows={rows} g={g}")
     W, X = inputs.custom(out, n, rows, seed=out + rows, dtype=dtype)
     alphas = list(inputs.AWQ_ALPHAS)
-    res = api.awq_search_alpha(W.to(gpu), X.to(gpu), alphas, bits=4, group_size=128)
+    res = api.awq_search_alpha(W.to(gpu), X.to(gpu), alphas, bits=4, group_size=g)
     torch.cuda.synchronize()
-    ref = oracle.awq_search(to64(W), to64(X), alphas, bits=4, g=128)
+    ref = oracle.awq_search(to64(W), to64(X), alphas, bits=4, g=g)
     _compare(res, ref, alphas)
 
 
