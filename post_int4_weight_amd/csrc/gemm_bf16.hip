@@ -79,8 +79,9 @@ struct Bf16GemmArgs {
     double* partial;           // [gridDim.y][tiles]
     int64_t tiles_n, ntiles;
     // EPI_GEMM (fp32 GEMM from three-term bf16 splits): A and B are three
-    // planes each (hi, mid, lo; plane strides a_plane, b_plane elements), K1
-    // the padded depth; C = alpha * sum of the six significant plane products
+    // planes each (hi, mid, lo; plane strides a_plane, b_plane elements),
+    // panel-blocked like the X^T X operands (split3_offset, pstride), K1 the
+    // padded depth; C = alpha * sum of the six significant plane products
     // (+ C when beta_one), with GemmArgs' tri / upper_only meaning.
     const uint16_t* Ap; const uint16_t* Bp;
     int64_t a_plane, b_plane;
@@ -434,11 +435,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     // the copies, so a copy that stalls at issue holds one of the SIMD's two
     // waves while the other keeps the MFMA pipe busy (2% on the down_proj
     // shape against copies from every wave).
-    constexpr int CWV = (EPI == EPI_HESSIAN) ? NW / 2 : NW;   // waves that issue copies
+    constexpr bool BLK = EPI == EPI_HESSIAN || EPI == EPI_GEMM;   // panel-blocked operands
+    // waves that issue copies: half of them for X^T X; all of them for the
+    // split planes (there half measured 9% slower: 124 vs 114 ms for the U
+    // of n = 28672, against 110.5 ms with all eight)
+    constexpr int CWV = (EPI == EPI_HESSIAN) ? NW / 2 : NW;
     constexpr int PER = BMX * S::CH / (64 * CWV);      // copies per copying wave per panel per stage
     constexpr int PANEL = BMX * ROWB;                  // bytes of one operand panel per stage
     static_assert(NST >= 2 && KSUB % 2 == 0 && NM >= NR && PER >= 1, "pipeline shape");
-    static_assert(EPI != EPI_HESSIAN || (DKT == 64 && PER % 2 == 0), "X^T X copy layout");
+    static_assert(!BLK || (DKT == 64 && PER % 2 == 0), "panel-blocked copy layout");
     int64_t i0, j0, L = 0;
     bool diag = false;
     if (EPI == EPI_HESSIAN) {
@@ -485,8 +490,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int t = threadIdx.x;
-    // X^T X keeps the wave index in an SGPR (scalar copy addressing and branch)
-    const int lane = t & 63, wave = (EPI == EPI_HESSIAN) ? __builtin_amdgcn_readfirstlane(t >> 6) : t >> 6;
+    // panel-blocked operands keep the wave index in an SGPR (scalar copy addressing and branch)
+    const int lane = t & 63, wave = BLK ? __builtin_amdgcn_readfirstlane(t >> 6) : t >> 6;
     const int wm = (wave >> 1) * WTL::TM, wn = (wave & 1) * WTL::TN;
     const int cw = wave % CWV;                           // copy slot of this wave
     const bool copier = CWV == NW || wave < CWV;
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(g.B1 + (int64_t)blockIdx.y * g.b_batch_stride + (EPI == EPI_HESSIAN ? hB : 0)), (short)0, left, 0x00020000);
     unsigned vo00 = 0, vo01 = 0, vo10 = 0, vo11 = 0;
-    if constexpr (EPI == EPI_HESSIAN) {
+    if constexpr (BLK) {
         const unsigned cb = (unsigned)(cw * PER) * 1024u;
         vo00 = 2u * lo0 + cb;
         vo10 = 2u * lo1 + cb;
@@ -520,7 +525,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     }
     // other products: element offsets from the operand base, rows clamped to the operand
     int64_t offA[PER], offB[PER];
-    if constexpr (EPI != EPI_HESSIAN) {
+    if constexpr (!BLK) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int p = (cw * PER + q) * 64 + lane;
@@ -543,25 +548,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         else if (g.tri == TRI_B_UPPER_KN) ke = std::min<int64_t>(g.K1, j0 + BMX);
         nst = (ke > kb) ? 6 * ((ke - kb) / DKT) : 0;
     }
+    // EPI_GEMM: stage s of the tile's A (or B) panel, one contiguous
+    // BMX x DKT block of a plane; plane pairs (A, B) by s % 6: hi.hi,
+    // hi.mid, mid.hi, hi.lo, lo.hi, mid.mid
+    auto gemm_block = [&](int64_t s, bool isa) -> const uint16_t* {
+        const int si = (int)s, kc = si / 6, pq = si - 6 * kc;
+        const int pl = isa ? ((0x120100 >> (4 * pq)) & 15) : ((0x102010 >> (4 * pq)) & 15);
+        return (isa ? g.Ap + pl * g.a_plane + hA : g.Bp + pl * g.b_plane + hB) +
+               (kb / DKT + kc) * (int64_t)(BMX * DKT);
+    };
     // operand bases of stage s
     auto stage_a = [&](int64_t s) -> const uint16_t* {
-        if constexpr (EPI == EPI_GEMM) {
-            // plane pairs (A, B): hi.hi, hi.mid, mid.hi, hi.lo, lo.hi, mid.mid
-            const int64_t kc = s / 6;
-            const int pq = (int)(s - 6 * kc);
-            return g.Ap + ((0x120100 >> (4 * pq)) & 15) * g.a_plane + kb + kc * DKT;
-        } else if constexpr (EPI == EPI_HESSIAN) {
+        if constexpr (EPI == EPI_HESSIAN || EPI == EPI_GEMM) {
             return A1 + s * (BMX * DKT);
         } else {
             return s < n1 ? A1 + s * DKT : g.A2 + (s - n1) * DKT;
         }
     };
     auto stage_b = [&](int64_t s) -> const uint16_t* {
-        if constexpr (EPI == EPI_GEMM) {
-            const int64_t kc = s / 6;
-            const int pq = (int)(s - 6 * kc);
-            return g.Bp + ((0x102010 >> (4 * pq)) & 15) * g.b_plane + kb + kc * DKT;
-        } else if constexpr (EPI == EPI_HESSIAN) {
+        if constexpr (EPI == EPI_HESSIAN || EPI == EPI_GEMM) {
             return B1 + s * (BMX * DKT);
         } else {
             return s < n1 ? B1 + s * DKT : B2 + (s - n1) * DKT;
@@ -573,17 +578,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         constexpr int q = decltype(qc)::value;
         constexpr bool isa = q < PER;
         constexpr int qq = isa ? q : q - PER;
-        if constexpr (EPI == EPI_HESSIAN) {
+        if constexpr (BLK) {
             // Buffer copies: the panel's resource in SGPRs, the stage's byte
-            // offset in soffset, the lane's 32-bit offset (one of four: parity
-            // x half) in voffset, and k KB in the immediate, which applies to
+            // offset in soffset (X^T X; the split planes take a resource per
+            // stage block), the lane's 32-bit offset (one of four: parity x
+            // half) in voffset, and k KB in the immediate, which applies to
             // the global and the LDS address alike, so copies qq = 4 h + k of
             // a half h share one M0 (PER is even: q' and qq have one parity)
             constexpr int h = qq >> 2, k = qq & 3;
             unsigned char* lb = smem + buf * (2 * PANEL) + (isa ? 0 : PANEL) + (cw * PER + 4 * h) * 1024;
             const unsigned vo = (qq & 1) ? (h ? vo11 : vo10) : (h ? vo01 : vo00);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? rsa : rsb, (lds_ptr_t)lb, 16, vo,
-                                                     (unsigned)(s * (BMX * DKT * 2)), k * 1024, 0);
+            if constexpr (EPI == EPI_HESSIAN)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? rsa : rsb, (lds_ptr_t)lb, 16, vo,
+                                                         (unsigned)(s * (BMX * DKT * 2)), k * 1024, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    __builtin_amdgcn_make_buffer_rsrc((void*)gemm_block(s, isa), (short)0, BMX * DKT * 2, 0x00020000),
+                    (lds_ptr_t)lb, 16, vo, 0u, k * 1024, 0);
         } else {
             const uint16_t* P = isa ? stage_a(s) + offA[qq] : stage_b(s) + offB[qq];
             unsigned char* dst = smem + buf * (2 * PANEL) + (isa ? 0 : PANEL) + (cw * PER + qq) * 1024;
@@ -792,31 +803,47 @@ __device__ __forceinline__ void split3_store8(const float (&v)[8], uint16_t* p, 
     *(uint4*)(p + 2 * plane) = pack(l);
 }
 
-// P[t][r][k] (t = hi, mid, lo; row stride ldp, plane stride plane) from
-// S[r][k] = X[r * ldx + k] for k < K, zero for K <= k < kp (kp % 8 == 0).
+// Split planes are panel-blocked like the X^T X operands: element (r, k) of
+// a plane sits at (r / 256) pstride + (k / 64) 256 * 64 + (r % 256) 64 + k % 64,
+// so one 64-deep stage of a 256-row panel is one contiguous 32 KB block.
+// Panels are padded to 256 rows (zeros) and pstride = 256 (kp + 64): one
+// spare stage per panel keeps panels off power-of-two distances.
+constexpr int SPLIT_PANEL = 256;
+__host__ __device__ inline int64_t split3_pstride(int64_t kp) { return SPLIT_PANEL * (kp + 64); }
+__device__ __forceinline__ int64_t split3_offset(int64_t r, int64_t k, int64_t pstride) {
+    return (r / SPLIT_PANEL) * pstride + (k >> 6) * (SPLIT_PANEL * 64) + (r % SPLIT_PANEL) * 64 + (k & 63);
+}
+
+// P[t] (t = hi, mid, lo; plane stride plane, blocked as split3_offset) from
+// S[r][k] = X[r * ldx + k] for r < R and k < K, zero for the padding rows
+// R <= r < Rp and depth K <= k < kp (kp % 64 == 0).
 __global__ __launch_bounds__(256) void split3_rows_kernel(const float* __restrict__ X, int64_t ldx, int64_t R,
-                                                          int64_t K, int vec, uint16_t* __restrict__ P, int64_t ldp,
-                                                          int64_t kp, int64_t plane) {
+                                                          int64_t Rp, int64_t K, int vec, uint16_t* __restrict__ P,
+                                                          int64_t pstride, int64_t kp, int64_t plane) {
     const int64_t nch = kp / 8;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < R * nch; e += (int64_t)gridDim.x * 256) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < Rp * nch; e += (int64_t)gridDim.x * 256) {
         const int64_t r = e / nch, k0 = 8 * (e % nch);
-        const float* x = X + r * ldx + k0;
         float v[8];
-        if (vec && k0 + 8 <= K) {
+        if (r >= R) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = 0.f;
+        } else if (vec && k0 + 8 <= K) {
+            const float* x = X + r * ldx + k0;
             const float4 a = *(const float4*)x, b = *(const float4*)(x + 4);
             v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
         } else {
+            const float* x = X + r * ldx + k0;
 #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] = (k0 + q < K) ? x[q] : 0.f;
         }
-        split3_store8(v, P + r * ldp + k0, plane);
+        split3_store8(v, P + split3_offset(r, k0, pstride), plane);
     }
 }
 
 // The same from S[r][k] = X[k * ldx + r] (X stored [K][R]), through a 64 x 64
-// LDS tile; grid (cdiv(R, 64), kp / 64), kp % 64 == 0.
+// LDS tile; grid (Rp / 64, kp / 64), kp % 64 == 0, Rp % 64 == 0.
 __global__ __launch_bounds__(256) void split3_cols_kernel(const float* __restrict__ X, int64_t ldx, int64_t R,
-                                                          int64_t K, uint16_t* __restrict__ P, int64_t ldp,
+                                                          int64_t K, uint16_t* __restrict__ P, int64_t pstride,
                                                           int64_t plane) {
     __shared__ float tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
@@ -827,27 +854,28 @@ __global__ __launch_bounds__(256) void split3_cols_kernel(const float* __restric
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * 8; i += 256) {
         const int rr = i >> 3, c = i & 7;
-        if (r0 + rr >= R) continue;
         float v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] = tile[8 * c + q][rr];
-        split3_store8(v, P + (r0 + rr) * ldp + k0 + 8 * c, plane);
+        split3_store8(v, P + split3_offset(r0 + rr, k0 + 8 * c, pstride), plane);
     }
 }
 
-int64_t split3_ld(int64_t K) { return cdiv(K, 64) * 64 + 64; }
+// elements of one plane of R rows at depth K
+int64_t split3_plane(int64_t R, int64_t K) { return cdiv(R, SPLIT_PANEL) * split3_pstride(cdiv(K, 64) * 64); }
 
 // planes of op(X) [R, K] (trans: X stored [K][R])
 int launch_split3(const float* X, int64_t ldx, bool trans, int64_t R, int64_t K, uint16_t* P, hipStream_t st) {
-    const int64_t kp = cdiv(K, 64) * 64, ldp = split3_ld(K), plane = R * ldp;
+    const int64_t kp = cdiv(K, 64) * 64, ps = split3_pstride(kp), plane = split3_plane(R, K);
+    const int64_t Rp = cdiv(R, SPLIT_PANEL) * SPLIT_PANEL;
     if (trans) {
-        hipLaunchKernelGGL(split3_cols_kernel, dim3((unsigned)cdiv(R, 64), (unsigned)(kp / 64)), dim3(256), 0, st, X,
-                           ldx, R, K, P, ldp, plane);
+        hipLaunchKernelGGL(split3_cols_kernel, dim3((unsigned)(Rp / 64), (unsigned)(kp / 64)), dim3(256), 0, st, X,
+                           ldx, R, K, P, ps, plane);
     } else {
         const int vec = (((uintptr_t)X & 15u) == 0) && (ldx % 4 == 0);
-        const int64_t items = R * (kp / 8);
+        const int64_t items = Rp * (kp / 8);
         hipLaunchKernelGGL(split3_rows_kernel, dim3((unsigned)std::min<int64_t>(cdiv(items, 256), 16384)), dim3(256),
-                           0, st, X, ldx, R, K, vec, P, ldp, kp, plane);
+                           0, st, X, ldx, R, Rp, K, vec, P, ps, kp, plane);
     }
     PTQ_LAUNCH_CHECK();
     return PTQ_OK;
@@ -855,20 +883,20 @@ int launch_split3(const float* X, int64_t ldx, bool trans, int64_t R, int64_t K,
 
 }  // namespace
 
-size_t gemm_f32_split3_elems(int64_t rows, int64_t K) { return (size_t)(3 * rows * split3_ld(K)); }
+size_t gemm_f32_split3_elems(int64_t rows, int64_t K) { return (size_t)(3 * split3_plane(rows, K)); }
 
 int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStream_t st) {
     if (a.M <= 0 || a.N <= 0) return PTQ_OK;
     if (a.K <= 0) return launch_gemm_f32(a, st);
-    const int64_t kp = cdiv(a.K, 64) * 64, ldp = split3_ld(a.K);
+    const int64_t kp = cdiv(a.K, 64) * 64;
     const bool same = a.A == a.B && a.lda == a.ldb && a.M == a.N &&
                       ((a.layout_a == A_MK && a.layout_b == B_NK) || (a.layout_a == A_KM && a.layout_b == B_KN));
     PTQ_TRY(launch_split3(a.A, a.lda, a.layout_a == A_KM, a.M, a.K, pa, st));
     if (!same) PTQ_TRY(launch_split3(a.B, a.ldb, a.layout_b == B_KN, a.N, a.K, pb, st));
     Bf16GemmArgs g{};
     g.Ap = pa; g.Bp = same ? pa : pb;
-    g.a_plane = a.M * ldp; g.b_plane = a.N * ldp;
-    g.lda = ldp; g.ldb = ldp;
+    g.a_plane = split3_plane(a.M, a.K); g.b_plane = split3_plane(a.N, a.K);
+    g.pstride = split3_pstride(kp);
     g.K1 = kp; g.K2 = 0;
     g.M = a.M; g.N = a.N;
     g.C = a.C; g.ldc = a.ldc;
