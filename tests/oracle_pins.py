@@ -177,9 +177,10 @@ def check_inverse_factor_identity(impl):
         assert np.array_equal(U, np.triu(U))
         assert np.all(np.diag(U) > 0)
         assert np.max(np.abs(U.T @ U @ H - np.eye(n))) <= 1e-10
-        # textbook identity: H = R R^T with R upper  =>  U = R^-1
-        R = reverse_cholesky(H)
-        assert np.allclose(U, np.linalg.inv(R), rtol=1e-10, atol=1e-12 * np.abs(U).max())
+        # the page's own route: invert H, lower Cholesky factor of the
+        # inverse, transpose (a different computation of the same unique factor)
+        Upage = np.linalg.cholesky(np.linalg.inv(H)).T
+        assert np.allclose(U, Upage, rtol=1e-9, atol=1e-11 * np.abs(U).max())
     # brute-force Cholesky (plain loops) on the flipped matrix
     H = spd(5, 9)
     J = np.eye(5)[::-1]
@@ -454,6 +455,29 @@ def check_zero_point(impl):
     assert np.array_equal(res["codes"][:, perm], ref["codes"])
 
 
+def check_output_energy_hand(impl):
+    """||X W^T||^2 and ||X (W - What)^T||^2 on the hand-worked values of
+    tests/golden/output_energy_hand.json, and by brute-force loops."""
+    gd = load_golden("output_energy_hand.json")
+    X, W, What = (np.array(gd[k], dtype=np.float64) for k in ("X", "W", "What"))
+    assert impl.output_energy(X, W) == gd["energy"]
+    assert impl.output_error(X, W, What) == gd["error"]
+    rng = np.random.default_rng(17)
+    for rows, out, n in ((5, 3, 4), (4, 4, 4), (3, 6, 2)):
+        X = rng.standard_normal((rows, n))
+        W = rng.standard_normal((out, n))
+        What = W + 0.1 * rng.standard_normal((out, n))
+        e = f = 0.0
+        for i in range(rows):
+            for o in range(out):
+                y = sum(X[i, j] * W[o, j] for j in range(n))
+                yq = sum(X[i, j] * What[o, j] for j in range(n))
+                e += y * y
+                f += (y - yq) * (y - yq)
+        assert abs(impl.output_energy(X, W) - e) <= 1e-12 * e
+        assert abs(impl.output_error(X, W, What) - f) <= 1e-12 * f
+
+
 ALL_CHECKS = [
     check_rtn_hand, check_gptq_hand, check_damping_hand, check_act_order_hand,
     check_hessian_bruteforce, check_hessian_orthogonal, check_hessian_chunking,
@@ -461,5 +485,5 @@ ALL_CHECKS = [
     check_babai_identity, check_babai_equivalence, check_grid_and_invariances,
     check_gptq_beats_rtn_correlated, check_act_order_matches_permuted_problem, check_awq,
     check_hessian_sizes, check_pack_hand, check_pack_roundtrip, check_dequant_g_idx_hand, check_awq_gptq,
-    check_zero_point, check_pack_zero_point,
+    check_zero_point, check_pack_zero_point, check_output_energy_hand,
 ]

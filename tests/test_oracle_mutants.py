@@ -75,6 +75,11 @@ def _lower_factor(H):
     return np.linalg.cholesky(np.linalg.inv(H))          # forgot the transpose
 
 
+def _factor_not_reversed(H):
+    L = np.linalg.cholesky(np.asarray(H, dtype=np.float64))   # H = L L^T in natural order
+    return np.linalg.inv(L).T                                 # upper, but U^T U = (L^T L)^-1
+
+
 def _no_damp(H0, damp):
     return np.asarray(H0, dtype=np.float64).copy(), 0.0
 
@@ -219,6 +224,22 @@ def _zp_with_params(params):
     return dict(zp_rtn=rtn, zp_gptq_layer=layer, zp_group_params=params)
 
 
+def _energy_untransposed(X, W):
+    Y = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64)   # X W instead of X W^T
+    return float(np.sum(Y * Y))
+
+
+def _energy_unsquared(X, W):
+    Y = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+    return float(np.sum(np.abs(Y)))                                      # |y| summed, not y^2
+
+
+def _error_untransposed(X, W, What):
+    dW = np.asarray(W, dtype=np.float64) - np.asarray(What, dtype=np.float64)
+    E = np.asarray(X, dtype=np.float64) @ dW
+    return float(np.sum(E * E))
+
+
 MUTANTS = {
     "feedback sign flipped": dict(gptq_layer=_layer_with(columns=_columns_factory(sign=-1.0))),
     "error not divided by U_jj": dict(gptq_layer=_layer_with(columns=_columns_factory(divide_by_ujj=False))),
@@ -227,6 +248,8 @@ MUTANTS = {
     "column of U instead of row": dict(gptq_layer=_layer_with(columns=_columns_factory(update_row_of_u=False))),
     "lower factor (no transpose)": dict(gptq_layer=_layer_with(factor=_lower_factor),
                                         inverse_upper_factor=_lower_factor),
+    "factor without the index reversal": dict(gptq_layer=_layer_with(factor=_factor_not_reversed),
+                                              inverse_upper_factor=_factor_not_reversed),
     "damping dropped": dict(gptq_layer=_layer_with(damped=_no_damp), damped=_no_damp),
     "damping by sum not mean": dict(gptq_layer=_layer_with(damped=_damp_sum), damped=_damp_sum),
     "act-order ascending": dict(gptq_layer=_layer_with(perm=_ascending), act_order_permutation=_ascending),
@@ -246,6 +269,9 @@ MUTANTS = {
     "zero-point: zero not subtracted": dict(zp_dequantize=_zp_dequant_no_zero),
     "zero-point: range without the origin": _zp_with_params(_zp_params_without_origin),
     "zero-point: zero floored": _zp_with_params(_zp_params_floor),
+    "output energy: X W instead of X W^T": dict(output_energy=_energy_untransposed),
+    "output energy: not squared": dict(output_energy=_energy_unsquared),
+    "output error: X dW instead of X dW^T": dict(output_error=_error_untransposed),
 }
 
 
