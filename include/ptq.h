@@ -75,11 +75,17 @@ int ptq_abi_version(void);
  *     ones inside 1 and 4; main loop only)
  * Enabling (any mask, 0 included) discards earlier records. ptq_profile_read
  * waits for the recorded events of class `kernel` and returns the sum of
- * their elapsed times (ms) and the number of launches. Process-wide; calls
- * that overlap from several threads share the records.
+ * their elapsed times (ms) and the number of launches. ptq_profile_flops
+ * returns the MFMA flops those launches execute, counted on the host at
+ * launch time over whole output tiles (edge padding, diagonal tiles and, for
+ * the split-operand GEMMs, all six bf16 term products included; 0 for the
+ * classes that are not counted: 1, 2, 3, 4 and 6 as wrappers or fp32 work).
+ * Process-wide; calls that overlap from several threads share the records.
+ * Errors: EINVAL (kernel out of range, NULL output), EHIP (profile_read).
  * ---------------------------------------------------------------------- */
 int ptq_profile_enable(unsigned kernel_mask);
 int ptq_profile_read(int kernel, double* total_ms, int64_t* launches);
+int ptq_profile_flops(int kernel, double* mfma_flops);
 
 /* ------------------------------------------------------------------------
  * Stage 1 — proxy Hessian.  [OBJ] "A strong answer": H = X^T X over the

@@ -48,6 +48,7 @@ def _load() -> ctypes.CDLL:
         "ptq_abi_version": (i32, []),
         "ptq_profile_enable": (i32, [ctypes.c_uint]),
         "ptq_profile_read": (i32, [i32, dp, ctypes.POINTER(i64)]),
+        "ptq_profile_flops": (i32, [i32, dp]),
         "hessian_workspace_bytes": (sz, [i64, i64]),
         "hessian_accumulate": (i32, [vp, vp, i64, vp, i32, i64, i64, vp, sz, vp]),
         "gptq_factor_workspace_bytes": (sz, [i64]),
@@ -141,6 +142,13 @@ def profile_read(kernel: str):
     cnt = ctypes.c_int64(0)
     _check(_lib.ptq_profile_read(PROFILE_KERNELS[kernel], ctypes.byref(tot), ctypes.byref(cnt)))
     return tot.value, cnt.value
+
+
+def profile_flops(kernel: str) -> float:
+    """MFMA flops executed by the recorded launches of one kernel class."""
+    f = ctypes.c_double(0.0)
+    _check(_lib.ptq_profile_flops(PROFILE_KERNELS[kernel], ctypes.byref(f)))
+    return f.value
 
 
 # ---------------------------------------------------------------- stage 1 ---

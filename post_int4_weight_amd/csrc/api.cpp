@@ -58,6 +58,7 @@ static int check_gptq_common(int64_t out, int64_t in, int bits, int g, int block
 struct ProfRec {
     hipEvent_t a, b;
     int kernel;
+    double flops;   // MFMA flops the launch executes (0: not counted)
 };
 static std::mutex g_prof_mu;
 static std::vector<ProfRec> g_prof_pool;
@@ -65,7 +66,7 @@ static size_t g_prof_used = 0;
 static unsigned g_prof_mask = 0;
 static int g_prof_open[PROF_NKERNELS];
 
-void prof_begin(int kernel, hipStream_t st) {
+void prof_begin(int kernel, hipStream_t st, double mfma_flops) {
     if (!(g_prof_mask & (1u << kernel))) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (g_prof_used == g_prof_pool.size()) {
@@ -75,6 +76,7 @@ void prof_begin(int kernel, hipStream_t st) {
     }
     ProfRec& r = g_prof_pool[g_prof_used];
     r.kernel = kernel;
+    r.flops = mfma_flops;
     if (hipEventRecord(r.a, st) != hipSuccess) return;
     g_prof_open[kernel] = (int)g_prof_used;
     ++g_prof_used;
@@ -138,14 +140,26 @@ int ptq_profile_read(int kernel, double* total_ms, int64_t* launches) {
     return PTQ_OK;
 }
 
+int ptq_profile_flops(int kernel, double* mfma_flops) {
+    if (kernel < 0 || kernel >= PROF_NKERNELS || !mfma_flops) return fail(PTQ_EINVAL, "ptq_profile_flops: bad arguments");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    double tot = 0.0;
+    for (size_t i = 0; i < g_prof_used; ++i)
+        if (g_prof_pool[i].kernel == kernel) tot += g_prof_pool[i].flops;
+    *mfma_flops = tot;
+    return PTQ_OK;
+}
+
 size_t hessian_workspace_bytes(int64_t in, int64_t rows) {
     if (in < 1 || rows < 0) return 0;
     return xtx_workspace_bytes(in, rows);
 }
 
-int hessian_accumulate(float* H, double* d, int64_t in, const void* X, int x_dtype, int64_t rows, int64_t ldx,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "hessian_accumulate";
+}  // extern "C"
+
+namespace ptq {
+int check_hessian_args(const char* fn, const float* H, const double* d, int64_t in, const void* X, int x_dtype,
+                       int64_t rows, int64_t ldx) {
     if (in < 1) return fail(PTQ_EINVAL, "%s: in = %lld < 1", fn, (long long)in);
     if (in % 4) return fail(PTQ_EINVAL, "%s: in = %lld must be a multiple of 4 (16-byte rows of H)", fn, (long long)in);
     if (rows < 0) return fail(PTQ_EINVAL, "%s: rows = %lld < 0", fn, (long long)rows);
@@ -156,6 +170,16 @@ int hessian_accumulate(float* H, double* d, int64_t in, const void* X, int x_dty
     if (rows > 0 && !X) return fail(PTQ_EINVAL, "%s: X is NULL", fn);
     if (!aligned16(H) || (X && !aligned16(X)) || (d && ((uintptr_t)d & 7u)))
         return fail(PTQ_EINVAL, "%s: misaligned pointer", fn);
+    return PTQ_OK;
+}
+}  // namespace ptq
+
+extern "C" {
+
+int hessian_accumulate(float* H, double* d, int64_t in, const void* X, int x_dtype, int64_t rows, int64_t ldx,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "hessian_accumulate";
+    PTQ_TRY(check_hessian_args(fn, H, d, in, X, x_dtype, rows, ldx));
     if (workspace_bytes > 0 && !workspace) return fail(PTQ_EINVAL, "%s: workspace NULL with nonzero size", fn);
     if (workspace && !aligned16(workspace)) return fail(PTQ_EINVAL, "%s: misaligned workspace", fn);
     if (rows == 0) return PTQ_OK;

@@ -112,7 +112,9 @@ enum ProfKernel {
     PROF_SPLIT3_GEMM = 7,   // fp32 GEMM as bf16 MFMAs on three-term splits (main loop only)
     PROF_NKERNELS = 8
 };
-void prof_begin(int kernel, hipStream_t st);
+// mfma_flops: the MFMA flops the bracketed launch executes (whole tiles,
+// padding included; 0 where not counted), summed by ptq_profile_flops.
+void prof_begin(int kernel, hipStream_t st, double mfma_flops = 0.0);
 void prof_end(int kernel, hipStream_t st);
 
 // ------------------------------------------------------------ launchers --
@@ -122,6 +124,15 @@ void prof_end(int kernel, hipStream_t st);
 size_t xtx_workspace_bytes(int64_t n, int64_t rows);
 int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64_t rows,
                int64_t ldx, void* ws, size_t ws_bytes, hipStream_t st);
+// The same within a fixed scratch of scratch_bytes (device memory the caller
+// owns): rows go in chunks sized to fit it; EINVAL when not even 64 rows fit.
+int launch_xtx_bounded(float* H, double* d, int64_t n, const void* X, int x_dtype, int64_t rows,
+                       int64_t ldx, void* scratch, size_t scratch_bytes, hipStream_t st);
+// Argument checks of hessian_accumulate (api.cpp); no HIP call.
+int check_hessian_args(const char* fn, const float* H, const double* d, int64_t in, const void* X, int x_dtype,
+                       int64_t rows, int64_t ldx);
+// Rows per chunk of launch_xtx_bounded for a scratch of scratch_bytes (0: none fit).
+int64_t xtx_bounded_chunk(int64_t n, size_t scratch_bytes);
 
 // fp32 MFMA GEMM: C = alpha * op(A) op(B) + beta * C, see gemm_f32.hip.
 enum GemmLayoutA { A_MK = 0, A_KM = 1 };   // A row-major [M,K] or stored as [K,M]

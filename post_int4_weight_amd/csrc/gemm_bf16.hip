@@ -881,6 +881,23 @@ int launch_split3(const float* X, int64_t ldx, bool trans, int64_t R, int64_t K,
     return PTQ_OK;
 }
 
+// MFMA flops of one split-operand launch: every computed 256 x 256 tile over
+// its depth range (the kernel's triangular skips, in whole 64-deep steps),
+// six bf16 term products per step.
+double split3_mfma_flops(const Bf16GemmArgs& g) {
+    double f = 0.0;
+    for (int64_t tm = 0; tm < g.tiles_m; ++tm)
+        for (int64_t tn = 0; tn < g.tiles_n; ++tn) {
+            if (g.upper_only && tm > tn) continue;
+            int64_t kb = 0, ke = g.K1;
+            if (g.tri == TRI_A_UPPER) kb = tm * 256;
+            else if (g.tri == TRI_B_UPPER_NK) kb = tn * 256;
+            else if (g.tri == TRI_B_UPPER_KN) ke = std::min<int64_t>(g.K1, tn * 256 + 256);
+            if (ke > kb) f += 6.0 * 2.0 * 256.0 * 256.0 * (double)(64 * ((ke - kb) / 64));
+        }
+    return f;
+}
+
 }  // namespace
 
 size_t gemm_f32_split3_elems(int64_t rows, int64_t K) { return (size_t)(3 * split3_plane(rows, K)); }
@@ -904,7 +921,7 @@ int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStr
     g.tiles_m = cdiv(a.M, 256); g.tiles_n = cdiv(a.N, 256);
     const unsigned grid = (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n
                                                        : g.tiles_m * g.tiles_n);
-    prof_begin(PROF_SPLIT3_GEMM, st);
+    prof_begin(PROF_SPLIT3_GEMM, st, split3_mfma_flops(g));
     const int rc = launch_direct<256, EPI_GEMM, 64, DNW, DMF>(g, 0, grid, 1, st);
     prof_end(PROF_SPLIT3_GEMM, st);
     PTQ_TRY(rc);
@@ -1126,12 +1143,14 @@ XtxPlan plan_xtx(int64_t n, int64_t rows) {
 
 }  // namespace
 
-size_t xtx_workspace_bytes(int64_t n, int64_t rows) { return plan_bytes(plan_xtx(n, rows), n); }
+namespace {
 
-int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64_t rows,
-               int64_t ldx, void* ws, size_t ws_bytes, hipStream_t st) {
-    if (rows == 0) return PTQ_OK;
-    XtxPlan p = plan_xtx(n, rows);
+// The chunk loop of H (+)= X^T X under a plan whose buffers fit `ws`. With
+// per_chunk_d, the fp64 column sums of every chunk are folded into d right
+// after the chunk, so the sums workspace holds one chunk's row groups only.
+int run_xtx(const XtxPlan& plan, bool per_chunk_d, float* H, double* d, int64_t n, const void* X, int x_dtype,
+            int64_t rows, int64_t ldx, void* ws, size_t ws_bytes, hipStream_t st) {
+    XtxPlan p = plan;
     if (x_dtype == PTQ_BF16 && plan_bytes(p, n) > ws_bytes) {
         set_error("hessian_accumulate: workspace of %zu bytes, %zu needed", ws_bytes, plan_bytes(p, n));
         return PTQ_EWORKSPACE;
@@ -1191,6 +1210,12 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
                                dim3(256), 0, st, (const uint16_t*)X, ldx, n, r0, nr, Xt, p.bm, pstride, kt);
         }
         PTQ_LAUNCH_CHECK();
+        if (vec && d && per_chunk_d) {
+            hipLaunchKernelGGL(reduce_slabs_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, d, dsum,
+                               (int)gofs, n);
+            PTQ_LAUNCH_CHECK();
+            gofs = 0;
+        }
         const bool last = r0 + p.chunk >= rows;
         const int ns = (p.nsplit > 1 && nr >= p.nsplit * SPLIT_ROWS_MIN) ? p.nsplit : 1;
         const int64_t kper = cdiv(cdiv(kt, ns), KT) * KT;
@@ -1204,7 +1229,7 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
             g.H = (ns > 1) ? hpart : H;
             g.h_batch_stride = n * n;
             g.ldh = n; g.mirror = (ns == 1 && last) ? 1 : 0; g.T = p.T; g.store_not_add = (ns > 1) ? 1 : 0;
-            prof_begin(PROF_XTX_GEMM, st);
+            prof_begin(PROF_XTX_GEMM, st, 2.0 * (double)p.bm * p.bm * (double)ntiles * (double)kt);
             const int rc = (p.bm == 256) ? launch_nt<256, EPI_HESSIAN>(g, ntiles, (unsigned)ns, st)
                                          : launch_nt<128, EPI_HESSIAN>(g, ntiles, (unsigned)ns, st);
             prof_end(PROF_XTX_GEMM, st);
@@ -1221,7 +1246,7 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
             PTQ_LAUNCH_CHECK();
         }
     }
-    if (vec && d) {
+    if (vec && d && gofs > 0) {
         hipLaunchKernelGGL(reduce_slabs_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, d, dsum, (int)gofs,
                            n);
         PTQ_LAUNCH_CHECK();
@@ -1232,6 +1257,53 @@ int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64
         PTQ_LAUNCH_CHECK();
     }
     return PTQ_OK;
+}
+
+}  // namespace
+
+size_t xtx_workspace_bytes(int64_t n, int64_t rows) { return plan_bytes(plan_xtx(n, rows), n); }
+
+int launch_xtx(float* H, double* d, int64_t n, const void* X, int x_dtype, int64_t rows,
+               int64_t ldx, void* ws, size_t ws_bytes, hipStream_t st) {
+    if (rows == 0) return PTQ_OK;
+    return run_xtx(plan_xtx(n, rows), false, H, d, n, X, x_dtype, rows, ldx, ws, ws_bytes, st);
+}
+
+// The same within a fixed scratch: no split over depth (no partial H), sums
+// of squares straight into d for non-vector X, chunks of the largest multiple
+// of 64 rows whose transposed copy and one chunk's fp64 row-group sums fit.
+int64_t xtx_bounded_chunk(int64_t n, size_t scratch_bytes) {
+    const int bm = (n >= 2048) ? 256 : 128;
+    const int64_t T = cdiv(n, bm);
+    // bytes of a chunk of c rows (plan_bytes with nsplit = nslab = 1, one
+    // chunk's groups), plus two 256-byte alignment slacks
+    auto need = [&](int64_t c) {
+        return (size_t)T * bm * (c + XT_PAD) * 2 + (size_t)cdiv(c, TR_ROWS) * n * 8 + 512;
+    };
+    int64_t lo = 0, hi = CHUNK_ROWS_MAX / 64;   // in units of 64 rows
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (need(64 * mid) <= scratch_bytes) lo = mid;
+        else hi = mid - 1;
+    }
+    return 64 * lo;
+}
+
+int launch_xtx_bounded(float* H, double* d, int64_t n, const void* X, int x_dtype, int64_t rows, int64_t ldx,
+                       void* scratch, size_t scratch_bytes, hipStream_t st) {
+    if (rows == 0) return PTQ_OK;
+    XtxPlan p = plan_xtx(n, rows);
+    p.nsplit = 1;
+    p.nslab = 1;
+    p.slab_rows = rows;
+    p.chunk = std::min<int64_t>(p.chunk, xtx_bounded_chunk(n, scratch_bytes));
+    if (p.chunk < 64) {
+        set_error("hessian_accumulate_noalloc: in = %lld needs more than the %zu bytes of scratch", (long long)n,
+                  scratch_bytes);
+        return PTQ_EINVAL;
+    }
+    p.ngroups = cdiv(p.chunk, TR_ROWS);
+    return run_xtx(p, true, H, d, n, X, x_dtype, rows, ldx, scratch, scratch_bytes, st);
 }
 
 // AWQ error GEMM: partial[z][tile] = sum over the tile of (X (hi_z + lo_z)^T)^2
@@ -1246,7 +1318,7 @@ int launch_awq_error_gemm(const uint16_t* X, int64_t ldx, int64_t rows, int64_t 
     g.ntiles = cdiv(rows, 256) * g.tiles_n;
     *ntiles_out = g.ntiles;
     g.partial = partial;
-    prof_begin(PROF_AWQ_GEMM, st);
+    prof_begin(PROF_AWQ_GEMM, st, 2.0 * 256.0 * 256.0 * (double)g.ntiles * (double)(g.K1 + g.K2) * nbatch);
     const int rc = launch_nt<256, EPI_SUMSQ>(g, g.ntiles, (unsigned)nbatch, st);
     prof_end(PROF_AWQ_GEMM, st);
     return rc;

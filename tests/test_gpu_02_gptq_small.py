@@ -122,6 +122,48 @@ def test_layer_shapes(gpu, out, n, rows, bits, g, block, act, dtype):
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_act_order_tied_keys(gpu, dtype):
+    """Act-order with exactly tied keys: duplicated channels (equal d_j) and
+    dead channels (d_j = 0), damp 0.01 ("GPTQ versus AWQ objectives", "What
+    interviewers probe next": act-order by decreasing Hessian diagonal, and
+    damping for channels that are dead or duplicated). Ties go to the lower
+    column index on both sides, so the permutation must be identical."""
+    from post_int4_weight_amd import api
+    out, n, rows = 48, 640, 2000
+    announce(f"act-order with tied keys, {dtype}, out={out} n={n}")
+    W, X = inputs.custom(out, n, rows, seed=77, dtype=dtype)
+    for dst in (5, 17, 450):
+        X[:, dst] = X[:, 300]             # four identical channels
+    X[:, 129] = X[:, 77]                  # an identical pair
+    for dead in (40, 41, 600, 601, 602):
+        X[:, dead] = 0                    # five dead channels: keys tied at 0
+    Wd, Xd = W.to(gpu), X.to(gpu)
+    H, d = _hessian(api, Xd, n, gpu)
+    res = api.gptq_quantize_layer(Wd, H, d, bits=4, group_size=128, damp=0.01, act_order=True, block_size=128)
+    U, perm, _ = api.gptq_inverse_factor(H, d, damp=0.01, act_order=True)
+    torch.cuda.synchronize()
+    H0, d0 = oracle.proxy_hessian(to64(X))
+    for grp in ((5, 17, 300, 450), (77, 129), (40, 41, 600, 601, 602)):
+        assert len(set(d0[list(grp)])) == 1
+        assert len(set(d.cpu().numpy()[list(grp)])) == 1
+    ref = oracle.gptq_layer(to64(W), H0, d0, bits=4, g=128, damp=0.01, act_order=True)
+    p = ref["perm"]
+    pos = np.argsort(p)
+    assert pos[5] < pos[17] < pos[300] < pos[450] and pos[77] < pos[129]
+    assert list(p[-5:]) == [40, 41, 600, 601, 602]
+    assert np.array_equal(perm.cpu().numpy(), p)
+    assert np.array_equal(res["perm"].cpu().numpy(), p)
+    assert np.array_equal(res["g_idx"].cpu().numpy(), ref["g_idx"])
+    assert rel_fro(U.cpu().double().numpy(), ref["U"]) <= 1e-4
+    codes = res["codes"].cpu().numpy()
+    assert code_match(codes, ref["codes"]) >= 0.99, code_match(codes, ref["codes"])
+    What = oracle.dequantize(codes, res["scales"].cpu().double().numpy(), ref["g_idx"])
+    e_gpu = relative_output_error(H0, to64(W), What)
+    e_ref = relative_output_error(H0, to64(W), ref["What"])
+    assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
+
+
 def test_identity_hessian_is_rtn(gpu):
     """H a multiple of I: U is diagonal, no feedback, GPTQ = RTN exactly."""
     from post_int4_weight_amd import api
