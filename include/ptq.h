@@ -111,6 +111,29 @@ int hessian_accumulate(float* H, double* d, int64_t in,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * hessian_accumulate without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight calibration or serving
+ * loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments (minus the workspace) and the same results as
+ * hessian_accumulate, up to the order of the fp32 sums across row chunks.
+ * The scratch (the transposed copy of a chunk of bf16 rows and that chunk's
+ * fp64 column sums) is a fixed array of PTQ_NOALLOC_SCRATCH_BYTES of device
+ * memory that the library holds on every GPU it runs on until the process
+ * ends; rows go in chunks that fit it, without splitting a launch over depth,
+ * so a large `in` runs slower than with a workspace (about 1100 rows a chunk
+ * at in = 28672). fp32 X needs no scratch. The call allocates nothing
+ * (no hipMalloc, no library allocation). Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams or two threads)
+ * race and must be serialized by the caller. Asynchronous on `stream`.
+ * Errors: as hessian_accumulate, plus EINVAL when a 64-row chunk does not fit
+ * the scratch (bf16 X with in > 253952).
+ * ---------------------------------------------------------------------- */
+#define PTQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int hessian_accumulate_noalloc(float* H, double* d, int64_t in, const void* X, int x_dtype, int64_t rows,
+                               int64_t ldx, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stage 2 — damping, act-order and the upper factor of the inverse.
  * [OBJ] "A strong answer": H += damp * mean(diag H) * I; U upper triangular
  * with U^T U = H^-1. [OBJ] "What interviewers probe next": act-order

@@ -51,6 +51,7 @@ def _load() -> ctypes.CDLL:
         "ptq_profile_flops": (i32, [i32, dp]),
         "hessian_workspace_bytes": (sz, [i64, i64]),
         "hessian_accumulate": (i32, [vp, vp, i64, vp, i32, i64, i64, vp, sz, vp]),
+        "hessian_accumulate_noalloc": (i32, [vp, vp, i64, vp, i32, i64, i64, vp]),
         "gptq_factor_workspace_bytes": (sz, [i64]),
         "gptq_inverse_factor": (i32, [vp, vp, i64, dbl, i32, vp, vp, dp, vp, sz, vp]),
         "gptq_columns_workspace_bytes": (sz, [i64, i64, i32]),
@@ -164,6 +165,16 @@ def hessian_accumulate(H: torch.Tensor, d: torch.Tensor | None, X: torch.Tensor,
     ws, wsb = _workspace(hessian_workspace_bytes(n, X.shape[0]), X.device, workspace)
     _check(_lib.hessian_accumulate(_ptr(H), _ptr(d), n, _ptr(X), _dtype_code(X), X.shape[0], ldx, _ptr(ws), wsb,
                                    _stream()))
+    return H, d
+
+
+def hessian_accumulate_noalloc(H: torch.Tensor, d: torch.Tensor | None, X: torch.Tensor):
+    """hessian_accumulate_noalloc (include/ptq.h): the same sums with the
+    library's fixed device scratch instead of a workspace (allocates nothing)."""
+    n = H.shape[0]
+    ldx = _rowmajor(X, "X")
+    _check(_lib.hessian_accumulate_noalloc(_ptr(H), _ptr(d), n, _ptr(X), _dtype_code(X), X.shape[0], ldx,
+                                           _stream()))
     return H, d
 
 

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libptq.so")
 
-SOURCES = ["api.cpp", "gemm_f32.hip", "gemm_bf16.hip", "chol.hip", "gptq.hip", "awq.hip", "pack.hip", "awq_gptq.hip"]
+SOURCES = ["api.cpp", "gemm_f32.hip", "gemm_bf16.hip", "chol.hip", "gptq.hip", "awq.hip", "pack.hip", "awq_gptq.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU ops are disabled for all device code (the compiler warns

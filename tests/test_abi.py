@@ -207,3 +207,12 @@ def test_output_error_validation(lib):
     assert "layer_output_error" in _err(lib)
     assert call(wsb=ws - 1) == 4                      # PTQ_EWORKSPACE
     assert call(w=None) == 4
+
+
+def test_noalloc_rejects_oversize_before_any_hip_call(lib):
+    fake = ctypes.c_void_p(1 << 20)      # never dereferenced: validation fails first
+    # bf16 X with in = 262144: a 64-row chunk's transposed copy exceeds the fixed scratch
+    assert lib.hessian_accumulate_noalloc(fake, None, 262144, fake, 0, 1, 262144, None) == 1
+    assert "too large" in _err(lib)
+    assert lib.hessian_accumulate_noalloc(fake, None, 6, fake, 0, 10, 8, None) == 1     # in % 4
+    assert lib.hessian_accumulate_noalloc(None, None, 16, fake, 0, 4, 16, None) == 1    # H NULL
