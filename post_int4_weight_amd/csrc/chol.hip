@@ -29,7 +29,6 @@ namespace ptq {
 namespace {
 
 constexpr int BASE = 128;                 // diagonal blocks factored by one workgroup
-constexpr int BASE_THREADS = (BASE / 4) * (BASE / 4);
 
 // lambda = damp * mean(key); key = d (fp64) or diag(H). One workgroup, fixed order.
 __global__ void damping_kernel(const float* H, const double* d, int64_t n, double damp, double* lam) {
@@ -127,46 +126,86 @@ __global__ void fill_int_kernel(int* p, int v) { *p = v; }
 //
 // Column k of A is last needed at step k + 1 (it holds column k of R), and
 // column c of S stays the identity's until step c (U[j][c] = 0 for c < j), so
-// one 4 x 4 register tile per thread holds M[i][k] = A[i][k] for k < j and
+// one TS x TS register tile per thread holds M[i][k] = A[i][k] for k < j and
 // S[i][k] for k >= j: at step j column j turns into the identity's column,
 // and the step's update is the single M[i][k] -= R[i][j] V[k] with
 // V[k] = R[k][j] (k < j) or U[j][k] (k >= j). Only column j of A and row j of
-// S go through LDS, so a step is one barrier, three 16-byte LDS reads and 16
-// FMAs per thread (rows already final skip the update). Outside m the block
-// is padded with the identity. U is written to the block (zeros below its
-// diagonal). Bit 0 of *flag: non-positive pivot; bit 1: NaN.
-__global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float* __restrict__ A,
-                                                                      float* __restrict__ U, int m, int64_t ld,
-                                                                      int* flag) {
-    constexpr int TB = BASE / 4;               // 4 x 4 tiles per block row
+// S go through LDS, so a step is one barrier, three TS-float LDS reads and
+// TS^2 FMAs per thread (rows already final skip the update). A is symmetric
+// and S is upper triangular (S[i][c] = 0 for i > c), and every value that
+// goes through LDS comes from a tile on or above the diagonal, so only those
+// tiles have a thread: TB (TB + 1) / 2 threads (the ones past that count only
+// join the barriers). Outside m the block is padded with the identity. U is
+// written on and above the diagonal of the block (the caller zeroes the rest).
+// Bit 0 of *flag: non-positive pivot; bit 1: NaN.
+template <int TS>
+constexpr int base_threads() {
+    return ((BASE / TS) * (BASE / TS + 1) / 2 + 63) / 64 * 64;
+}
+template <int TS>
+__global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const float* __restrict__ A,
+                                                                          float* __restrict__ U, int m, int64_t ld,
+                                                                          int* flag) {
+    constexpr int TB = BASE / TS;              // TS x TS tiles per block row
+    constexpr int NV = TS / 4;                 // float4 pieces per tile row
     __shared__ __attribute__((aligned(16))) float colb[BASE][BASE];   // colb[j][i] = A[i][j] at step j
     __shared__ __attribute__((aligned(16))) float rowb[BASE][BASE];   // rowb[j][c] = S[j][c] at step j
     const int t = threadIdx.x;
-    const int ib = t / TB, kb = t % TB;        // this thread's tile: rows 4*ib.., columns 4*kb..
-    const int i0 = 4 * ib, k0 = 4 * kb;
-    float a[4][4];                             // M: A left of the current column, S from it on
+    // this thread's tile (rows TS*ib.., columns TS*kb.., ib <= kb): the t-th
+    // of the upper triangle's tiles in row-major order
+    int ib = 0, rem = t;
+    while (ib < TB && rem >= TB - ib) {
+        rem -= TB - ib;
+        ++ib;
+    }
+    const bool live = ib < TB;
+    const int kb = live ? ib + rem : 0;
+    if (!live) ib = 0;
+    const int i0 = TS * ib, k0 = TS * kb;
+    float a[TS][TS];                           // M: A left of the current column, S from it on
 #pragma unroll
-    for (int di = 0; di < 4; ++di)
+    for (int di = 0; di < TS; ++di)
 #pragma unroll
-        for (int dk = 0; dk < 4; ++dk) {
+        for (int dk = 0; dk < TS; ++dk) {
             const int i = i0 + di, k = k0 + dk;
             const int r = min(min(i, k), m - 1), c = min(max(i, k), m - 1);   // upper triangle only
             a[di][dk] = A[(int64_t)r * ld + c];
             if (i >= m || k >= m) a[di][dk] = (i == k) ? 1.f : 0.f;
         }
+    auto put = [&](float* dst, const float (&v)[TS]) {
+#pragma unroll
+        for (int h = 0; h < NV; ++h) *(float4*)(dst + 4 * h) = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+    };
+    auto get = [&](const float* src, float (&v)[TS]) {
+#pragma unroll
+        for (int h = 0; h < NV; ++h) {
+            const float4 x = *(const float4*)(src + 4 * h);
+            v[4 * h] = x.x; v[4 * h + 1] = x.y; v[4 * h + 2] = x.z; v[4 * h + 3] = x.w;
+        }
+    };
     // row BASE - 1 of S is the identity's
-    if (kb == TB - 1) *(float4*)&colb[BASE - 1][i0] = make_float4(a[0][3], a[1][3], a[2][3], a[3][3]);
-    if (ib == TB - 1)
-        *(float4*)&rowb[BASE - 1][k0] = make_float4(0.f, 0.f, 0.f, (kb == TB - 1) ? 1.f : 0.f);
+    if (live && kb == TB - 1) {
+        float v[TS];
+#pragma unroll
+        for (int q = 0; q < TS; ++q) v[q] = a[q][TS - 1];
+        put(&colb[BASE - 1][i0], v);
+    }
+    if (live && ib == TB - 1) {
+        float v[TS];
+#pragma unroll
+        for (int q = 0; q < TS; ++q) v[q] = (kb == TB - 1 && q == TS - 1) ? 1.f : 0.f;
+        put(&rowb[BASE - 1][k0], v);
+    }
     for (int jb = TB - 1; jb >= 0; --jb) {
 #pragma unroll
-        for (int dj = 3; dj >= 0; --dj) {
-            const int j = 4 * jb + dj;
+        for (int dj = TS - 1; dj >= 0; --dj) {
+            const int j = TS * jb + dj;
             __syncthreads();
             float piv = colb[j][j];
-            const float4 ci = *(const float4*)&colb[j][i0];
-            const float4 ck = *(const float4*)&colb[j][k0];
-            const float4 rj = *(const float4*)&rowb[j][k0];
+            float civ[TS], ckv[TS], rjv[TS];
+            get(&colb[j][i0], civ);
+            get(&colb[j][k0], ckv);
+            get(&rowb[j][k0], rjv);
             if (!(piv > 0.f)) {
                 if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
                 piv = 1.f;
@@ -176,53 +215,63 @@ __global__ __launch_bounds__(BASE_THREADS) void chol_inv_base_kernel(const float
             // of dependent instructions sat on every step's critical path)
             const float r0 = __builtin_amdgcn_rsqf(piv);
             const float r = r0 * fmaf(-0.5f * piv, r0 * r0, 1.5f);
-            const float civ[4] = {ci.x, ci.y, ci.z, ci.w};
-            const float ckv[4] = {ck.x, ck.y, ck.z, ck.w};
-            const float rjv[4] = {rj.x, rj.y, rj.z, rj.w};
-            float Ri[4], V[4];
+            float Ri[TS], V[TS];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < TS; ++q) {
                 Ri[q] = (i0 + q < j) ? civ[q] * r : 0.f;
                 V[q] = (k0 + q < j) ? ckv[q] * r : rjv[q] * r;
             }
+            if (!live) continue;
             if (kb == jb) {   // column j of A is spent: it becomes column j of S (the identity's)
 #pragma unroll
-                for (int di = 0; di < 4; ++di) a[di][dj] = (i0 + di == j) ? 1.f : 0.f;
+                for (int di = 0; di < TS; ++di) a[di][dj] = (i0 + di == j) ? 1.f : 0.f;
             }
             if (ib == jb) {   // row j of S is final: U[j][k] for k >= j
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < TS; ++q)
                     if (k0 + q >= j) a[dj][q] = V[q];
             }
             if (i0 < j) {   // rows >= j are final (Ri = 0): whole waves skip the update as j falls
 #pragma unroll
-                for (int di = 0; di < 4; ++di)
+                for (int di = 0; di < TS; ++di)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) a[di][q] -= Ri[di] * V[q];
+                    for (int q = 0; q < TS; ++q) a[di][q] -= Ri[di] * V[q];
             }
             if (j > 0) {   // publish column j-1 of A and row j-1 of S (final after this update)
-                const int djn = (dj + 3) & 3;
-                const int jn = j - 1, jbn = jn >> 2;
-                if (kb == jbn)
-                    *(float4*)&colb[jn][i0] = make_float4(a[0][djn], a[1][djn], a[2][djn], a[3][djn]);
+                const int djn = (dj + TS - 1) % TS;
+                const int jn = j - 1, jbn = jn / TS;
+                if (kb == jbn) {
+                    float v[TS];
+#pragma unroll
+                    for (int q = 0; q < TS; ++q) v[q] = a[q][djn];
+                    put(&colb[jn][i0], v);
+                }
                 if (ib == jbn) {
                     // S[jn][k]: the identity's left of column j, M from column j on
-                    float v[4];
+                    float v[TS];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = (k0 + q < j) ? ((k0 + q == jn) ? 1.f : 0.f) : a[djn][q];
-                    *(float4*)&rowb[jn][k0] = make_float4(v[0], v[1], v[2], v[3]);
+                    for (int q = 0; q < TS; ++q) v[q] = (k0 + q < j) ? ((k0 + q == jn) ? 1.f : 0.f) : a[djn][q];
+                    put(&rowb[jn][k0], v);
                 }
             }
         }
     }
+    if (!live) return;
 #pragma unroll
-    for (int di = 0; di < 4; ++di)
+    for (int di = 0; di < TS; ++di)
 #pragma unroll
-        for (int dk = 0; dk < 4; ++dk) {
+        for (int dk = 0; dk < TS; ++dk) {
             const int i = i0 + di, k = k0 + dk;
-            if (i < m && k < m) U[(int64_t)i * ld + k] = a[di][dk];
+            if (i < m && k < m && i <= k) U[(int64_t)i * ld + k] = a[di][dk];
         }
 }
+
+// 4 x 4 tiles: 528 threads (nine waves) for the 128 x 128 block. With 8 x 8
+// tiles (136 threads, one wave per SIMD and no other wave to hide the step's
+// latency behind) a block took 82 us against 63 for the full 4 x 4 grid of
+// 1024 threads; leaving out the tiles below the diagonal took it to 55 us.
+constexpr int BASE_TS = 4;
+constexpr int BASE_THREADS = base_threads<BASE_TS>();
 
 // GEMMs with all of M, N, K at least this large run on the bf16 MFMA from
 // three-term splits of their operands (fp32 accuracy, gemm_bf16.hip); the
@@ -262,7 +311,7 @@ int recurse(Ctx& c, int64_t o, int64_t m) {
     const int64_t n = c.n;
     if (m <= BASE) {
         prof_begin(PROF_FACTOR_BASE, c.st);
-        hipLaunchKernelGGL(chol_inv_base_kernel, dim3(1), dim3(BASE_THREADS), 0, c.st, c.A + o * n + o, c.U + o * n + o,
+        hipLaunchKernelGGL(chol_inv_base_kernel<BASE_TS>, dim3(1), dim3(BASE_THREADS), 0, c.st, c.A + o * n + o, c.U + o * n + o,
                            (int)m, n, c.flag);
         prof_end(PROF_FACTOR_BASE, c.st);
         PTQ_LAUNCH_CHECK();
