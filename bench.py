@@ -205,9 +205,11 @@ class Layer:
         return t, res
 
     def breakdown(self):
-        """One extra instrumented step: stage times from torch events on the
-        current stream (the library launches on it), kernel-class totals and
-        executed MFMA flops from the library's own event records."""
+        """Two extra steps: stage times from torch events on the current stream
+        (the library launches on it) in a step without per-kernel records, then
+        kernel-class totals and executed MFMA flops from the library's own
+        event records in a second, instrumented step (its hundreds of event
+        pairs around small launches would lengthen the stages)."""
         api, torch, cfg = self.api, self.torch, self.cfg
         n, o, N = cfg.inp, cfg.out, self.X.shape[0]
         dev = self.X.device
@@ -226,6 +228,24 @@ class Layer:
                     e["total_ms"] += ms
                     e["launches"] += cnt
                     e["mfma_flops"] += api.profile_flops(k)
+
+        api.profile_enable([])
+        self.H.zero_()
+        self.d.zero_()
+        ev[0].record()
+        api.hessian_accumulate(self.H, self.d, self.X, workspace=self.ws_h)
+        ev[1].record()
+        api.gptq_inverse_factor(self.H, self.d, damp=0.01, act_order=self.act_order, U=U, perm=self.perm,
+                                workspace=fws)
+        ev[2].record()
+        api.gptq_quantize_columns(self.W, U, self.perm if self.act_order else None, bits=self.bits, group_size=G,
+                                  block_size=BLOCK, codes=self.codes, scales=self.scales, g_idx=self.g_idx,
+                                  workspace=cws)
+        ev[3].record()
+        torch.cuda.synchronize()
+        t_h = ev[0].elapsed_time(ev[1]) / 1e3
+        t_u = ev[1].elapsed_time(ev[2]) / 1e3
+        t_c = ev[2].elapsed_time(ev[3]) / 1e3
 
         self.H.zero_()
         self.d.zero_()
@@ -254,9 +274,6 @@ class Layer:
             if not e["mfma_flops"]:
                 del e["mfma_flops"]
             del e["by_stage"]
-        t_h = ev[0].elapsed_time(ev[1]) / 1e3
-        t_u = ev[1].elapsed_time(ev[2]) / 1e3
-        t_c = ev[2].elapsed_time(ev[3]) / 1e3
         f_xtx, f_u = flops_xtx(N, n), flops_factor(n)
         f_inner, f_past = flops_updates(o, n)
         nb = (n + BLOCK - 1) // BLOCK
