@@ -12,9 +12,9 @@
 //  * gptq_block_kernel: 16 lanes per row, 8 columns per lane, the row's block
 //    in registers and U's B x B diagonal block in LDS. Step j: every lane
 //    rounds its copy of column j, the owner lane's error is broadcast across
-//    the row's 16 lanes (ds_bpermute), and each lane updates its 8 columns
-//    with one LDS read of U[j][..] (U's strictly lower part is zero, so
-//    columns <= j are untouched). Group maxima are lane-group reductions.
+//    the row's 16 lanes (a DPP row broadcast), and each lane updates its 8
+//    columns with one LDS read of U[j][..] (U's strictly lower part is zero,
+//    so columns <= j are untouched). Group maxima are lane-group reductions.
 //  * the trailing update W[:, b1:] -= E U[b0:b1, b1:], E being the block's
 //    errors, batched a second time: the block's errors update the rest of its
 //    2048-column super-block at once (fp32 MFMA, gemm_f32.hip), the columns
@@ -32,6 +32,15 @@ namespace ptq {
 namespace {
 
 constexpr int CPL = 8;     // columns per lane
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 // Super-block of the two-level lazy batch (a multiple of every block size).
 // On the 8192 x 28672 down_proj shape the column stage takes 75.0 ms at 512,
 // 63.8 at 1024 and 60.4 at 2048: the trailing GEMMs get 4x the depth per pass
@@ -116,8 +125,11 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
 #pragma unroll
     for (int c = 0; c < CPL; ++c) { cq[c] = 0.f; ce[c] = 0.f; }
 
-    const int lane = t & 63;
-    const int row_lane0 = lane - lr;              // first lane of this row in the wave
+    const int row_lane0 = (t & 63) - lr;          // first lane of this row in the wave
+    // 1 / U[j][j] of this lane's own columns (only the owner's error is kept)
+    float rd[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) rd[c] = rdiag[c0 + c];
     float scale = 0.f;
     float rscale = 0.f;     // 1 / scale (0 while scale is 0)
     float gmax = 0.f;       // symmetric: the group's max |w| (scale = gmax / qmax); zero-point: hi
@@ -167,64 +179,87 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
         }
     }
 
+    // Column j = CPL o + c belongs to lane o of its row (segment o). Group
+    // starts and the block's end fall on segment starts (groups of g <= B
+    // columns are multiples of 8, and bc is), so those checks run once per
+    // segment; the segments are unrolled at compile time, which makes the
+    // owner lane a constant (the DPP broadcast needs one).
+    int64_t gnext = (b0 + g - 1) / g;             // index of the next group to start in this block
+    // U[j][c0..c0+8) of the next column, read one column ahead (off the
+    // dependency chain of the error broadcast)
+    float4 un0 = *(const float4*)&Us[0][c0];
+    float4 un1 = *(const float4*)&Us[0][c0 + 4];
+    static_for<0, LPR>([&](auto oc) {
+        constexpr int o = decltype(oc)::value;
+        if (CPL * o >= bc) return;
+        if (((o * CPL < 64 ? (gs_lo >> ((o * CPL) & 63)) : (gs_hi >> ((o * CPL) & 63))) & 1) != 0) {
+            // the group [j, j+g) lies inside this block: lanes whose columns fall in it
+            const int j = CPL * o;
+            float loc = 0.f, lmn = 0.f;
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-        if (j < bc) {
-            if (((j < 64 ? (gs_lo >> (j & 63)) : (gs_hi >> (j & 63))) & 1) != 0) {
-                // the group [j, j+g) lies inside this block: lanes whose columns fall in it
-                float loc = 0.f, lmn = 0.f;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const int col = c0 + c;
-                    if (col >= j && col < j + g && col < bc) {
-                        if (ZP) {
-                            loc = fmaxf(loc, w[c]);
-                            lmn = fminf(lmn, w[c]);
-                        } else {
-                            loc = fmaxf(loc, fabsf(w[c]));
-                        }
+            for (int c = 0; c < CPL; ++c) {
+                const int col = c0 + c;
+                if (col >= j && col < j + g && col < bc) {
+                    if (ZP) {
+                        loc = fmaxf(loc, w[c]);
+                        lmn = fminf(lmn, w[c]);
+                    } else {
+                        loc = fmaxf(loc, fabsf(w[c]));
                     }
                 }
+            }
 #pragma unroll
-                for (int off = 1; off < LPR; off <<= 1) {
-                    loc = fmaxf(loc, __shfl_xor(loc, off, 64));
-                    if (ZP) lmn = fminf(lmn, __shfl_xor(lmn, off, 64));
-                }
-                gmax = loc;
-                glo = lmn;
-                if (ZP) zp_params(loc, lmn, qmax, scale, zero);
-                else scale = loc / qmax;
-                rscale = (scale > 0.f) ? 1.f / scale : 0.f;
-                if (live && lr == 0) {
-                    scales[r * ngroups + (b0 + j) / g] = scale;
-                    if (ZP) zeros[r * ngroups + (b0 + j) / g] = (int8_t)(int)zero;
-                }
+            for (int off = 1; off < LPR; off <<= 1) {
+                loc = fmaxf(loc, __shfl_xor(loc, off, 64));
+                if (ZP) lmn = fminf(lmn, __shfl_xor(lmn, off, 64));
             }
-            // round this lane's copy of column j (the owner's copy is the real one).
-            // The rounding decision is the fp64 one, x / (gmax / qmax) in double:
-            // the fp32 x * (1 / scale) is within 3 ulp of it, so only quotients
-            // that close to a half-integer (TIE_BAND, far wider) are recomputed
-            // in fp64.
-            const float x = w[j % CPL];
-            float q = 0.f;
-            if (scale > 0.f) {
-                const float t = x * rscale;
-                float rq = rintf(t);
-                if (fabsf(fabsf(t - rq) - 0.5f) < TIE_BAND) {
-                    const double s64 = ZP ? ((double)gmax - (double)glo) / (double)qmax : (double)gmax / (double)qmax;
-                    rq = (float)rint((double)x / s64);
-                }
-                q = ZP ? fminf(fmaxf(rq + zero, 0.f), qmax) : fminf(fmaxf(rq, -qmax - 1.f), qmax);
+            gmax = loc;
+            glo = lmn;
+            if (ZP) zp_params(loc, lmn, qmax, scale, zero);
+            else scale = loc / qmax;
+            rscale = (scale > 0.f) ? 1.f / scale : 0.f;
+            if (live && lr == 0) {
+                scales[r * ngroups + gnext] = scale;
+                if (ZP) zeros[r * ngroups + gnext] = (int8_t)(int)zero;
             }
-            const float e = (x - (q - zero) * scale) * rdiag[j];
-            const int owner = j / CPL;
-            const float eb = __shfl(e, row_lane0 + owner, 64);
-            const bool own = lr == owner;
-            cq[j % CPL] = own ? q : cq[j % CPL];
-            ce[j % CPL] = own ? e : ce[j % CPL];
+            ++gnext;
+        }
+        const bool own = lr == o;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int j = CPL * o + c;
+            const float4 u0 = un0, u1 = un1;
+            if (j + 1 < B) {
+                un0 = *(const float4*)&Us[j + 1][c0];
+                un1 = *(const float4*)&Us[j + 1][c0 + 4];
+            }
+            // round this lane's copy of column j (the owner's copy is the
+            // real one). The rounding decision is the fp64 one,
+            // x / (gmax / qmax) in double: the fp32 x * (1 / scale) is within
+            // 3 ulp of it, so only quotients that close to a half-integer
+            // (TIE_BAND, far wider) are recomputed in fp64. Scale 0 gives
+            // code 0 through the select (rscale is 0 then).
+            const float x = w[c];
+            const float tq = x * rscale;
+            float rq = rintf(tq);
+            if (fabsf(fabsf(tq - rq) - 0.5f) < TIE_BAND && scale > 0.f) {
+                const double s64 = ZP ? ((double)gmax - (double)glo) / (double)qmax : (double)gmax / (double)qmax;
+                rq = (float)rint((double)x / s64);
+            }
+            float q = ZP ? fminf(fmaxf(rq + zero, 0.f), qmax) : fminf(fmaxf(rq, -qmax - 1.f), qmax);
+            q = (scale > 0.f) ? q : 0.f;
+            const float e = (x - (q - zero) * scale) * rd[c];
+            // the owner's error to the row's lanes: with 16 lanes per row a
+            // DPP broadcast of lane o within each 16-lane row (row_newbcast),
+            // no LDS round trip; else a bpermute
+            float eb;
+            if constexpr (LPR == 16)
+                eb = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e), 0x150 + o, 0xF, 0xF, false));
+            else
+                eb = __shfl(e, row_lane0 + o, 64);
+            cq[c] = own ? q : cq[c];
+            ce[c] = own ? e : ce[c];
             e2 = own ? fmaf(e, e, e2) : e2;
-            const float4 u0 = *(const float4*)&Us[j][c0];
-            const float4 u1 = *(const float4*)&Us[j][c0 + 4];
             w[0] = fmaf(-eb, u0.x, w[0]);
             w[1] = fmaf(-eb, u0.y, w[1]);
             w[2] = fmaf(-eb, u0.z, w[2]);
@@ -234,7 +269,7 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             w[6] = fmaf(-eb, u1.z, w[6]);
             w[7] = fmaf(-eb, u1.w, w[7]);
         }
-    }
+    });
 
     if (!live) return;
     // errors for the trailing GEMM, codes, per-(row, block) sum of err^2
