@@ -283,7 +283,6 @@ constexpr int64_t SPLIT3_MIN = 3072;
 struct Ctx {
     float* A;      // damped (permuted) H, destroyed
     float* U;      // output
-    float* T;      // scratch, >= (n/2)^2 + slack
     uint16_t* Pa;  // split planes of the GEMM operands (NULL: fp32 GEMMs only)
     uint16_t* Pb;
     int64_t n;
@@ -291,17 +290,24 @@ struct Ctx {
     hipStream_t st;
 };
 
-int gemm(Ctx& c, int64_t M, int64_t N, int64_t K, const float* A, int la, int64_t lda, const float* B, int lb,
-         int64_t ldb, float* C, int64_t ldc, float alpha, int beta_one, int tri, int upper_only) {
+GemmArgs gemm_args(int64_t M, int64_t N, int64_t K, const float* A, int la, int64_t lda, const float* B, int lb,
+                   int64_t ldb, float* C, int64_t ldc, float alpha, int beta_one, int tri, int upper_only) {
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.A = A; g.lda = lda; g.layout_a = la;
     g.B = B; g.ldb = ldb; g.layout_b = lb;
     g.C = C; g.ldc = ldc;
     g.alpha = alpha; g.beta_one = beta_one; g.tri = tri; g.upper_only = upper_only;
+    return g;
+}
+
+bool split_size(const Ctx& c, const GemmArgs& g) {
+    return c.Pa && g.M >= SPLIT3_MIN && g.N >= SPLIT3_MIN && g.K >= SPLIT3_MIN;
+}
+
+int gemm(Ctx& c, const GemmArgs& g) {
     prof_begin(PROF_FACTOR_GEMM, c.st);
-    const bool split = c.Pa && M >= SPLIT3_MIN && N >= SPLIT3_MIN && K >= SPLIT3_MIN;
-    const int s = split ? launch_gemm_f32_split3(g, c.Pa, c.Pb, c.st) : launch_gemm_f32(g, c.st);
+    const int s = split_size(c, g) ? launch_gemm_f32_split3(g, c.Pa, c.Pb, c.st) : launch_gemm_f32(g, c.st);
     prof_end(PROF_FACTOR_GEMM, c.st);
     return s;
 }
@@ -327,14 +333,26 @@ int recurse(Ctx& c, int64_t o, int64_t m) {
     float* U22 = c.U + (o + n1) * n + (o + n1);
     PTQ_TRY(recurse(c, o + n1, n2));
     // R12 = H12 U22^T  (U22 stored [N][K], upper: entries with k < j are zero)
-    PTQ_TRY(gemm(c, n1, n2, n2, A12, A_MK, n, U22, B_NK, n, U12, n, 1.f, 0, TRI_B_UPPER_NK, 0));
-    // H11 -= R12 R12^T (upper tiles only)
-    PTQ_TRY(gemm(c, n1, n1, n2, U12, A_MK, n, U12, B_NK, n, A11, n, -1.f, 1, TRI_NONE, 1));
+    PTQ_TRY(gemm(c, gemm_args(n1, n2, n2, A12, A_MK, n, U22, B_NK, n, U12, n, 1.f, 0, TRI_B_UPPER_NK, 0)));
+    // H11 -= R12 R12^T (upper tiles only), and T = R12 U22 (U22 upper:
+    // B[k][j] = 0 for k > j) into A12, whose H12 is spent: T is [n1, n2] at
+    // row stride n, outside everything the recursion on H11 touches. Both
+    // read R12 and neither depends on the other, so on the split-operand path
+    // they are one launch with R12 split once.
+    const GemmArgs syrk = gemm_args(n1, n1, n2, U12, A_MK, n, U12, B_NK, n, A11, n, -1.f, 1, TRI_NONE, 1);
+    const GemmArgs tprod = gemm_args(n1, n2, n2, U12, A_MK, n, U22, B_KN, n, A12, n, 1.f, 0, TRI_B_UPPER_KN, 0);
+    if (split_size(c, syrk) && split_size(c, tprod)) {
+        prof_begin(PROF_FACTOR_GEMM, c.st);
+        const int s = launch_gemm_f32_split3_pair(syrk, tprod, c.Pa, c.Pb, c.st);
+        prof_end(PROF_FACTOR_GEMM, c.st);
+        PTQ_TRY(s);
+    } else {
+        PTQ_TRY(gemm(c, syrk));
+        PTQ_TRY(gemm(c, tprod));
+    }
     PTQ_TRY(recurse(c, o, n1));
-    // T = R12 U22 (U22 upper: B[k][j] = 0 for k > j), T is [n1, n2] with row stride n2
-    PTQ_TRY(gemm(c, n1, n2, n2, U12, A_MK, n, U22, B_KN, n, c.T, n2, 1.f, 0, TRI_B_UPPER_KN, 0));
     // U12 = -U11 T (U11 upper: A[i][k] = 0 for k < i)
-    PTQ_TRY(gemm(c, n1, n2, n1, U11, A_MK, n, c.T, B_KN, n2, U12, n, -1.f, 0, TRI_A_UPPER, 0));
+    PTQ_TRY(gemm(c, gemm_args(n1, n2, n1, U11, A_MK, n, A12, B_KN, n, U12, n, -1.f, 0, TRI_A_UPPER, 0)));
     return PTQ_OK;
 }
 
@@ -348,7 +366,6 @@ size_t factor_workspace_bytes(int64_t n) {
     Sizer z;
     z.take<float>((size_t)n * n);                          // A
     const int64_t half = split_half(n);
-    z.take<float>((size_t)half * half + 1024);             // T
     z.take<double>(1);                                     // lambda
     z.take<int>(1);                                        // flag
     z.take<int32_t>((size_t)n);                            // perm (when the caller passes none)
@@ -367,14 +384,13 @@ int run_inverse_factor(const float* H, const double* d, int64_t n, double damp, 
     c.st = st;
     c.A = ar.take<float>((size_t)n * n);
     const int64_t half = split_half(n);
-    c.T = ar.take<float>((size_t)half * half + 1024);
     double* lam = ar.take<double>(1);
     c.flag = ar.take<int>(1);
     int32_t* ptmp = ar.take<int32_t>((size_t)n);
     const bool split = half >= SPLIT3_MIN;
     c.Pa = split ? ar.take<uint16_t>(gemm_f32_split3_elems(half, half)) : nullptr;
     c.Pb = split ? ar.take<uint16_t>(gemm_f32_split3_elems(half, half)) : nullptr;
-    if (!c.A || !c.T || !lam || !c.flag || !ptmp || (split && (!c.Pa || !c.Pb))) {
+    if (!c.A || !lam || !c.flag || !ptmp || (split && (!c.Pa || !c.Pb))) {
         set_error("gptq_inverse_factor: workspace of %zu bytes, %zu needed", ws_bytes, factor_workspace_bytes(n));
         return PTQ_EWORKSPACE;
     }

@@ -161,6 +161,10 @@ int launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 // (N, K) bf16 elements of scratch (pb is unused when B is A's transpose view).
 size_t gemm_f32_split3_elems(int64_t rows, int64_t K);
 int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStream_t st);
+// Two such products in one launch: a0 = A op(A)^T (its planes in pa serve
+// both operands) and a1 with the same A (rows, depth, layout) and its own B
+// (planes in pb). EINVAL when the products do not fit that pattern.
+int launch_gemm_f32_split3_pair(const GemmArgs& a0, const GemmArgs& a1, uint16_t* pa, uint16_t* pb, hipStream_t st);
 
 // Stage 2 helpers (chol.hip)
 size_t factor_workspace_bytes(int64_t n);

@@ -88,6 +88,14 @@ struct Bf16GemmArgs {
     float* C; int64_t ldc;
     float alpha; int beta_one; int tri; int upper_only;
     int64_t tiles_m;
+    // EPI_GEMM pair: two products with one A operand (same rows and depth) in
+    // one launch; workgroups from grid0 on (a multiple of 8, so both keep the
+    // XCD order) compute the second, whose B, N and output differ (grid0 = 0:
+    // one product)
+    int64_t grid0;
+    const uint16_t* Bp2; int64_t b_plane2, N2, tiles_n2;
+    float* C2; int64_t ldc2;
+    float alpha2; int beta_one2; int tri2; int upper_only2;
 };
 
 template <int BMX>
@@ -465,7 +473,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int BMX, int EPI, int DKT, int NST, int NW, int MF>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g, int64_t nwork) {
+__global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16GemmArgs g_in, int64_t nwork) {
     using S = DStage<DKT>;
     using WTL = WaveTile<BMX, NW, MF>;
     using Sh = MfmaShape<MF>;
@@ -485,6 +493,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     constexpr int PANEL = BMX * ROWB;                  // bytes of one operand panel per stage
     static_assert(NST >= 2 && KSUB % 2 == 0 && NM >= NR && PER >= 1, "pipeline shape");
     static_assert(!BLK || (DKT == 64 && PER % 2 == 0), "panel-blocked copy layout");
+    Bf16GemmArgs g = g_in;
+    unsigned bid = blockIdx.x;
+    if constexpr (EPI == EPI_GEMM) {
+        if (g.grid0 > 0 && bid >= (unsigned)g.grid0) {
+            bid -= (unsigned)g.grid0;
+            g.Bp = g.Bp2; g.b_plane = g.b_plane2; g.N = g.N2; g.tiles_n = g.tiles_n2;
+            g.C = g.C2; g.ldc = g.ldc2;
+            g.alpha = g.alpha2; g.beta_one = g.beta_one2; g.tri = g.tri2; g.upper_only = g.upper_only2;
+        }
+    }
     int64_t i0, j0, L = 0;
     bool diag = false;
     if (EPI == EPI_HESSIAN) {
@@ -501,14 +519,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         // upper_only). Else plain row-major.
         int64_t tm, tn;
         if (g.tiles_m >= NXCD) {
-            const int64_t x = blockIdx.x % NXCD, i = blockIdx.x / NXCD, k = i / g.tiles_n;
+            const int64_t x = bid % NXCD, i = bid / NXCD, k = i / g.tiles_n;
             tm = NXCD * k + ((k & 1) ? NXCD - 1 - x : x);
             tn = i % g.tiles_n;
             if (tm >= g.tiles_m) return;
         } else {
-            if ((int64_t)blockIdx.x >= g.tiles_m * g.tiles_n) return;
-            tm = blockIdx.x / g.tiles_n;
-            tn = blockIdx.x % g.tiles_n;
+            if ((int64_t)bid >= g.tiles_m * g.tiles_n) return;
+            tm = bid / g.tiles_n;
+            tn = bid % g.tiles_n;
         }
         // B upper triangular [K][N]: a tile's depth grows with its column,
         // so columns go in descending order and the deepest tiles start first
@@ -943,16 +961,12 @@ double split3_mfma_flops(const Bf16GemmArgs& g) {
 
 size_t gemm_f32_split3_elems(int64_t rows, int64_t K) { return (size_t)(3 * split3_plane(rows, K)); }
 
-int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStream_t st) {
-    if (a.M <= 0 || a.N <= 0) return PTQ_OK;
-    if (a.K <= 0) return launch_gemm_f32(a, st);
+namespace {
+// split-operand kernel arguments of one product whose planes are pa (A) and pb (B)
+Bf16GemmArgs split3_args(const GemmArgs& a, const uint16_t* pa, const uint16_t* pb) {
     const int64_t kp = cdiv(a.K, 64) * 64;
-    const bool same = a.A == a.B && a.lda == a.ldb && a.M == a.N &&
-                      ((a.layout_a == A_MK && a.layout_b == B_NK) || (a.layout_a == A_KM && a.layout_b == B_KN));
-    PTQ_TRY(launch_split3(a.A, a.lda, a.layout_a == A_KM, a.M, a.K, pa, st));
-    if (!same) PTQ_TRY(launch_split3(a.B, a.ldb, a.layout_b == B_KN, a.N, a.K, pb, st));
     Bf16GemmArgs g{};
-    g.Ap = pa; g.Bp = same ? pa : pb;
+    g.Ap = pa; g.Bp = pb;
     g.a_plane = split3_plane(a.M, a.K); g.b_plane = split3_plane(a.N, a.K);
     g.pstride = split3_pstride(kp);
     g.K1 = kp; g.K2 = 0;
@@ -960,8 +974,50 @@ int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStr
     g.C = a.C; g.ldc = a.ldc;
     g.alpha = a.alpha; g.beta_one = a.beta_one; g.tri = a.tri; g.upper_only = a.upper_only;
     g.tiles_m = cdiv(a.M, 256); g.tiles_n = cdiv(a.N, 256);
-    const unsigned grid = (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n
-                                                       : g.tiles_m * g.tiles_n);
+    return g;
+}
+unsigned split3_grid(const Bf16GemmArgs& g) {
+    return (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n : g.tiles_m * g.tiles_n);
+}
+// op(B) is A's transpose view: one set of planes serves both operands
+bool same_operand(const GemmArgs& a) {
+    return a.A == a.B && a.lda == a.ldb && a.M == a.N &&
+           ((a.layout_a == A_MK && a.layout_b == B_NK) || (a.layout_a == A_KM && a.layout_b == B_KN));
+}
+}  // namespace
+
+int launch_gemm_f32_split3_pair(const GemmArgs& a0, const GemmArgs& a1, uint16_t* pa, uint16_t* pb, hipStream_t st) {
+    if (a0.A != a1.A || a0.lda != a1.lda || a0.layout_a != a1.layout_a || a0.M != a1.M || a0.K != a1.K ||
+        !same_operand(a0) || a0.K <= 0 || a0.M <= 0 || a0.N <= 0 || a1.N <= 0) {
+        set_error("split-operand GEMM pair: the products must share A (rows, depth, layout) and the first must be "
+                  "A op(A)^T");
+        return PTQ_EINVAL;
+    }
+    PTQ_TRY(launch_split3(a0.A, a0.lda, a0.layout_a == A_KM, a0.M, a0.K, pa, st));
+    PTQ_TRY(launch_split3(a1.B, a1.ldb, a1.layout_b == B_KN, a1.N, a1.K, pb, st));
+    Bf16GemmArgs g = split3_args(a0, pa, pa);
+    const Bf16GemmArgs g1 = split3_args(a1, pa, pb);
+    const unsigned grid0 = (unsigned)cdiv(split3_grid(g), NXCD) * NXCD, grid1 = split3_grid(g1);
+    g.grid0 = grid0;
+    g.Bp2 = g1.Bp; g.b_plane2 = g1.b_plane; g.N2 = g1.N; g.tiles_n2 = g1.tiles_n;
+    g.C2 = g1.C; g.ldc2 = g1.ldc;
+    g.alpha2 = g1.alpha; g.beta_one2 = g1.beta_one; g.tri2 = g1.tri; g.upper_only2 = g1.upper_only;
+    prof_begin(PROF_SPLIT3_GEMM, st, split3_mfma_flops(g) + split3_mfma_flops(g1));
+    const int rc = launch_direct<256, EPI_GEMM, 64, DNW, DMF>(g, 0, grid0 + grid1, 1, st);
+    prof_end(PROF_SPLIT3_GEMM, st);
+    PTQ_TRY(rc);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
+int launch_gemm_f32_split3(const GemmArgs& a, uint16_t* pa, uint16_t* pb, hipStream_t st) {
+    if (a.M <= 0 || a.N <= 0) return PTQ_OK;
+    if (a.K <= 0) return launch_gemm_f32(a, st);
+    const bool same = same_operand(a);
+    PTQ_TRY(launch_split3(a.A, a.lda, a.layout_a == A_KM, a.M, a.K, pa, st));
+    if (!same) PTQ_TRY(launch_split3(a.B, a.ldb, a.layout_b == B_KN, a.N, a.K, pb, st));
+    const Bf16GemmArgs g = split3_args(a, pa, same ? pa : pb);
+    const unsigned grid = split3_grid(g);
     prof_begin(PROF_SPLIT3_GEMM, st, split3_mfma_flops(g));
     const int rc = launch_direct<256, EPI_GEMM, 64, DNW, DMF>(g, 0, grid, 1, st);
     prof_end(PROF_SPLIT3_GEMM, st);
