@@ -49,6 +49,24 @@ def test_split3_layouts(gpu, M, N, K, la, lb):
         assert e < 1e-5 and e <= 4 * e32 + 1e-9, (e, e32)
 
 
+@pytest.mark.parametrize("beta_one", [0, 1])
+def test_split3_large_ragged(gpu, beta_one):
+    """A product of 33 x 17 output tiles with ragged edges on both sides and a
+    depth that is not a multiple of 64."""
+    from post_int4_weight_amd import api
+    M, N, K = 8200, 4100, 100
+    announce(f"gemm_f32_split3 large ragged M={M} N={N} K={K} beta_one={beta_one}")
+    g = torch.Generator().manual_seed(11 + beta_one)
+    A = torch.randn(M, K, generator=g)
+    B = torch.randn(N, K, generator=g)
+    C0 = torch.randn(M, N, generator=g)
+    C = _pad4(C0, gpu)
+    api._test_gemm_f32_split3(_pad4(A, gpu), _pad4(B, gpu), C, M, N, K, 0, 1, alpha=-1.0, beta_one=beta_one)
+    torch.cuda.synchronize()
+    want = (-(A.double() @ B.double().T) + (C0.double() if beta_one else 0)).numpy()
+    assert rel_fro(C[:, :N].cpu().double().numpy(), want) < 1e-5
+
+
 @pytest.mark.parametrize("tri", [1, 2, 3])
 def test_split3_triangles(gpu, tri):
     from post_int4_weight_amd import api
