@@ -128,15 +128,25 @@ __global__ void fill_int_kernel(int* p, int v) { *p = v; }
 // column c of S stays the identity's until step c (U[j][c] = 0 for c < j), so
 // one TS x TS register tile per thread holds M[i][k] = A[i][k] for k < j and
 // S[i][k] for k >= j: at step j column j turns into the identity's column,
-// and the step's update is the single M[i][k] -= R[i][j] V[k] with
-// V[k] = R[k][j] (k < j) or U[j][k] (k >= j). Only column j of A and row j of
-// S go through LDS, so a step is one barrier, three TS-float LDS reads and
-// TS^2 FMAs per thread (rows already final skip the update). A is symmetric
-// and S is upper triangular (S[i][c] = 0 for i > c), and every value that
-// goes through LDS comes from a tile on or above the diagonal, so only those
-// tiles have a thread: TB (TB + 1) / 2 threads (the ones past that count only
-// join the barriers). Outside m the block is padded with the identity. U is
-// written on and above the diagonal of the block (the caller zeroes the rest).
+// and the step's update is the single M[i][k] -= Ri[i] V[k] with
+// Ri[i] = R[i][j] (0 for i >= j) and V[k] = R[k][j] (k < j) or U[j][k]
+// (k >= j). A is symmetric and S is upper triangular, and every value the
+// steps need comes from a tile on or above the diagonal, so only those tiles
+// have a thread: TB (TB + 1) / 2 threads (the ones past that count only join
+// the barriers).
+//
+// The sweep goes one tile column (TS = 4 steps) at a time, in two phases
+// between barriers. The tiles holding the block's 4 columns of A and 4 rows
+// of S publish them as they stand before the block. Phase 1: thread x < BASE
+// derives, for row x, Ri of each of the 4 steps and, for column x, V of each
+// step, by taking the block's steps on those few values in the order and
+// with the operations the tiles themselves would apply (so U is the same,
+// bit for bit, as with one step and one barrier per column). Phase 2: every
+// tile takes the 4 steps on its registers from the published Ri and V. Two
+// barriers per 4 columns instead of one per column: the sweep is bound by
+// each step's latency chain (barrier, LDS read, pivot, update, publish).
+// Outside m the block is padded with the identity. U is written on and
+// above the diagonal of the block (the caller zeroes the rest).
 // Bit 0 of *flag: non-positive pivot; bit 1: NaN.
 template <int TS>
 constexpr int base_threads() {
@@ -146,10 +156,14 @@ template <int TS>
 __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const float* __restrict__ A,
                                                                           float* __restrict__ U, int m, int64_t ld,
                                                                           int* flag) {
+    static_assert(TS == 4, "a block of the sweep is one tile column, stored as float4 rows in LDS");
     constexpr int TB = BASE / TS;              // TS x TS tiles per block row
-    constexpr int NV = TS / 4;                 // float4 pieces per tile row
-    __shared__ __attribute__((aligned(16))) float colb[BASE][BASE];   // colb[j][i] = A[i][j] at step j
-    __shared__ __attribute__((aligned(16))) float rowb[BASE][BASE];   // rowb[j][c] = S[j][c] at step j
+    // per block jb (columns / rows 4 jb .. 4 jb + 3), index [x][t] for column
+    // or row 4 jb + t:
+    __shared__ __attribute__((aligned(16))) float colb[BASE][TS];   // A[x][4jb+t] before the block
+    __shared__ __attribute__((aligned(16))) float rowb[BASE][TS];   // tile value at row 4jb+t, column x, before it
+    __shared__ __attribute__((aligned(16))) float Rb[BASE][TS];     // Ri[x] of step 4jb+t
+    __shared__ __attribute__((aligned(16))) float Vb[BASE][TS];     // V[x] of step 4jb+t
     const int t = threadIdx.x;
     // this thread's tile (rows TS*ib.., columns TS*kb.., ib <= kb): the t-th
     // of the upper triangle's tiles in row-major order
@@ -172,89 +186,112 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
             a[di][dk] = A[(int64_t)r * ld + c];
             if (i >= m || k >= m) a[di][dk] = (i == k) ? 1.f : 0.f;
         }
-    auto put = [&](float* dst, const float (&v)[TS]) {
+    // the tiles in tile column jbn publish its 4 columns of A, the tiles in
+    // tile row jbn its 4 rows (as they stand: left of the block they are S's
+    // identity part, which phase 1 takes from the rule, not from here)
+    auto publish = [&](int jbn) {
+        if (!live) return;
+        if (kb == jbn) {
 #pragma unroll
-        for (int h = 0; h < NV; ++h) *(float4*)(dst + 4 * h) = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
-    };
-    auto get = [&](const float* src, float (&v)[TS]) {
+            for (int q = 0; q < TS; ++q) *(float4*)&colb[i0 + q][0] = make_float4(a[q][0], a[q][1], a[q][2], a[q][3]);
+        }
+        if (ib == jbn) {
 #pragma unroll
-        for (int h = 0; h < NV; ++h) {
-            const float4 x = *(const float4*)(src + 4 * h);
-            v[4 * h] = x.x; v[4 * h + 1] = x.y; v[4 * h + 2] = x.z; v[4 * h + 3] = x.w;
+            for (int q = 0; q < TS; ++q) *(float4*)&rowb[k0 + q][0] = make_float4(a[0][q], a[1][q], a[2][q], a[3][q]);
         }
     };
-    // row BASE - 1 of S is the identity's
-    if (live && kb == TB - 1) {
-        float v[TS];
-#pragma unroll
-        for (int q = 0; q < TS; ++q) v[q] = a[q][TS - 1];
-        put(&colb[BASE - 1][i0], v);
-    }
-    if (live && ib == TB - 1) {
-        float v[TS];
-#pragma unroll
-        for (int q = 0; q < TS; ++q) v[q] = (kb == TB - 1 && q == TS - 1) ? 1.f : 0.f;
-        put(&rowb[BASE - 1][k0], v);
-    }
+    publish(TB - 1);
     for (int jb = TB - 1; jb >= 0; --jb) {
+        const int jb0 = TS * jb;
+        __syncthreads();
+        if (t < BASE) {
+            // Phase 1, x = t. c[u] = A[x][jb0+u] (row x of the block's
+            // columns), s[u] = row jb0+u of the tile at column x, d[u][v] =
+            // A[jb0+v][jb0+u] (the diagonal tile, column u, row v), each taken
+            // through the block's steps as the tile holding it would.
+            const int x = t;
+            float c[TS], s[TS], d[TS][TS];
+            {
+                const float4 cv = *(const float4*)&colb[x][0];
+                const float4 sv = *(const float4*)&rowb[x][0];
+                c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
+                s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
 #pragma unroll
-        for (int dj = TS - 1; dj >= 0; --dj) {
-            const int j = TS * jb + dj;
-            __syncthreads();
-            float piv = colb[j][j];
-            float civ[TS], ckv[TS], rjv[TS];
-            get(&colb[j][i0], civ);
-            get(&colb[j][k0], ckv);
-            get(&rowb[j][k0], rjv);
-            if (!(piv > 0.f)) {
-                if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
-                piv = 1.f;
+                for (int v = 0; v < TS; ++v) {
+                    const float4 dv = *(const float4*)&colb[jb0 + v][0];
+                    d[0][v] = dv.x; d[1][v] = dv.y; d[2][v] = dv.z; d[3][v] = dv.w;
+                }
             }
-            // 1 / sqrt(piv): the hardware reciprocal square root and one Newton
-            // step (within about an ulp, as IEEE sqrt then divide; their dozens
-            // of dependent instructions sat on every step's critical path)
-            const float r0 = __builtin_amdgcn_rsqf(piv);
-            const float r = r0 * fmaf(-0.5f * piv, r0 * r0, 1.5f);
-            float Ri[TS], V[TS];
+            float Rx[TS], Vx[TS];
+#pragma unroll
+            for (int tt = TS - 1; tt >= 0; --tt) {
+                const int j = jb0 + tt;
+                float piv = d[tt][tt];
+                if (!(piv > 0.f)) {
+                    if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
+                    piv = 1.f;
+                }
+                // 1 / sqrt(piv): the hardware reciprocal square root and one
+                // Newton step (within about an ulp, as IEEE sqrt then divide;
+                // their dozens of dependent instructions sat on every step's
+                // critical path)
+                const float r0 = __builtin_amdgcn_rsqf(piv);
+                const float r = r0 * fmaf(-0.5f * piv, r0 * r0, 1.5f);
+                // row x's Ri and column x's V of step j: the S row is the
+                // identity's up to column j (its columns turn at their own step)
+                Rx[tt] = (x < j) ? c[tt] * r : 0.f;
+                Vx[tt] = (x < j) ? c[tt] * r : ((x == j) ? 1.f : s[tt]) * r;
+#pragma unroll
+                for (int u = 0; u < tt; ++u) {
+                    // column jb0+u < j of A and row jb0+u of S under step j;
+                    // R[jb0+u][j] = d[tt][u] r is that column's V and that
+                    // row's Ri
+                    const float Rdu = d[tt][u] * r;
+                    if (TS * (x / TS) < j) c[u] -= Rx[tt] * Rdu;   // the tile holding (x, jb0+u) updates iff its first row is above j
+#pragma unroll
+                    for (int v = 0; v < tt; ++v) {
+                        const float Rdv = d[tt][v] * r;
+                        d[u][v] -= Rdv * Rdu;
+                    }
+                    if (x == j) s[u] = 0.f;                        // column j turns into the identity's
+                    s[u] -= Rdu * Vx[tt];
+                }
+            }
+            *(float4*)&Rb[x][0] = make_float4(Rx[0], Rx[1], Rx[2], Rx[3]);
+            *(float4*)&Vb[x][0] = make_float4(Vx[0], Vx[1], Vx[2], Vx[3]);
+        }
+        __syncthreads();
+        if (live) {
+            // Phase 2: the block's 4 steps on this tile
+            float Ri[TS][TS], V[TS][TS];   // [q][tt]: rows i0+q / columns k0+q at step jb0+tt
 #pragma unroll
             for (int q = 0; q < TS; ++q) {
-                Ri[q] = (i0 + q < j) ? civ[q] * r : 0.f;
-                V[q] = (k0 + q < j) ? ckv[q] * r : rjv[q] * r;
+                const float4 rv = *(const float4*)&Rb[i0 + q][0];
+                const float4 vv = *(const float4*)&Vb[k0 + q][0];
+                Ri[q][0] = rv.x; Ri[q][1] = rv.y; Ri[q][2] = rv.z; Ri[q][3] = rv.w;
+                V[q][0] = vv.x; V[q][1] = vv.y; V[q][2] = vv.z; V[q][3] = vv.w;
             }
-            if (!live) continue;
-            if (kb == jb) {   // column j of A is spent: it becomes column j of S (the identity's)
 #pragma unroll
-                for (int di = 0; di < TS; ++di) a[di][dj] = (i0 + di == j) ? 1.f : 0.f;
-            }
-            if (ib == jb) {   // row j of S is final: U[j][k] for k >= j
+            for (int tt = TS - 1; tt >= 0; --tt) {
+                const int j = jb0 + tt;
+                if (kb == jb) {   // column j of A is spent: it becomes column j of S (the identity's)
 #pragma unroll
-                for (int q = 0; q < TS; ++q)
-                    if (k0 + q >= j) a[dj][q] = V[q];
-            }
-            if (i0 < j) {   // rows >= j are final (Ri = 0): whole waves skip the update as j falls
-#pragma unroll
-                for (int di = 0; di < TS; ++di)
-#pragma unroll
-                    for (int q = 0; q < TS; ++q) a[di][q] -= Ri[di] * V[q];
-            }
-            if (j > 0) {   // publish column j-1 of A and row j-1 of S (final after this update)
-                const int djn = (dj + TS - 1) % TS;
-                const int jn = j - 1, jbn = jn / TS;
-                if (kb == jbn) {
-                    float v[TS];
-#pragma unroll
-                    for (int q = 0; q < TS; ++q) v[q] = a[q][djn];
-                    put(&colb[jn][i0], v);
+                    for (int di = 0; di < TS; ++di) a[di][tt] = (i0 + di == j) ? 1.f : 0.f;
                 }
-                if (ib == jbn) {
-                    // S[jn][k]: the identity's left of column j, M from column j on
-                    float v[TS];
+                if (ib == jb) {   // row j of S is final: U[j][k] for k >= j
 #pragma unroll
-                    for (int q = 0; q < TS; ++q) v[q] = (k0 + q < j) ? ((k0 + q == jn) ? 1.f : 0.f) : a[djn][q];
-                    put(&rowb[jn][k0], v);
+                    for (int q = 0; q < TS; ++q)
+                        if (k0 + q >= j) a[tt][q] = V[q][tt];
+                }
+                if (i0 < j) {   // rows >= j are final (Ri = 0): whole waves skip the update as j falls
+#pragma unroll
+                    for (int di = 0; di < TS; ++di)
+#pragma unroll
+                        for (int q = 0; q < TS; ++q) a[di][q] -= Ri[di][tt] * V[q][tt];
                 }
             }
         }
+        if (jb > 0) publish(jb - 1);
     }
     if (!live) return;
 #pragma unroll
