@@ -152,18 +152,20 @@ template <int TS>
 constexpr int base_threads() {
     return ((BASE / TS) * (BASE / TS + 1) / 2 + 63) / 64 * 64;
 }
-template <int TS>
+template <int TS, int CB>
 __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const float* __restrict__ A,
                                                                           float* __restrict__ U, int m, int64_t ld,
                                                                           int* flag) {
-    static_assert(TS == 4, "a block of the sweep is one tile column, stored as float4 rows in LDS");
+    static_assert(TS == 4 && CB % TS == 0 && BASE % CB == 0, "rounds of whole tile columns, float4 pieces in LDS");
     constexpr int TB = BASE / TS;              // TS x TS tiles per block row
-    // per block jb (columns / rows 4 jb .. 4 jb + 3), index [x][t] for column
-    // or row 4 jb + t:
-    __shared__ __attribute__((aligned(16))) float colb[BASE][TS];   // A[x][4jb+t] before the block
-    __shared__ __attribute__((aligned(16))) float rowb[BASE][TS];   // tile value at row 4jb+t, column x, before it
-    __shared__ __attribute__((aligned(16))) float Rb[BASE][TS];     // Ri[x] of step 4jb+t
-    __shared__ __attribute__((aligned(16))) float Vb[BASE][TS];     // V[x] of step 4jb+t
+    constexpr int NB = BASE / CB;              // rounds
+    constexpr int TPR = CB / TS;               // tile columns per round
+    // per round jb (columns / rows CB jb .. CB jb + CB - 1), index [x][t]
+    // for column or row CB jb + t:
+    __shared__ __attribute__((aligned(16))) float colb[BASE][CB];   // A[x][CBjb+t] before the round
+    __shared__ __attribute__((aligned(16))) float rowb[BASE][CB];   // tile value at row CBjb+t, column x, before it
+    __shared__ __attribute__((aligned(16))) float Rb[BASE][CB];     // Ri[x] of step CBjb+t
+    __shared__ __attribute__((aligned(16))) float Vb[BASE][CB];     // V[x] of step CBjb+t
     const int t = threadIdx.x;
     // this thread's tile (rows TS*ib.., columns TS*kb.., ib <= kb): the t-th
     // of the upper triangle's tiles in row-major order
@@ -191,18 +193,20 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
     // identity part, which phase 1 takes from the rule, not from here)
     auto publish = [&](int jbn) {
         if (!live) return;
-        if (kb == jbn) {
+        if (kb / TPR == jbn) {
+            const int o = TS * (kb % TPR);
 #pragma unroll
-            for (int q = 0; q < TS; ++q) *(float4*)&colb[i0 + q][0] = make_float4(a[q][0], a[q][1], a[q][2], a[q][3]);
+            for (int q = 0; q < TS; ++q) *(float4*)&colb[i0 + q][o] = make_float4(a[q][0], a[q][1], a[q][2], a[q][3]);
         }
-        if (ib == jbn) {
+        if (ib / TPR == jbn) {
+            const int o = TS * (ib % TPR);
 #pragma unroll
-            for (int q = 0; q < TS; ++q) *(float4*)&rowb[k0 + q][0] = make_float4(a[0][q], a[1][q], a[2][q], a[3][q]);
+            for (int q = 0; q < TS; ++q) *(float4*)&rowb[k0 + q][o] = make_float4(a[0][q], a[1][q], a[2][q], a[3][q]);
         }
     };
-    publish(TB - 1);
-    for (int jb = TB - 1; jb >= 0; --jb) {
-        const int jb0 = TS * jb;
+    publish(NB - 1);
+    for (int jb = NB - 1; jb >= 0; --jb) {
+        const int jb0 = CB * jb;
         __syncthreads();
         if (t < BASE) {
             // Phase 1, x = t. c[u] = A[x][jb0+u] (row x of the block's
@@ -210,21 +214,22 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
             // A[jb0+v][jb0+u] (the diagonal tile, column u, row v), each taken
             // through the block's steps as the tile holding it would.
             const int x = t;
-            float c[TS], s[TS], d[TS][TS];
-            {
-                const float4 cv = *(const float4*)&colb[x][0];
-                const float4 sv = *(const float4*)&rowb[x][0];
-                c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
-                s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
+            float c[CB], s[CB], d[CB][CB];
 #pragma unroll
-                for (int v = 0; v < TS; ++v) {
-                    const float4 dv = *(const float4*)&colb[jb0 + v][0];
-                    d[0][v] = dv.x; d[1][v] = dv.y; d[2][v] = dv.z; d[3][v] = dv.w;
+            for (int h = 0; h < CB; h += 4) {
+                const float4 cv = *(const float4*)&colb[x][h];
+                const float4 sv = *(const float4*)&rowb[x][h];
+                c[h] = cv.x; c[h + 1] = cv.y; c[h + 2] = cv.z; c[h + 3] = cv.w;
+                s[h] = sv.x; s[h + 1] = sv.y; s[h + 2] = sv.z; s[h + 3] = sv.w;
+#pragma unroll
+                for (int v = 0; v < CB; ++v) {
+                    const float4 dv = *(const float4*)&colb[jb0 + v][h];
+                    d[h][v] = dv.x; d[h + 1][v] = dv.y; d[h + 2][v] = dv.z; d[h + 3][v] = dv.w;
                 }
             }
-            float Rx[TS], Vx[TS];
+            float Rx[CB], Vx[CB];
 #pragma unroll
-            for (int tt = TS - 1; tt >= 0; --tt) {
+            for (int tt = CB - 1; tt >= 0; --tt) {
                 const int j = jb0 + tt;
                 float piv = d[tt][tt];
                 if (!(piv > 0.f)) {
@@ -257,31 +262,37 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
                     s[u] -= Rdu * Vx[tt];
                 }
             }
-            *(float4*)&Rb[x][0] = make_float4(Rx[0], Rx[1], Rx[2], Rx[3]);
-            *(float4*)&Vb[x][0] = make_float4(Vx[0], Vx[1], Vx[2], Vx[3]);
+#pragma unroll
+            for (int h = 0; h < CB; h += 4) {
+                *(float4*)&Rb[x][h] = make_float4(Rx[h], Rx[h + 1], Rx[h + 2], Rx[h + 3]);
+                *(float4*)&Vb[x][h] = make_float4(Vx[h], Vx[h + 1], Vx[h + 2], Vx[h + 3]);
+            }
         }
         __syncthreads();
-        if (live) {
-            // Phase 2: the block's 4 steps on this tile
-            float Ri[TS][TS], V[TS][TS];   // [q][tt]: rows i0+q / columns k0+q at step jb0+tt
+        if (live && i0 < jb0 + CB) {
+            // Phase 2: the round's steps on this tile (tiles whose rows are
+            // all at or below the round only wait: nothing of them changes)
+            float Ri[TS][CB], V[TS][CB];   // [q][tt]: rows i0+q / columns k0+q at step jb0+tt
 #pragma unroll
-            for (int q = 0; q < TS; ++q) {
-                const float4 rv = *(const float4*)&Rb[i0 + q][0];
-                const float4 vv = *(const float4*)&Vb[k0 + q][0];
-                Ri[q][0] = rv.x; Ri[q][1] = rv.y; Ri[q][2] = rv.z; Ri[q][3] = rv.w;
-                V[q][0] = vv.x; V[q][1] = vv.y; V[q][2] = vv.z; V[q][3] = vv.w;
-            }
+            for (int q = 0; q < TS; ++q)
 #pragma unroll
-            for (int tt = TS - 1; tt >= 0; --tt) {
-                const int j = jb0 + tt;
-                if (kb == jb) {   // column j of A is spent: it becomes column j of S (the identity's)
-#pragma unroll
-                    for (int di = 0; di < TS; ++di) a[di][tt] = (i0 + di == j) ? 1.f : 0.f;
+                for (int h = 0; h < CB; h += 4) {
+                    const float4 rv = *(const float4*)&Rb[i0 + q][h];
+                    const float4 vv = *(const float4*)&Vb[k0 + q][h];
+                    Ri[q][h] = rv.x; Ri[q][h + 1] = rv.y; Ri[q][h + 2] = rv.z; Ri[q][h + 3] = rv.w;
+                    V[q][h] = vv.x; V[q][h + 1] = vv.y; V[q][h + 2] = vv.z; V[q][h + 3] = vv.w;
                 }
-                if (ib == jb) {   // row j of S is final: U[j][k] for k >= j
+#pragma unroll
+            for (int tt = CB - 1; tt >= 0; --tt) {
+                const int j = jb0 + tt, dj = tt % TS;
+                if (kb == j / TS) {   // column j of A is spent: it becomes column j of S (the identity's)
+#pragma unroll
+                    for (int di = 0; di < TS; ++di) a[di][dj] = (i0 + di == j) ? 1.f : 0.f;
+                }
+                if (ib == j / TS) {   // row j of S is final: U[j][k] for k >= j
 #pragma unroll
                     for (int q = 0; q < TS; ++q)
-                        if (k0 + q >= j) a[tt][q] = V[q][tt];
+                        if (k0 + q >= j) a[dj][q] = V[q][tt];
                 }
                 if (i0 < j) {   // rows >= j are final (Ri = 0): whole waves skip the update as j falls
 #pragma unroll
@@ -309,6 +320,7 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
 // 1024 threads; leaving out the tiles below the diagonal took it to 55 us.
 constexpr int BASE_TS = 4;
 constexpr int BASE_THREADS = base_threads<BASE_TS>();
+constexpr int BASE_CB = 4;   // steps per round of the sweep (8: 54 us per block, phase 1 grows as CB^2)
 
 // GEMMs with all of M, N, K at least this large run on the bf16 MFMA from
 // three-term splits of their operands (fp32 accuracy, gemm_bf16.hip); the
@@ -354,7 +366,7 @@ int recurse(Ctx& c, int64_t o, int64_t m) {
     const int64_t n = c.n;
     if (m <= BASE) {
         prof_begin(PROF_FACTOR_BASE, c.st);
-        hipLaunchKernelGGL(chol_inv_base_kernel<BASE_TS>, dim3(1), dim3(BASE_THREADS), 0, c.st, c.A + o * n + o, c.U + o * n + o,
+        hipLaunchKernelGGL((chol_inv_base_kernel<BASE_TS, BASE_CB>), dim3(1), dim3(BASE_THREADS), 0, c.st, c.A + o * n + o, c.U + o * n + o,
                            (int)m, n, c.flag);
         prof_end(PROF_FACTOR_BASE, c.st);
         PTQ_LAUNCH_CHECK();
