@@ -16,10 +16,11 @@
 //    columns with one LDS read of U[j][..] (U's strictly lower part is zero,
 //    so columns <= j are untouched). Group maxima are lane-group reductions.
 //  * the trailing update W[:, b1:] -= E U[b0:b1, b1:], E being the block's
-//    errors, batched a second time: the block's errors update the rest of its
-//    2048-column super-block at once (fp32 MFMA, gemm_f32.hip), the columns
-//    past the super-block get all of its errors in one K = 2048 GEMM (on the
-//    bf16 MFMA from three-term operand splits when large, gemm_bf16.hip).
+//    errors, batched twice more: the block's errors update the rest of its
+//    512-column mid-block at once and a mid-block's errors the rest of its
+//    2048-column super-block (fp32 MFMA, gemm_f32.hip); the columns past the
+//    super-block get all of its errors in one K = 2048 GEMM (on the bf16 MFMA
+//    from three-term operand splits when large, gemm_bf16.hip).
 // Act-order is a gather of W's columns into processing order up front; codes
 // are written straight back to their original column positions.
 #include "common.hpp"
@@ -363,6 +364,13 @@ __global__ void zero_int_kernel(int* p) { *p = 0; }
 // MFMA from three-term bf16 splits of E and U's rows (fp32 accuracy,
 // gemm_bf16.hip); smaller ones on the fp32 MFMA GEMM.
 constexpr int64_t TRAIL_SPLIT3_MIN = 2048;
+// Mid-blocks of the three-level lazy batch: inside a super-block, a block's
+// errors update only the rest of its mid-block (depth B); at each mid-block's
+// end its errors update the rest of the super-block at depth MID_COLS. On the
+// down_proj shape the column stage takes about 1.3 ms less than with two
+// levels (256- and 1024-column mid-blocks: 0.5 ms more than 512; the
+// mid-block updates on the split-operand GEMM: no faster than on fp32).
+constexpr int64_t MID_COLS = 512;
 
 template <int B, bool ZP>
 int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float qmax, const int32_t* perm,
@@ -371,13 +379,17 @@ int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float q
     constexpr int RPW = NTH / (B / CPL);
     const unsigned grid = (unsigned)cdiv(out, RPW);
     // W_cur[:, c1:] -= Err[:, 0:K] U[k0:k0+K, c1:c2]
-    // Two levels of lazy batching: inside a super-block of SB columns each
-    // block's errors update only the rest of the super-block; the columns past
-    // it receive the whole super-block's errors in one GEMM with K = SB (the
-    // same sums, regrouped). A group that spans blocks must not straddle a
-    // super-block (its scale reads columns ahead), so such group sizes that do
-    // not divide SB_COLS fall back to single blocks.
+    // Three levels of lazy batching: inside a mid-block of MB columns each
+    // block's errors update only the rest of the mid-block; at a mid-block's
+    // end its errors update the rest of its super-block of SB columns; the
+    // columns past a super-block receive all of its errors in one GEMM with
+    // K = SB (the same sums, regrouped). A group that spans blocks must not
+    // straddle a super-block or a mid-block (its scale reads columns ahead), so
+    // such group sizes that do not divide SB_COLS fall back to single blocks,
+    // and those that do not divide MID_COLS to two levels.
     const int64_t SB = (g > B && SB_COLS % g != 0) ? B : SB_COLS;
+    // the same for mid-blocks (without them: two levels)
+    const int64_t MB = (g > B && MID_COLS % g != 0) ? SB : std::min<int64_t>(MID_COLS, SB);
     auto update = [&](int64_t k0, int64_t K, int64_t c1, int64_t c2, int kernel) {
         GemmArgs a{};
         a.M = out; a.N = c2 - c1; a.K = K;
@@ -393,19 +405,23 @@ int run_blocks(float* Wc, int64_t out, int64_t n, const float* U, int g, float q
     };
     for (int64_t s0 = 0; s0 < n; s0 += SB) {
         const int64_t s1 = std::min<int64_t>(n, s0 + SB);
-        for (int64_t b0 = s0; b0 < s1; b0 += B) {
-            const int bc = (int)std::min<int64_t>(B, s1 - b0);
-            prof_begin(PROF_BLOCK_LOOP, st);
-            uint64_t gs[2] = {0, 0};   // group starts inside the block (groups of g <= B)
-            if (g <= B)
-                for (int j = 0; j < bc; j += g) gs[j >> 6] |= (uint64_t)1 << (j & 63);
-            hipLaunchKernelGGL((gptq_block_kernel<B, ZP>), dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc, g,
-                               qmax, perm, codes, scales, zeros, ngroups, gmaxes, E + (b0 - s0), (int)SB, err2,
-                               nblocks, flag, gs[0], gs[1]);
-            prof_end(PROF_BLOCK_LOOP, st);
-            PTQ_LAUNCH_CHECK();
-            const int64_t b1 = b0 + bc;
-            if (b1 < s1) PTQ_TRY(update(b0, bc, b1, s1, PROF_INNER_GEMM));
+        for (int64_t m0 = s0; m0 < s1; m0 += MB) {
+            const int64_t m1 = std::min<int64_t>(s1, m0 + MB);
+            for (int64_t b0 = m0; b0 < m1; b0 += B) {
+                const int bc = (int)std::min<int64_t>(B, m1 - b0);
+                prof_begin(PROF_BLOCK_LOOP, st);
+                uint64_t gs[2] = {0, 0};   // group starts inside the block (groups of g <= B)
+                if (g <= B)
+                    for (int j = 0; j < bc; j += g) gs[j >> 6] |= (uint64_t)1 << (j & 63);
+                hipLaunchKernelGGL((gptq_block_kernel<B, ZP>), dim3(grid), dim3(NTH), 0, st, Wc, out, n, U, b0, bc,
+                                   g, qmax, perm, codes, scales, zeros, ngroups, gmaxes, E + (b0 - s0), (int)SB,
+                                   err2, nblocks, flag, gs[0], gs[1]);
+                prof_end(PROF_BLOCK_LOOP, st);
+                PTQ_LAUNCH_CHECK();
+                const int64_t b1 = b0 + bc;
+                if (b1 < m1) PTQ_TRY(update(b0, bc, b1, m1, PROF_INNER_GEMM));
+            }
+            if (m1 < s1) PTQ_TRY(update(m0, m1 - m0, m1, s1, PROF_INNER_GEMM));
         }
         if (s1 < n) PTQ_TRY(update(s0, s1 - s0, s1, n, PROF_TRAIL_GEMM));
     }
