@@ -6,9 +6,13 @@ Parity with the fp64 oracle:
   * d against the oracle's streamed column sums of squares, H on sampled
     blocks against X's columns;
   * U in full: the oracle factors the device's H (fp64 copy, + lambda I) by
-    its own route (inv, Cholesky, transpose) — 8192^2 takes seconds;
+    its own route (reversed Cholesky, triangular inverse) — 8192^2 takes
+    seconds;
   * the column loop on 16 sampled rows run by the oracle with ITS U
-    (rows are independent in the loop): >= 99% codes, output error within 1%.
+    (rows are independent in the loop): >= 99% codes, output error within 1%;
+  * the same with act-order: the permutation equal to the stable sort of the
+    oracle's fp64 keys, U of the permuted damped H in full, the sampled rows'
+    codes back in the original column order and g_idx exact.
 
 Report ("AWQ alpha search ... report RTN vs AWQ vs GPTQ output error on a
 held-out X with the channel sigma redrawn"): RTN, AWQ at the searched alpha
@@ -32,6 +36,17 @@ SAMPLE_ROWS = 16
 
 
 @pytest.fixture(scope="module")
+def qkv_d0(qkv):
+    """The oracle's fp64 column sums of squares of X, streamed in row chunks."""
+    cfg, W, X, H, d = qkv
+    d0 = np.zeros(cfg.inp)
+    for r0 in range(0, cfg.rows, 16384):
+        xc = X[r0:r0 + 16384].cpu().float().numpy().astype(np.float64)
+        d0 += np.sum(xc * xc, axis=0)
+    return d0
+
+
+@pytest.fixture(scope="module")
 def qkv(gpu):
     from post_int4_weight_amd import api
     cfg = inputs.CONFIGS["llama70b_qkv_proj"]
@@ -43,15 +58,12 @@ def qkv(gpu):
     return cfg, W, X, H, d
 
 
-def test_qkv_gptq_fullsize(qkv):
+def test_qkv_gptq_fullsize(qkv, qkv_d0):
     from post_int4_weight_amd import api
     cfg, W, X, H, d = qkv
     n, out = cfg.inp, cfg.out
     announce("qkv gptq 4-bit: d, H blocks, full U, sampled rows")
-    d0 = np.zeros(n)
-    for r0 in range(0, cfg.rows, 16384):
-        xc = X[r0:r0 + 16384].cpu().float().numpy().astype(np.float64)
-        d0 += np.sum(xc * xc, axis=0)
+    d0 = qkv_d0
     assert np.max(np.abs(d.cpu().numpy() - d0) / d0) <= 1e-12
     for c0 in (0, n - 512):
         H0b, _ = oracle.proxy_hessian(to64(X[:, c0:c0 + 512].cpu()), chunk_rows=16384)
@@ -85,6 +97,49 @@ def test_qkv_gptq_fullsize(qkv):
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
     print(f"[oracle] {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal, relative output "
           f"error {e_gpu:.6g} vs {e_ref:.6g}", flush=True)
+
+
+def test_qkv_gptq_act_order_fullsize(qkv, qkv_d0):
+    from post_int4_weight_amd import api
+    cfg, W, X, H, d = qkv
+    n, out = cfg.inp, cfg.out
+    d0 = qkv_d0
+    announce("qkv gptq 4-bit act-order: perm, full U, sampled rows")
+    res = api.gptq_quantize_layer(W, H, d, bits=4, group_size=128, damp=0.01, act_order=True)
+    U, perm, lam = api.gptq_inverse_factor(H, d, damp=0.01, act_order=True)
+    torch.cuda.synchronize()
+    p = oracle.act_order_permutation(d0)
+    assert np.array_equal(perm.cpu().numpy(), p)
+    assert np.array_equal(res["perm"].cpu().numpy(), p)
+    lam0 = 0.01 * float(np.mean(d0))
+    assert abs(lam - lam0) <= 1e-12 * lam0
+    Hh = H.cpu().numpy().astype(np.float64)
+    Hh[np.diag_indices(n)] += lam0
+    Uref = oracle.inverse_upper_factor(Hh[np.ix_(p, p)])
+    del Hh
+    assert rel_fro(U.cpu().numpy().astype(np.float64), Uref) <= 1e-4
+    print("[oracle] act-order permutation and full U checked", flush=True)
+
+    rows = list(range(0, out, out // SAMPLE_ROWS))
+    cp_ref, s_ref, _ = oracle.gptq_columns(to64(W[rows].cpu())[:, p], Uref, 4, 128)
+    c_ref = np.empty_like(cp_ref)
+    c_ref[:, p] = cp_ref                       # codes back in the original column order
+    g_ref = np.empty(n, dtype=np.int64)
+    g_ref[p] = np.arange(n) // 128
+    assert np.array_equal(res["g_idx"].cpu().numpy(), g_ref)
+    c_gpu = res["codes"][rows].cpu().numpy()
+    assert code_match(c_gpu, c_ref) >= 0.99
+    Hd = H.double()
+    gi = torch.tensor(g_ref, device=W.device)
+    Ws = W[rows].double()
+    dWg = Ws - res["codes"][rows].double() * res["scales"][rows].double()[:, gi]
+    dWr = Ws - torch.tensor(c_ref, device=W.device, dtype=torch.float64) * torch.tensor(s_ref, device=W.device)[:, gi]
+    den = float(((Ws @ Hd) * Ws).sum())
+    e_gpu = float(((dWg @ Hd) * dWg).sum()) / den
+    e_ref = float(((dWr @ Hd) * dWr).sum()) / den
+    assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
+    print(f"[oracle] act-order, {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal, "
+          f"relative output error {e_gpu:.6g} vs {e_ref:.6g}", flush=True)
 
 
 def _err(X, W, What):
