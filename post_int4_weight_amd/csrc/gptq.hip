@@ -239,16 +239,19 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             // x / (gmax / qmax) in double: the fp32 x * (1 / scale) is within
             // 3 ulp of it, so only quotients that close to a half-integer
             // (TIE_BAND, far wider) are recomputed in fp64. Scale 0 gives
-            // code 0 through the select (rscale is 0 then).
+            // code 0 with no test on the chain: rscale is 0 then, so the
+            // quotient of a finite weight is 0 (and zero is 0), never a tie.
             const float x = w[c];
             const float tq = x * rscale;
             float rq = rintf(tq);
-            if (fabsf(fabsf(tq - rq) - 0.5f) < TIE_BAND && scale > 0.f) {
+            if (fabsf(fabsf(tq - rq) - 0.5f) < TIE_BAND) {
                 const double s64 = ZP ? ((double)gmax - (double)glo) / (double)qmax : (double)gmax / (double)qmax;
                 rq = (float)rint((double)x / s64);
             }
-            float q = ZP ? fminf(fmaxf(rq + zero, 0.f), qmax) : fminf(fmaxf(rq, -qmax - 1.f), qmax);
-            q = (scale > 0.f) ? q : 0.f;
+            // the clip as one median-of-three (the same value as min(max())
+            // for every finite rq)
+            const float q = ZP ? __builtin_amdgcn_fmed3f(rq + zero, 0.f, qmax)
+                               : __builtin_amdgcn_fmed3f(rq, -qmax - 1.f, qmax);
             const float e = (x - (q - zero) * scale) * rd[c];
             // the owner's error to the row's lanes: with 16 lanes per row a
             // DPP broadcast of lane o within each 16-lane row (row_newbcast),
