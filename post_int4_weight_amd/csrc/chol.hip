@@ -107,10 +107,12 @@ __global__ void build_damped_vec_kernel(const float4* __restrict__ H, int64_t n4
     }
 }
 
-__global__ void fill_zero_kernel(float* p, int64_t count) {
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
-         e += (int64_t)gridDim.x * blockDim.x)
-        p[e] = 0.f;
+// U[i][j] = 0 for j < i: the recursion writes every entry on and above the
+// diagonal (grid y = rows)
+__global__ void zero_lower_kernel(float* U, int64_t n) {
+    const int64_t i = blockIdx.y;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < i; j += (int64_t)gridDim.x * blockDim.x)
+        U[i * n + j] = 0.f;
 }
 
 __global__ void fill_int_kernel(int* p, int v) { *p = v; }
@@ -463,7 +465,8 @@ int run_inverse_factor(const float* H, const double* d, int64_t n, double damp, 
         hipLaunchKernelGGL(build_damped_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)n),
                            dim3(256), 0, st, H, act_order ? p : nullptr, n, lam, c.A);
     PTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, st, U, n * n);
+    hipLaunchKernelGGL(zero_lower_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)n), dim3(256), 0,
+                       st, U, n);
     PTQ_LAUNCH_CHECK();
     PTQ_TRY(recurse(c, 0, n));
 

@@ -64,6 +64,26 @@ __global__ void gather_columns_kernel(const T* __restrict__ W, int64_t ldw, int6
     }
 }
 
+// The same without a permutation, for bf16 W with 16-byte aligned rows and
+// n % 8 == 0: Wc[r][8q .. 8q+7] from one 16-byte load, two 16-byte stores
+__global__ void widen_rows_bf16_kernel(const uint16_t* __restrict__ W, int64_t ldw, int64_t n,
+                                       float* __restrict__ Wc) {
+    const int64_t r = blockIdx.y, n8 = n / 8;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n8; q += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 v = *(const uint4*)(W + r * ldw + 8 * q);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = bf16_bits_to_float((uint16_t)(w[e] & 0xFFFFu));
+            f[2 * e + 1] = bf16_bits_to_float((uint16_t)(w[e] >> 16));
+        }
+        float4* o = (float4*)(Wc + r * n + 8 * q);
+        o[0] = make_float4(f[0], f[1], f[2], f[3]);
+        o[1] = make_float4(f[4], f[5], f[6], f[7]);
+    }
+}
+
 // Zero-point group parameters from the group's range [lo, hi] (0 included):
 // scale = (hi - lo) / maxq in fp32; zero = round(-lo / scale), decided in
 // fp64 like the codes.
@@ -478,7 +498,10 @@ int run_quantize_columns(const void* W, int w_dtype, int64_t out, int64_t n, int
     PTQ_LAUNCH_CHECK();
     if (out > 0) {
         dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)out);
-        if (w_dtype == PTQ_BF16)
+        if (w_dtype == PTQ_BF16 && !perm && n % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)W & 15u) == 0)
+            hipLaunchKernelGGL(widen_rows_bf16_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n / 8, 256), 64), (unsigned)out),
+                               dim3(256), 0, st, (const uint16_t*)W, ldw, n, Wc);
+        else if (w_dtype == PTQ_BF16)
             hipLaunchKernelGGL(gather_columns_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)W, ldw, out,
                                n, perm, Wc);
         else
