@@ -98,6 +98,14 @@ struct Bf16GemmArgs {
     float alpha2; int beta_one2; int tri2; int upper_only2;
 };
 
+// EPI_GEMM tile order: 4 x 8 sub-blocks per XCD for dense products of at
+// least 8 x 8 tiles (the GPTQ trailing updates: column stage -0.7 ms); the
+// triangular ones keep whole tile rows in a zigzag over the XCDs, which
+// balances their uneven tile depths (sub-blocks made the factor 10 ms slower)
+__host__ __device__ inline bool split3_subblocks(int64_t tiles_m, int64_t tiles_n, int tri, int upper_only) {
+    return tiles_m >= 8 && tiles_n >= 8 && tri == TRI_NONE && !upper_only;
+}
+
 template <int BMX>
 struct Stg {
     uint4 a[BMX * CPR / NTH];
@@ -518,7 +526,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         // triangular products whose row work falls with the row (A upper,
         // upper_only). Else plain row-major.
         int64_t tm, tn;
-        if (g.tiles_m >= NXCD) {
+        if (split3_subblocks(g.tiles_m, g.tiles_n, g.tri, g.upper_only)) {
+            // 4 x 8 sub-blocks of tiles dealt round-robin to the XCDs: the 32
+            // tiles an XCD runs side by side read 12 panels through its L2
+            // (whole tile rows: 33)
+            const int64_t x = bid % NXCD, i = bid / NXCD, sbc = cdiv(g.tiles_n, 8);
+            const int64_t sbi = NXCD * (i / 32) + x, w = i % 32;
+            tm = 4 * (sbi / sbc) + w / 8;
+            tn = 8 * (sbi % sbc) + w % 8;
+            if (tm >= g.tiles_m || tn >= g.tiles_n) return;
+        } else if (g.tiles_m >= NXCD) {
             const int64_t x = bid % NXCD, i = bid / NXCD, k = i / g.tiles_n;
             tm = NXCD * k + ((k & 1) ? NXCD - 1 - x : x);
             tn = i % g.tiles_n;
@@ -977,6 +994,8 @@ Bf16GemmArgs split3_args(const GemmArgs& a, const uint16_t* pa, const uint16_t* 
     return g;
 }
 unsigned split3_grid(const Bf16GemmArgs& g) {
+    if (split3_subblocks(g.tiles_m, g.tiles_n, g.tri, g.upper_only))
+        return (unsigned)(cdiv(cdiv(g.tiles_m, 4) * cdiv(g.tiles_n, 8), NXCD) * NXCD * 32);
     return (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n : g.tiles_m * g.tiles_n);
 }
 // op(B) is A's transpose view: one set of planes serves both operands
