@@ -106,6 +106,20 @@ __host__ __device__ inline bool split3_subblocks(int64_t tiles_m, int64_t tiles_
     return tiles_m >= 8 && tiles_n >= 8 && tri == TRI_NONE && !upper_only;
 }
 
+// AWQ error tiles: 4 x 8 sub-blocks of the tile grid dealt round-robin to
+// the XCDs, so the 32 tiles an XCD runs side by side read 12 panels through
+// its L2 (a contiguous run of whole tile rows: 33). Returns the tile's
+// row-major index tm * tiles_n + tn, or -1 for a slot past the grid.
+__host__ __device__ inline int64_t sumsq_tile(int64_t b, int64_t tiles_m, int64_t tiles_n) {
+    const int64_t x = b % NXCD, i = b / NXCD, sbc = (tiles_n + 7) / 8;
+    const int64_t sbi = NXCD * (i / 32) + x, w = i % 32;
+    const int64_t tm = 4 * (sbi / sbc) + w / 8, tn = 8 * (sbi % sbc) + w % 8;
+    return (tm < tiles_m && tn < tiles_n) ? tm * tiles_n + tn : -1;
+}
+inline int64_t sumsq_grid(int64_t tiles_m, int64_t tiles_n) {
+    return ((((tiles_m + 3) / 4) * ((tiles_n + 7) / 8) + NXCD - 1) / NXCD) * NXCD * 32;
+}
+
 template <int BMX>
 struct Stg {
     uint4 a[BMX * CPR / NTH];
@@ -219,10 +233,8 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
         j0 = (int64_t)tj * BMX;
         diag = (ti == tj);
     } else {
-        // row-major tiles, a contiguous run per XCD
-        const int64_t per = (nwork + NXCD - 1) / NXCD;
-        L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
-        if (L >= nwork) return;
+        L = sumsq_tile(blockIdx.x, nwork / g.tiles_n, g.tiles_n);
+        if (L < 0) return;
         i0 = (L / g.tiles_n) * BMX;
         j0 = (L % g.tiles_n) * BMX;
     }
@@ -553,10 +565,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         i0 = tm * BMX;
         j0 = tn * BMX;
     } else {
-        // row-major tiles, a contiguous run per XCD
-        const int64_t per = (nwork + NXCD - 1) / NXCD;
-        L = (int64_t)(blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
-        if (L >= nwork) return;
+        L = sumsq_tile(blockIdx.x, nwork / g.tiles_n, g.tiles_n);
+        if (L < 0) return;
         i0 = (L / g.tiles_n) * BMX;
         j0 = (L % g.tiles_n) * BMX;
     }
@@ -826,7 +836,7 @@ constexpr int DMF = 16;
 // depth (64, else 32), the register-staged one otherwise.
 template <int BMX, int EPI>
 int launch_nt(const Bf16GemmArgs& g, int64_t nwork, unsigned grid_y, hipStream_t st) {
-    const unsigned grid = (unsigned)(EPI == EPI_HESSIAN ? 256 * hessian_rounds(g.T) : cdiv(nwork, NXCD) * NXCD);
+    const unsigned grid = (unsigned)(EPI == EPI_HESSIAN ? 256 * hessian_rounds(g.T) : sumsq_grid(nwork / g.tiles_n, g.tiles_n));
     if (g.M > 0 && g.N > 0 && g.K1 % 64 == 0 && g.K2 % 64 == 0) {
         PTQ_TRY((launch_direct<BMX, EPI, 64, BMX == 256 ? DNW : 4, BMX == 256 ? DMF : 32>(g, nwork, grid, grid_y, st)));
     } else if constexpr (EPI == EPI_HESSIAN) {
