@@ -77,13 +77,19 @@ __global__ void identity_perm_kernel(int32_t* perm, int64_t n) {
     if (j < n) perm[j] = (int32_t)j;
 }
 
-// A[i][j] = H[p_i][p_j] + lambda [i == j]  (p = perm or identity)
+// A[i][j] = H[p_i][p_j] + lambda [i == j]  (p = perm or identity), for
+// j >= A_ROW_START(i): the recursion reads A on and above the diagonal only,
+// and its GEMMs' output tiles (at most 256 wide, aligned) inside the diagonal
+// 256 x 256 blocks, so the copy starts each row at its diagonal block
+constexpr int64_t A_DIAG_TILE = 256;
+__host__ __device__ inline int64_t a_row_start(int64_t i) { return (i / A_DIAG_TILE) * A_DIAG_TILE; }
 __global__ void build_damped_kernel(const float* __restrict__ H, const int32_t* __restrict__ perm, int64_t n,
                                     const double* lam, float* __restrict__ A) {
     const int64_t i = blockIdx.y;
     const int64_t pi = perm ? perm[i] : i;
     const float l = (float)*lam;
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t j = a_row_start(i) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n;
+         j += (int64_t)gridDim.x * blockDim.x) {
         const int64_t pj = perm ? perm[j] : j;
         float v = H[pi * n + pj];
         if (i == j) v = (float)((double)v + (double)l);
@@ -96,7 +102,8 @@ __global__ void build_damped_vec_kernel(const float4* __restrict__ H, int64_t n4
                                         float4* __restrict__ A) {
     const int64_t i = blockIdx.y;
     const float l = (float)*lam;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t q = a_row_start(i) / 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4;
+         q += (int64_t)gridDim.x * blockDim.x) {
         float4 v = H[i * n4 + q];
         const int64_t d = i - 4 * q;   // position of the diagonal inside this float4, if any
         if (d == 0) v.x = (float)((double)v.x + (double)l);
