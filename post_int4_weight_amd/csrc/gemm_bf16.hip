@@ -110,11 +110,13 @@ __host__ __device__ inline bool split3_subblocks(int64_t tiles_m, int64_t tiles_
 // the XCDs, so the 32 tiles an XCD runs side by side read 12 panels through
 // its L2 (a contiguous run of whole tile rows: 33). Returns the tile's
 // row-major index tm * tiles_n + tn, or -1 for a slot past the grid.
-__host__ __device__ inline int64_t sumsq_tile(int64_t b, int64_t tiles_m, int64_t tiles_n) {
-    const int64_t x = b % NXCD, i = b / NXCD, sbc = (tiles_n + 7) / 8;
-    const int64_t sbi = NXCD * (i / 32) + x, w = i % 32;
-    const int64_t tm = 4 * (sbi / sbc) + w / 8, tn = 8 * (sbi % sbc) + w % 8;
-    return (tm < tiles_m && tn < tiles_n) ? tm * tiles_n + tn : -1;
+__host__ __device__ inline int64_t sumsq_tile(uint32_t b, int64_t tiles_m, int64_t tiles_n) {
+    // 32-bit arithmetic (tile counts are small): with 64-bit the AWQ kernel
+    // spilled 5 registers
+    const uint32_t x = b % NXCD, i = b / NXCD, sbc = (uint32_t)(tiles_n + 7) / 8;
+    const uint32_t sbi = NXCD * (i / 32) + x, w = i % 32;
+    const uint32_t tm = 4 * (sbi / sbc) + w / 8, tn = 8 * (sbi % sbc) + w % 8;
+    return (tm < tiles_m && tn < tiles_n) ? (int64_t)tm * tiles_n + tn : -1;
 }
 inline int64_t sumsq_grid(int64_t tiles_m, int64_t tiles_n) {
     return ((((tiles_m + 3) / 4) * ((tiles_n + 7) / 8) + NXCD - 1) / NXCD) * NXCD * 32;

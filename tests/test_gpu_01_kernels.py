@@ -125,6 +125,32 @@ def test_hessian_vs_oracle(gpu, rows, n, dtype):
     assert np.max(np.abs(d.cpu().numpy() - d0) / d0) <= 1e-12
 
 
+@pytest.mark.parametrize("rows", [3000, 70000])
+def test_hessian_large_n(gpu, rows):
+    """n = 12544 (49 tile rows of 256: ten rounds of tiles, the last tile
+    column a single one): blocks of H in the last tile column, on the
+    diagonal and inside, against the oracle, with one chunk of rows and with
+    two (the second adds onto the first and writes the mirror); H exactly
+    symmetric; d to fp64 rounding."""
+    import inputs
+    from post_int4_weight_amd import api
+    n = 12544
+    announce(f"hessian large n rows={rows} n={n}")
+    W, X = inputs.custom(8, n, rows, seed=rows, dtype="bf16", device="cpu")
+    H, d = zeros_h(n, gpu)
+    api.hessian_accumulate(H, d, X.to(gpu))
+    torch.cuda.synchronize()
+    assert torch.equal(H, H.T)
+    X64 = to64(X)
+    for (r0, c0) in ((8192, 12288), (12288, 12288), (0, 256), (4096, 8192)):
+        Xa, Xb = X64[:, r0:r0 + 256], X64[:, c0:c0 + 256]
+        ref = Xa.T @ Xb
+        got = H[r0:r0 + 256, c0:c0 + 256].cpu().double().numpy()
+        assert rel_fro(got, ref) <= 1e-5, (r0, c0)
+    d0 = np.sum(X64 * X64, axis=0)
+    assert np.max(np.abs(d.cpu().numpy() - d0) / d0) <= 1e-12
+
+
 def test_hessian_is_additive(gpu):
     """Two calls on two halves equal one call on the whole (chunked streaming)."""
     import inputs
