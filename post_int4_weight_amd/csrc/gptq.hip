@@ -156,7 +156,6 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
     float gmax = 0.f;       // symmetric: the group's max |w| (scale = gmax / qmax); zero-point: hi
     float glo = 0.f;        // zero-point: lo
     float zero = 0.f;       // zero-point: the group's zero
-    float e2 = 0.f;
 
     if (g > B) {
         // groups span several blocks and start on block boundaries
@@ -246,55 +245,87 @@ __global__ __launch_bounds__(NTH) void gptq_block_kernel(float* __restrict__ Wc,
             ++gnext;
         }
         const bool own = lr == o;
+        // The segment's 8 columns run first without the fp64 recheck (a
+        // branch on every column of the dependency chain), noting whether an
+        // owner's quotient fell within TIE_BAND of a half-integer. If one did
+        // (rare: the band is 2^-14 wide per half-integer), the wave restores
+        // the segment's starting state and runs it again with the recheck,
+        // so every result is the rechecked one.
+        float wsave[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int j = CPL * o + c;
-            const float4 u0 = un0, u1 = un1;
-            if (j + 1 < B) {
-                un0 = *(const float4*)&Us[j + 1][c0];
-                un1 = *(const float4*)&Us[j + 1][c0 + 4];
+        for (int c = 0; c < CPL; ++c) wsave[c] = w[c];
+        auto columns = [&](auto exact_c) {
+            constexpr bool EXACT = decltype(exact_c)::value;
+            float near = 1.f;   // least distance of this lane's quotients to a half-integer
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int j = CPL * o + c;
+                const float4 u0 = un0, u1 = un1;
+                if (j + 1 < B) {
+                    un0 = *(const float4*)&Us[j + 1][c0];
+                    un1 = *(const float4*)&Us[j + 1][c0 + 4];
+                }
+                // round this lane's copy of column j (the owner's copy is the
+                // real one). The rounding decision is the fp64 one,
+                // x / (gmax / qmax) in double: the fp32 x * (1 / scale) is
+                // within 3 ulp of it, so only quotients that close to a
+                // half-integer (TIE_BAND, far wider) are recomputed in fp64.
+                // Scale 0 gives code 0 with no test on the chain: rscale is 0
+                // then, so the quotient of a finite weight is 0 (and zero is
+                // 0), never a tie.
+                const float x = w[c];
+                const float tq = x * rscale;
+                float rq = rintf(tq);
+                const float dist = fabsf(fabsf(tq - rq) - 0.5f);
+                if constexpr (EXACT) {
+                    if (dist < TIE_BAND) {
+                        const double s64 =
+                            ZP ? ((double)gmax - (double)glo) / (double)qmax : (double)gmax / (double)qmax;
+                        rq = (float)rint((double)x / s64);
+                    }
+                } else {
+                    near = fminf(near, dist);
+                }
+                // the clip as one median-of-three (the same value as
+                // min(max()) for every finite rq)
+                const float q = ZP ? __builtin_amdgcn_fmed3f(rq + zero, 0.f, qmax)
+                                   : __builtin_amdgcn_fmed3f(rq, -qmax - 1.f, qmax);
+                const float e = (x - (q - zero) * scale) * rd[c];
+                // the owner's error to the row's lanes: with 16 lanes per row
+                // a DPP broadcast of lane o within each 16-lane row
+                // (row_newbcast), no LDS round trip; else a bpermute
+                float eb;
+                if constexpr (LPR == 16)
+                    eb = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(e), 0x150 + o, 0xF, 0xF, false));
+                else
+                    eb = __shfl(e, row_lane0 + o, 64);
+                cq[c] = own ? q : cq[c];
+                ce[c] = own ? e : ce[c];
+                w[0] = fmaf(-eb, u0.x, w[0]);
+                w[1] = fmaf(-eb, u0.y, w[1]);
+                w[2] = fmaf(-eb, u0.z, w[2]);
+                w[3] = fmaf(-eb, u0.w, w[3]);
+                w[4] = fmaf(-eb, u1.x, w[4]);
+                w[5] = fmaf(-eb, u1.y, w[5]);
+                w[6] = fmaf(-eb, u1.z, w[6]);
+                w[7] = fmaf(-eb, u1.w, w[7]);
             }
-            // round this lane's copy of column j (the owner's copy is the
-            // real one). The rounding decision is the fp64 one,
-            // x / (gmax / qmax) in double: the fp32 x * (1 / scale) is within
-            // 3 ulp of it, so only quotients that close to a half-integer
-            // (TIE_BAND, far wider) are recomputed in fp64. Scale 0 gives
-            // code 0 with no test on the chain: rscale is 0 then, so the
-            // quotient of a finite weight is 0 (and zero is 0), never a tie.
-            const float x = w[c];
-            const float tq = x * rscale;
-            float rq = rintf(tq);
-            if (fabsf(fabsf(tq - rq) - 0.5f) < TIE_BAND) {
-                const double s64 = ZP ? ((double)gmax - (double)glo) / (double)qmax : (double)gmax / (double)qmax;
-                rq = (float)rint((double)x / s64);
-            }
-            // the clip as one median-of-three (the same value as min(max())
-            // for every finite rq)
-            const float q = ZP ? __builtin_amdgcn_fmed3f(rq + zero, 0.f, qmax)
-                               : __builtin_amdgcn_fmed3f(rq, -qmax - 1.f, qmax);
-            const float e = (x - (q - zero) * scale) * rd[c];
-            // the owner's error to the row's lanes: with 16 lanes per row a
-            // DPP broadcast of lane o within each 16-lane row (row_newbcast),
-            // no LDS round trip; else a bpermute
-            float eb;
-            if constexpr (LPR == 16)
-                eb = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e), 0x150 + o, 0xF, 0xF, false));
-            else
-                eb = __shfl(e, row_lane0 + o, 64);
-            cq[c] = own ? q : cq[c];
-            ce[c] = own ? e : ce[c];
-            e2 = own ? fmaf(e, e, e2) : e2;
-            w[0] = fmaf(-eb, u0.x, w[0]);
-            w[1] = fmaf(-eb, u0.y, w[1]);
-            w[2] = fmaf(-eb, u0.z, w[2]);
-            w[3] = fmaf(-eb, u0.w, w[3]);
-            w[4] = fmaf(-eb, u1.x, w[4]);
-            w[5] = fmaf(-eb, u1.y, w[5]);
-            w[6] = fmaf(-eb, u1.z, w[6]);
-            w[7] = fmaf(-eb, u1.w, w[7]);
+            return near;
+        };
+        const float near = columns(std::false_type{});
+        if (__builtin_amdgcn_ballot_w64(own && near < TIE_BAND) != 0) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) w[c] = wsave[c];
+            un0 = *(const float4*)&Us[CPL * o][c0];
+            un1 = *(const float4*)&Us[CPL * o][c0 + 4];
+            columns(std::true_type{});
         }
     });
 
+    // the sum of this lane's own squared errors, in column order
+    float e2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) e2 = fmaf(ce[c], ce[c], e2);
     if (!live) return;
     // errors for the trailing GEMM, codes, per-(row, block) sum of err^2
     bool bad = false;
