@@ -213,6 +213,7 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
             for (int q = 0; q < TS; ++q) *(float4*)&rowb[k0 + q][o] = make_float4(a[0][q], a[1][q], a[2][q], a[3][q]);
         }
     };
+    int bad = 0;   // thread 0: non-positive (1) or NaN (2) pivots seen
     publish(NB - 1);
     for (int jb = NB - 1; jb >= 0; --jb) {
         const int jb0 = CB * jb;
@@ -241,10 +242,8 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
             for (int tt = CB - 1; tt >= 0; --tt) {
                 const int j = jb0 + tt;
                 float piv = d[tt][tt];
-                if (!(piv > 0.f)) {
-                    if (t == 0) atomicOr(flag, (piv != piv) ? 2 : 1);
-                    piv = 1.f;
-                }
+                bad |= (piv != piv) ? 2 : (piv > 0.f ? 0 : 1);
+                piv = (piv > 0.f) ? piv : 1.f;
                 // 1 / sqrt(piv): the hardware reciprocal square root and one
                 // Newton step (within about an ulp, as IEEE sqrt then divide;
                 // their dozens of dependent instructions sat on every step's
@@ -313,6 +312,7 @@ __global__ __launch_bounds__(base_threads<TS>()) void chol_inv_base_kernel(const
         }
         if (jb > 0) publish(jb - 1);
     }
+    if (t == 0 && bad) atomicOr(flag, bad);
     if (!live) return;
 #pragma unroll
     for (int di = 0; di < TS; ++di)
