@@ -42,6 +42,20 @@ int ptq_test_gemm_f32_split3(int64_t M, int64_t N, int64_t K, const float* A, in
                              int beta_one, int tri, int upper_only, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Two independent products of the fp32 GEMM in one launch, as the U
+ * recursion runs H11 -= R12 R12^T and T = R12 U22 at its small levels:
+ * product 0 with B stored [N][K] (layout_b 1), product 1 with B row-major
+ * [K][N] (layout_b 0), A row-major [M, K] for both, each with its own C,
+ * alpha, beta, tri and upper_only as in ptq_test_gemm_f32. The results are
+ * those of two ptq_test_gemm_f32 calls, bit for bit (when the two cannot
+ * share a launch, two launches are made). Device pointers; K, lda, ldb
+ * multiples of 4. Asynchronous. Returns PTQ_OK, PTQ_EINVAL or PTQ_EHIP. */
+int ptq_test_gemm_f32_pair(int64_t M0, int64_t N0, int64_t K0, const float* A0, int64_t lda0, const float* B0,
+                           int64_t ldb0, float* C0, int64_t ldc0, float alpha0, int beta_one0, int tri0,
+                           int upper_only0, int64_t M1, int64_t N1, int64_t K1, const float* A1, int64_t lda1,
+                           const float* B1, int64_t ldb1, float* C1, int64_t ldc1, float alpha1, int beta_one1,
+                           int tri1, int upper_only1, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

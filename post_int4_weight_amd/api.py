@@ -72,6 +72,9 @@ def _load() -> ctypes.CDLL:
         "gptq_quantize_layer_zp": (i32, [vp, i32, i64, i64, i64, vp, vp, i32, i32, dbl, i32, i32, vp, vp, vp, vp, vp,
                                          dp, vp, sz, vp]),
         "layer_output_error_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "ptq_test_gemm_f32_pair": (i32, [i64, i64, i64, vp, i64, vp, i64, vp, i64, ctypes.c_float, i32, i32, i32,
+                                         i64, i64, i64, vp, i64, vp, i64, vp, i64, ctypes.c_float, i32, i32, i32,
+                                         vp]),
         "ptq_test_gemm_f32_split3_workspace_bytes": (sz, [i64, i64, i64]),
         "ptq_test_gemm_f32_split3": (i32, [i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64, ctypes.c_float, i32,
                                            i32, i32, vp, sz, vp]),
@@ -377,6 +380,17 @@ def _test_gemm_f32(A, B, C, M, N, K, layout_a, layout_b, alpha=1.0, beta_one=0, 
     _check(_lib.ptq_test_gemm_f32(M, N, K, _ptr(A), A.stride(0), layout_a, _ptr(B), B.stride(0), layout_b, _ptr(C),
                                   C.stride(0), float(alpha), int(beta_one), int(tri), int(upper_only), _stream()))
     return C
+
+
+def _test_gemm_f32_pair(p0, p1):
+    """ptq_test_gemm_f32_pair (include/ptq_testing.h): two products in one launch, the first with B stored
+    [N][K], the second with B row-major [K][N]. Each pi is a dict with A, B, C, M, N, K and optionally alpha,
+    beta_one, tri, upper_only."""
+    def args(p):
+        return (p["M"], p["N"], p["K"], _ptr(p["A"]), p["A"].stride(0), _ptr(p["B"]), p["B"].stride(0), _ptr(p["C"]),
+                p["C"].stride(0), float(p.get("alpha", 1.0)), int(p.get("beta_one", 0)), int(p.get("tri", 0)),
+                int(p.get("upper_only", 0)))
+    _check(_lib.ptq_test_gemm_f32_pair(*args(p0), *args(p1), _stream()))
 
 
 def _test_gemm_f32_split3(A, B, C, M, N, K, layout_a, layout_b, alpha=1.0, beta_one=0, tri=0, upper_only=0):

@@ -335,6 +335,29 @@ int ptq_test_gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     return launch_gemm_f32(g, (hipStream_t)stream);
 }
 
+int ptq_test_gemm_f32_pair(int64_t M0, int64_t N0, int64_t K0, const float* A0, int64_t lda0, const float* B0,
+                           int64_t ldb0, float* C0, int64_t ldc0, float alpha0, int beta_one0, int tri0,
+                           int upper_only0, int64_t M1, int64_t N1, int64_t K1, const float* A1, int64_t lda1,
+                           const float* B1, int64_t ldb1, float* C1, int64_t ldc1, float alpha1, int beta_one1,
+                           int tri1, int upper_only1, void* stream) {
+    if (M0 < 0 || N0 < 0 || K0 < 0 || M1 < 0 || N1 < 0 || K1 < 0 || !A0 || !B0 || !C0 || !A1 || !B1 || !C1 ||
+        tri0 < 0 || tri0 > 3 || tri1 < 0 || tri1 > 3 || K0 % 4 || K1 % 4 || lda0 % 4 || ldb0 % 4 || lda1 % 4 ||
+        ldb1 % 4 || !aligned16(A0) || !aligned16(B0) || !aligned16(A1) || !aligned16(B1))
+        return fail(PTQ_EINVAL, "ptq_test_gemm_f32_pair: bad arguments");
+    GemmArgs g0{}, g1{};
+    g0.M = M0; g0.N = N0; g0.K = K0;
+    g0.A = A0; g0.lda = lda0; g0.layout_a = A_MK;
+    g0.B = B0; g0.ldb = ldb0; g0.layout_b = B_NK;
+    g0.C = C0; g0.ldc = ldc0;
+    g0.alpha = alpha0; g0.beta_one = beta_one0; g0.tri = tri0; g0.upper_only = upper_only0;
+    g1.M = M1; g1.N = N1; g1.K = K1;
+    g1.A = A1; g1.lda = lda1; g1.layout_a = A_MK;
+    g1.B = B1; g1.ldb = ldb1; g1.layout_b = B_KN;
+    g1.C = C1; g1.ldc = ldc1;
+    g1.alpha = alpha1; g1.beta_one = beta_one1; g1.tri = tri1; g1.upper_only = upper_only1;
+    return launch_gemm_f32_pair(g0, g1, (hipStream_t)stream);
+}
+
 size_t ptq_test_gemm_f32_split3_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return 0;
     Sizer z;

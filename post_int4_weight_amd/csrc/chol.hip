@@ -404,6 +404,12 @@ int recurse(Ctx& c, int64_t o, int64_t m) {
         const int s = launch_gemm_f32_split3_pair(syrk, tprod, c.Pa, c.Pb, c.st);
         prof_end(PROF_FACTOR_GEMM, c.st);
         PTQ_TRY(s);
+    } else if (!split_size(c, syrk) && !split_size(c, tprod)) {
+        // the small levels: both on the fp32 kernel, in one launch
+        prof_begin(PROF_FACTOR_GEMM, c.st);
+        const int s = launch_gemm_f32_pair(syrk, tprod, c.st);
+        prof_end(PROF_FACTOR_GEMM, c.st);
+        PTQ_TRY(s);
     } else {
         PTQ_TRY(gemm(c, syrk));
         PTQ_TRY(gemm(c, tprod));

@@ -156,6 +156,11 @@ struct GemmArgs {
     int upper_only;   // only output tiles with tile_row <= tile_col (SYRK-style)
 };
 int launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+// Two products in one launch when both take the direct kernel at the same
+// tile and ring shape, the first with B stored [N][K] and the second with B
+// stored [K][N]; otherwise two launches. Same results as launch_gemm_f32 on
+// each.
+int launch_gemm_f32_pair(const GemmArgs& a0, const GemmArgs& a1, hipStream_t st);
 // The same GEMM on the bf16 MFMA from three-term bf16 splits of both
 // operands (gemm_bf16.hip): pa and pb hold gemm_f32_split3_elems(M, K) and
 // (N, K) bf16 elements of scratch (pb is unused when B is A's transpose view).

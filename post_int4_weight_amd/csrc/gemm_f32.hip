@@ -260,7 +260,7 @@ __device__ __forceinline__ void f32_wait_vmcnt() {
 // 32 x 32 block each): the small tile quadruples the workgroups of the small
 // products deep in the U recursion, which otherwise run on a few CUs.
 template <bool B_KMAJOR, int DNST, int BT>
-__global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
+__device__ __forceinline__ void direct_tile(const GemmArgs& g, int64_t tiles_m, int64_t tiles_n, unsigned bid) {
     static_assert(DNST >= 3, "the ring needs three stages");
     static_assert(BT == 128 || BT == 64, "tile");
     constexpr int WB = BT / 64;                          // 32 x 32 blocks per wave and dimension
@@ -275,14 +275,14 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
     // row-major order over all XCDs.
     int64_t tm, tn;
     if (tiles_m >= XCDS) {
-        const int64_t x = blockIdx.x % XCDS, i = blockIdx.x / XCDS, k = i / tiles_n;
+        const int64_t x = bid % XCDS, i = bid / XCDS, k = i / tiles_n;
         tm = XCDS * k + ((k & 1) ? XCDS - 1 - x : x);
         tn = i % tiles_n;
         if (tm >= tiles_m) return;
     } else {
-        if ((int64_t)blockIdx.x >= tiles_m * tiles_n) return;
-        tm = blockIdx.x / tiles_n;
-        tn = blockIdx.x % tiles_n;
+        if ((int64_t)bid >= tiles_m * tiles_n) return;
+        tm = bid / tiles_n;
+        tn = bid % tiles_n;
     }
     // B upper triangular [K][N]: a tile's depth grows with its column, so
     // columns go in descending order and the deepest tiles start first (the
@@ -478,6 +478,25 @@ __global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, in
 }
 
 template <bool B_KMAJOR, int DNST, int BT>
+__global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_kernel(GemmArgs g, int64_t tiles_m, int64_t tiles_n) {
+    direct_tile<B_KMAJOR, DNST, BT>(g, tiles_m, tiles_n, blockIdx.x);
+}
+
+// Two independent products in one launch: workgroups below grid0 (a
+// multiple of 8, so both keep their XCD order) compute g0 with B stored
+// [N][K], the rest g1 with B stored [K][N]; each tile is computed exactly as
+// in a launch of its own. The factor's H11 -= R12 R12^T and T = R12 U22 at
+// the recursion's small levels, where each launch runs on a few CUs and its
+// fixed cost dominates.
+template <int DNST, int BT>
+__global__ __launch_bounds__(NT, DWG) void gemm_f32_direct_pair_kernel(GemmArgs g0, int64_t tm0, int64_t tn0,
+                                                                       unsigned grid0, GemmArgs g1, int64_t tm1,
+                                                                       int64_t tn1) {
+    if (blockIdx.x < grid0) direct_tile<false, DNST, BT>(g0, tm0, tn0, blockIdx.x);
+    else direct_tile<true, DNST, BT>(g1, tm1, tn1, blockIdx.x - grid0);
+}
+
+template <bool B_KMAJOR, int DNST, int BT>
 int launch_direct_ring(const GemmArgs& a, hipStream_t st) {
     static bool ready = false;
     if (!ready) {
@@ -518,7 +537,47 @@ bool direct_ok(const GemmArgs& a) {
     return true;
 }
 
+// the launch shape launch_direct picks: tile side and ring depth
+int direct_shape(const GemmArgs& a) {
+    const bool small = cdiv(a.M, BM) * cdiv(a.N, BN) < SMALL_TILES;
+    return (small ? 64 : 128) + (a.K <= SHORT_K ? 0 : 1);
+}
+
+template <int DNST, int BT>
+int launch_direct_pair(const GemmArgs& a0, const GemmArgs& a1, hipStream_t st) {
+    static bool ready = false;
+    if (!ready) {
+        PTQ_HIP(hipFuncSetAttribute((const void*)gemm_f32_direct_pair_kernel<DNST, BT>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, DNST * DSTAGE_BYTES<BT>));
+        ready = true;
+    }
+    auto grid_of = [](int64_t tm, int64_t tn) {
+        return (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
+    };
+    const int64_t tm0 = cdiv(a0.M, BT), tn0 = cdiv(a0.N, BT), tm1 = cdiv(a1.M, BT), tn1 = cdiv(a1.N, BT);
+    const unsigned grid0 = (unsigned)cdiv(grid_of(tm0, tn0), XCDS) * XCDS, grid1 = grid_of(tm1, tn1);
+    hipLaunchKernelGGL((gemm_f32_direct_pair_kernel<DNST, BT>), dim3(grid0 + grid1), dim3(NT),
+                       DNST * DSTAGE_BYTES<BT>, st, a0, tm0, tn0, grid0, a1, tm1, tn1);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
+}
+
 }  // namespace
+
+int launch_gemm_f32_pair(const GemmArgs& a0, const GemmArgs& a1, hipStream_t st) {
+    const bool pairable = a0.M > 0 && a0.N > 0 && a1.M > 0 && a1.N > 0 && direct_ok(a0) && direct_ok(a1) &&
+                          a0.layout_b == B_NK && a1.layout_b == B_KN && direct_shape(a0) == direct_shape(a1);
+    if (!pairable) {
+        PTQ_TRY(launch_gemm_f32(a0, st));
+        return launch_gemm_f32(a1, st);
+    }
+    switch (direct_shape(a0)) {
+        case 64: return launch_direct_pair<DNST_SHORT, 64>(a0, a1, st);
+        case 65: return launch_direct_pair<DNST_LONG, 64>(a0, a1, st);
+        case 128: return launch_direct_pair<DNST_SHORT, 128>(a0, a1, st);
+        default: return launch_direct_pair<DNST_LONG, 128>(a0, a1, st);
+    }
+}
 
 int launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
     if (a.M <= 0 || a.N <= 0) return PTQ_OK;

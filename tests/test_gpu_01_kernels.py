@@ -70,6 +70,42 @@ def test_gemm_f32_triangles(gpu, tri, n, m):
     assert rel_fro(C.cpu().double().numpy(), ref.numpy()) < 1e-5
 
 
+# (n1, n2): the recursion's small levels (one launch, 64 x 64 tiles), ragged
+# sizes, a depth past the short ring, and a pair whose two products take
+# different tile sizes (4200: 128 x 128 tiles for the update; two launches)
+@pytest.mark.parametrize("n1,n2", [(128, 128), (256, 256), (1024, 1024), (200, 332), (256, 2048), (4200, 200)])
+def test_gemm_f32_pair(gpu, n1, n2):
+    """The U recursion's H11 -= R12 R12^T (upper tiles) and T = R12 U22 (U22 upper) in one launch: bit for bit
+    the two separate launches, and both against fp64."""
+    from post_int4_weight_amd import api
+    announce(f"gemm_f32 pair n1={n1} n2={n2}")
+    g = torch.Generator().manual_seed(n1 * 7 + n2)
+    R = torch.randn(n1, n2, generator=g)
+    Uu = torch.triu(torch.randn(n2, n2, generator=g))
+    H0 = torch.randn(n1, n1, generator=g)
+    Rd, Ud = R.to(gpu), Uu.to(gpu)
+    outs = []
+    for paired in (True, False):
+        H = H0.clone().to(gpu)
+        T = torch.full((n1, n2), float("nan"), device=gpu)
+        syrk = dict(A=Rd, B=Rd, C=H, M=n1, N=n1, K=n2, alpha=-1.0, beta_one=1, upper_only=1)
+        tprod = dict(A=Rd, B=Ud, C=T, M=n1, N=n2, K=n2, tri=2)
+        if paired:
+            api._test_gemm_f32_pair(syrk, tprod)
+        else:
+            api._test_gemm_f32(Rd, Rd, H, n1, n1, n2, 0, 1, alpha=-1.0, beta_one=1, upper_only=1)
+            api._test_gemm_f32(Rd, Ud, T, n1, n2, n2, 0, 0, tri=2)
+        torch.cuda.synchronize()
+        outs.append((H.cpu(), T.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    Hg, Tg = outs[0]
+    want_t = R.double() @ Uu.double()
+    assert rel_fro(Tg.double().numpy(), want_t.numpy()) < 1e-5
+    want_h = H0.double() - R.double() @ R.double().T
+    up = np.triu(np.ones((n1, n1), dtype=bool))
+    assert rel_fro(Hg.double().numpy()[up], want_h.numpy()[up]) < 1e-5
+
+
 @pytest.mark.parametrize("n", [300, 1800])
 @pytest.mark.parametrize("k", [50, 64])
 def test_gemm_f32_upper_only(gpu, k, n):
