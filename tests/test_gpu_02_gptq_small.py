@@ -61,6 +61,43 @@ def test_tiny_layer_all_stages(gpu):
     assert abs(res["stats"]["objective"] - obj) <= 1e-3 * obj
 
 
+@pytest.mark.parametrize("block", [128, 64, 32])
+def test_column_loop_near_ties_decided_in_fp64(gpu, block):
+    """With U = I the loop has no feedback, so every code is its group's
+    round-to-nearest-even of w / (max |w| / qmax), decided in fp64 as the
+    oracle decides it. The weights sit a few fp32 ulps from half-integer
+    multiples of the scale, where the fp32 quotient w * (1 / scale) rounds the
+    other way on a share of them: every GPU code must still be the oracle's
+    (the loop's fast pass rounds in fp32 and replays a segment with the fp64
+    decision when an owner's quotient falls near a half-integer)."""
+    from post_int4_weight_amd import api
+    announce(f"column loop near ties, U = I, block={block}")
+    out, n, g, q = 64, 1024, 128, 7
+    rng = np.random.default_rng(11)
+    W = np.empty((out, n), dtype=np.float32)
+    gmax = rng.uniform(0.5, 2.0, size=(out, n // g)).astype(np.float32)
+    for gi in range(n // g):
+        k = rng.integers(-7, 7, size=(out, g)).astype(np.float64)        # ties between k and k + 1
+        x = ((k + 0.5) * gmax[:, gi:gi + 1].astype(np.float64) / q).astype(np.float32)
+        for _ in range(3):                                                # a few ulps either way
+            step = rng.integers(-1, 2, size=x.shape)
+            x = np.where(step > 0, np.nextafter(x, np.float32(np.inf)),
+                         np.where(step < 0, np.nextafter(x, np.float32(-np.inf)), x)).astype(np.float32)
+        x[:, 0] = gmax[:, gi]                                            # the group's max |w|
+        W[:, gi * g:(gi + 1) * g] = x
+    # the fixture must hold weights where fp32 and fp64 round differently
+    s32 = (gmax / np.float32(q)).astype(np.float32)
+    r32 = (np.float32(1.0) / s32).astype(np.float32)
+    fast = np.rint((W.reshape(out, n // g, g) * r32[:, :, None]).astype(np.float32)).reshape(out, n)
+    ref_codes, _, _ = oracle.gptq_columns(W.astype(np.float64), np.eye(n), bits=4, g=g)
+    assert np.mean(np.clip(fast, -8, 7) != ref_codes) >= 0.005
+    codes, scales, g_idx, stats = api.gptq_quantize_columns(torch.from_numpy(W).to(gpu),
+                                                            torch.eye(n, dtype=torch.float32, device=gpu), None,
+                                                            bits=4, group_size=g, block_size=block)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+
+
 def test_columns_stage_alone_with_oracle_U(gpu):
     """Stage 3 given the oracle's own U (fp32-rounded): isolates the loop."""
     from post_int4_weight_amd import api
