@@ -7,9 +7,9 @@
 //  * the proxy Hessian H (+)= X^T X ("GPTQ versus AWQ objectives", "A strong
 //    answer"), run on a transposed, panel-blocked chunk of the calibration
 //    rows (xt_offset) with A = B = Xt: only tiles on or above the diagonal
-//    are computed; the tile is added into H (fp32) and, on request,
-//    mirrored, or, when a chunk is split over depth (grid.y), stored into the
-//    split's own partial H;
+//    are computed; the tile is added into H (fp32) or, when a chunk is split
+//    over depth (grid.y), stored into the split's own partial H; the lower
+//    triangle is mirrored by a separate pass at the end of each call;
 //  * AWQ's calibration output error ||X dW^T||^2 (same page, AWQ paragraph),
 //    with A = X [rows, in] and B = dW [out, in] split into a bf16 high part and
 //    a bf16 residual (dW = hi + lo to ~16 significant bits): the K loop runs
@@ -74,7 +74,7 @@ struct Bf16GemmArgs {
     // EPI_HESSIAN operands are panel-blocked (xt_offset): pstride elements per panel of BMX rows
     int64_t pstride;
     // EPI_HESSIAN
-    float* H; int64_t ldh; int mirror; int T; int store_not_add;
+    float* H; int64_t ldh; int T; int store_not_add;
     // EPI_SUMSQ
     double* partial;           // [gridDim.y][tiles]
     int64_t tiles_n, ntiles;
@@ -220,20 +220,18 @@ template <int BMX, int EPI, int NW = 4, int MF = 32>
 __device__ __forceinline__ void store_tile(
     const Bf16GemmArgs& g,
     typename WaveTile<BMX, NW, MF>::acc_t (&acc)[WaveTile<BMX, NW, MF>::WA][WaveTile<BMX, NW, MF>::WB], int64_t i0,
-    int64_t j0, bool diag, int64_t L, unsigned char* smem);
+    int64_t j0, int64_t L, unsigned char* smem);
 
 // Register-staged variant: any shape (bounds-checked loads, zero fill).
 template <int BMX, int EPI>
 __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, int64_t nwork) {
     constexpr int WT = BMX / 64;
     int64_t i0, j0, L = 0;
-    bool diag = false;
     if (EPI == EPI_HESSIAN) {
         int ti, tj;
         if (!hessian_tile(blockIdx.x, g.T, ti, tj)) return;
         i0 = (int64_t)ti * BMX;
         j0 = (int64_t)tj * BMX;
-        diag = (ti == tj);
     } else {
         L = sumsq_tile(blockIdx.x, nwork / g.tiles_n, g.tiles_n);
         if (L < 0) return;
@@ -319,7 +317,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_bf16_nt_kernel(Bf16GemmArgs g, in
         __syncthreads();
     }
 
-    store_tile<BMX, EPI>(g, acc, i0, j0, diag, L, smem);
+    store_tile<BMX, EPI>(g, acc, i0, j0, L, smem);
 }
 
 // Tile epilogue (accumulator layout in MfmaShape). `smem` is free scratch by now.
@@ -327,7 +325,7 @@ template <int BMX, int EPI, int NW, int MF>
 __device__ __forceinline__ void store_tile(
     const Bf16GemmArgs& g,
     typename WaveTile<BMX, NW, MF>::acc_t (&acc)[WaveTile<BMX, NW, MF>::WA][WaveTile<BMX, NW, MF>::WB], int64_t i0,
-    int64_t j0, bool diag, int64_t L, unsigned char* smem) {
+    int64_t j0, int64_t L, unsigned char* smem) {
     using WTL = WaveTile<BMX, NW, MF>;
     using Sh = MfmaShape<MF>;
     constexpr int WA = WTL::WA, WB = WTL::WB, NACC = Sh::NACC;
@@ -343,7 +341,7 @@ __device__ __forceinline__ void store_tile(
     // 90 us per 256 x 256 tile (an X^T X launch of the down_proj shape runs
     // 25 tiles per CU); batched, about 45 us, most of it the burst of H
     // traffic when a round's tiles end together.
-    auto add_store_full = [&](float* Ct, int64_t ld, float alpha, float* Cm, bool mirror) {
+    auto add_store_full = [&](float* Ct, int64_t ld, float alpha) {
         float old[2][WB][NACC];
         auto load_block = [&](int a, int slot) {
 #pragma unroll
@@ -364,7 +362,6 @@ __device__ __forceinline__ void store_tile(
                     const int ii = wm + MF * a + Sh::row(lane, r);
                     const float v = old[a & 1][b][r] + alpha * acc[a][b][r];
                     Ct[(int64_t)ii * ld + jj] = v;
-                    if (mirror) Cm[(int64_t)jj * ld + ii] = v;
                 }
             }
         }
@@ -372,10 +369,9 @@ __device__ __forceinline__ void store_tile(
     if (EPI == EPI_HESSIAN) {
         float* Hy = g.H + (int64_t)blockIdx.y * g.h_batch_stride;
         float* Ht = Hy + i0 * g.ldh + j0;                       // tile origin
-        float* Hm = Hy + j0 * g.ldh + i0;                       // mirror origin
         const int ld = (int)g.ldh;
         if (mi == BMX && nj == BMX && !g.store_not_add) {
-            add_store_full(Ht, ld, 1.f, Hm, g.mirror && !diag);
+            add_store_full(Ht, ld, 1.f);
             return;
         }
 #pragma unroll
@@ -390,14 +386,13 @@ __device__ __forceinline__ void store_tile(
                         float* p = Ht + (int64_t)ii * ld + jj;
                         const float v = g.store_not_add ? acc[a][b][r] : (*p + acc[a][b][r]);
                         *p = v;
-                        if (g.mirror && !diag) Hm[(int64_t)jj * ld + ii] = v;
                     }
                 }
             }
     } else if (EPI == EPI_GEMM) {
         float* Ct = g.C + i0 * g.ldc + j0;
         if (mi == BMX && nj == BMX && g.beta_one) {
-            add_store_full(Ct, g.ldc, g.alpha, nullptr, false);
+            add_store_full(Ct, g.ldc, g.alpha);
             return;
         }
 #pragma unroll
@@ -526,13 +521,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         }
     }
     int64_t i0, j0, L = 0;
-    bool diag = false;
     if (EPI == EPI_HESSIAN) {
         int ti, tj;
         if (!hessian_tile(blockIdx.x, g.T, ti, tj)) return;
         i0 = (int64_t)ti * BMX;
         j0 = (int64_t)tj * BMX;
-        diag = (ti == tj);
     } else if (EPI == EPI_GEMM) {
         // With at least 8 tile rows, XCD x takes whole rows (its tiles share
         // A panels in its L2): its k-th is row 8k + x for even k and
@@ -795,7 +788,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
     }
     wait_vmcnt<0, true>();
     __syncthreads();
-    store_tile<BMX, EPI, NW, MF>(g, acc, i0, j0, diag, L, smem);
+    store_tile<BMX, EPI, NW, MF>(g, acc, i0, j0, L, smem);
 }
 
 // Opt a kernel into more than 64 KB of dynamic LDS (once per instantiation).
@@ -1163,18 +1156,70 @@ __global__ __launch_bounds__(256) void transpose_sumsq_kernel(const uint16_t* __
     }
 }
 
-__global__ void mirror_diag_blocks_kernel(float* H, int64_t n, int bm) {
-    const int64_t base = (int64_t)blockIdx.y * bm;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < (int64_t)bm * bm;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = base + e / bm, j = base + e % bm;
-        if (i < n && j < n && i > j) H[i * n + j] = H[j * n + i];
+// H[j][i] = H[i][j] for every i < j, once per accumulation (the X^T X tiles
+// and the fp32 path add into the upper triangle only). One workgroup per
+// 64 x 64 tile of the upper triangle (blockIdx.y = tile row <= blockIdx.x =
+// tile column): the tile is read row by row in 16-byte pieces, turned
+// through LDS and written row by row into its mirror position; a diagonal
+// tile writes its own strictly lower half. Mirroring inside the X^T X
+// epilogue instead (column-wise 4-byte stores from every tile of the last
+// chunk) lengthened that launch by about 1 ms at in = 28672; this pass
+// moves the 2 x 1.6 GB at HBM rate.
+constexpr int MIR = 64;
+__global__ __launch_bounds__(256) void mirror_upper_kernel(float* H, int64_t n) {
+    const int64_t I = blockIdx.y, J = blockIdx.x;
+    if (I > J) return;
+    __shared__ float tile[MIR][MIR + 1];
+    const int t = threadIdx.x, cq = 4 * (t % 16), rq = t / 16;
+    const int64_t r0 = I * MIR, c0 = J * MIR;
+    const bool full = r0 + MIR <= n && c0 + MIR <= n && n % 4 == 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = rq + 16 * p;
+        const int64_t gi = r0 + r;
+        if (full) {
+            const float4 v = *(const float4*)(H + gi * n + c0 + cq);
+            tile[r][cq] = v.x; tile[r][cq + 1] = v.y; tile[r][cq + 2] = v.z; tile[r][cq + 3] = v.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t gj = c0 + cq + q;
+                tile[r][cq + q] = (gi < n && gj < n) ? H[gi * n + gj] : 0.f;
+            }
+        }
     }
+    __syncthreads();
+    // mirror row c0 + c holds tile column c; its columns r0 + cq .. are tile rows cq ..
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int c = rq + 16 * p;
+        const int64_t gi = c0 + c;
+        if (full && I < J) {
+            *(float4*)(H + gi * n + r0 + cq) = make_float4(tile[cq][c], tile[cq + 1][c], tile[cq + 2][c], tile[cq + 3][c]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t gj = r0 + cq + q;
+                if (gi < n && gj < n && gi > gj) H[gi * n + gj] = tile[cq + q][c];
+            }
+        }
+    }
+}
+
+int launch_mirror_upper(float* H, int64_t n, hipStream_t st) {
+    const int64_t T = cdiv(n, MIR);
+    if (T > 65535) {
+        set_error("hessian_accumulate: in = %lld is beyond the mirror pass's grid", (long long)n);
+        return PTQ_EINVAL;
+    }
+    hipLaunchKernelGGL(mirror_upper_kernel, dim3((unsigned)T, (unsigned)T), dim3(256), 0, st, H, n);
+    PTQ_LAUNCH_CHECK();
+    return PTQ_OK;
 }
 
 // H[i][j] += sum over the splits of part[s][i][j] on and above the diagonal
 // (in split order); one row per blockIdx.y. The lower triangle is mirrored
-// once after the last chunk.
+// once after the last chunk (mirror_upper_kernel).
 __global__ void reduce_partials_kernel(float* H, const float* part, int nsplit, int64_t n) {
     const int64_t nn = n * n;
     for (int64_t i = blockIdx.y; i < n; i += gridDim.y)
@@ -1313,9 +1358,7 @@ int run_xtx(const XtxPlan& plan, bool per_chunk_d, float* H, double* d, int64_t 
         g.B = (const float*)X; g.ldb = ldx; g.layout_b = B_KN;
         g.C = H; g.ldc = n; g.alpha = 1.f; g.beta_one = 1; g.tri = TRI_NONE; g.upper_only = 1;
         PTQ_TRY(launch_gemm_f32(g, st));
-        hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(1024, 1), dim3(256), 0, st, H, n, (int)n);
-        PTQ_LAUNCH_CHECK();
-        return PTQ_OK;
+        return launch_mirror_upper(H, n, st);
     }
 
     uint16_t* Xt = ar.take<uint16_t>((size_t)p.T * p.bm * (p.chunk + XT_PAD));
@@ -1344,7 +1387,6 @@ int run_xtx(const XtxPlan& plan, bool per_chunk_d, float* H, double* d, int64_t 
             PTQ_LAUNCH_CHECK();
             gofs = 0;
         }
-        const bool last = r0 + p.chunk >= rows;
         const int ns = (p.nsplit > 1 && nr >= p.nsplit * SPLIT_ROWS_MIN) ? p.nsplit : 1;
         const int64_t kper = cdiv(cdiv(kt, ns), KT) * KT;
         {
@@ -1356,7 +1398,7 @@ int run_xtx(const XtxPlan& plan, bool per_chunk_d, float* H, double* d, int64_t 
             g.pstride = pstride; g.lda = 64; g.ldb = 64; g.M = n; g.N = n;
             g.H = (ns > 1) ? hpart : H;
             g.h_batch_stride = n * n;
-            g.ldh = n; g.mirror = (ns == 1 && last) ? 1 : 0; g.T = p.T; g.store_not_add = (ns > 1) ? 1 : 0;
+            g.ldh = n; g.T = p.T; g.store_not_add = (ns > 1) ? 1 : 0;
             prof_begin(PROF_XTX_GEMM, st, 2.0 * (double)p.bm * p.bm * (double)ntiles * (double)kt);
             const int rc = (p.bm == 256) ? launch_nt<256, EPI_HESSIAN>(g, ntiles, (unsigned)ns, st)
                                          : launch_nt<128, EPI_HESSIAN>(g, ntiles, (unsigned)ns, st);
@@ -1364,13 +1406,10 @@ int run_xtx(const XtxPlan& plan, bool per_chunk_d, float* H, double* d, int64_t 
             PTQ_TRY(rc);
         }
         if (ns > 1) {
-            // reduce the split partials into H (upper triangle; mirrored after the last chunk)
+            // reduce the split partials into H (upper triangle)
             hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 32),
                                                             (unsigned)std::min<int64_t>(n, 65535)),
                                dim3(256), 0, st, H, hpart, ns, n);
-            PTQ_LAUNCH_CHECK();
-        } else if (last) {
-            hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(64, (unsigned)p.T), dim3(256), 0, st, H, n, p.bm);
             PTQ_LAUNCH_CHECK();
         }
     }
@@ -1379,12 +1418,8 @@ int run_xtx(const XtxPlan& plan, bool per_chunk_d, float* H, double* d, int64_t 
                            n);
         PTQ_LAUNCH_CHECK();
     }
-    if (p.nsplit > 1) {
-        // chunks that ran without splitting left only their upper triangle: mirror all
-        hipLaunchKernelGGL(mirror_diag_blocks_kernel, dim3(1024, 1), dim3(256), 0, st, H, n, (int)n);
-        PTQ_LAUNCH_CHECK();
-    }
-    return PTQ_OK;
+    // every chunk added into the upper triangle only
+    return launch_mirror_upper(H, n, st);
 }
 
 }  // namespace
