@@ -11,6 +11,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running case")
+    import gpu_util
+    gpu_util.set_config(config)
 
 
 @pytest.fixture(scope="session")

@@ -5,10 +5,31 @@ import numpy as np
 import torch
 
 
-def announce(msg: str):
-    """Name the case before a GPU step, flushed, so a failing run says which."""
-    print(f"[gpu-case] {msg}", flush=True)
+_CONFIG = None   # pytest's config, set by conftest.py
+
+
+def set_config(config) -> None:
+    global _CONFIG
+    _CONFIG = config
+
+
+def progress(msg: str, flush: bool = True) -> None:
+    """Print past pytest's output capture, flushed: the long host-side oracle
+    steps of the full-size tests report as they go (a run that prints nothing
+    for minutes cannot be told from a hung one), and a failing run names its
+    case."""
+    capman = _CONFIG.pluginmanager.getplugin("capturemanager") if _CONFIG is not None else None
+    if capman is not None:
+        with capman.global_and_fixture_disabled():
+            print(msg, flush=True)
+    else:
+        print(msg, flush=True)
     sys.stdout.flush()
+
+
+def announce(msg: str) -> None:
+    """Name the case before a GPU step, flushed, so a failing run says which."""
+    progress(f"[gpu-case] {msg}")
 
 
 def to64(t: torch.Tensor) -> np.ndarray:

@@ -25,7 +25,7 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, code_match, rel_fro, to64, zeros_h
+from gpu_util import announce, code_match, rel_fro, to64, zeros_h, progress
 
 # generating X, H and the host factorization take minutes, not seconds
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1500)]
@@ -49,7 +49,7 @@ def down_proj(gpu):
         xc = X[r0:r0 + 8192].cpu().float().numpy().astype(np.float64)
         d0 += np.sum(xc * xc, axis=0)
         if (r0 // 8192) % 8 == 7:
-            print(f"[oracle] column sums of squares: {r0 + 8192} of {cfg.rows} rows", flush=True)
+            progress(f"[oracle] column sums of squares: {r0 + 8192} of {cfg.rows} rows", flush=True)
     return cfg, W, X, H, d, d0
 
 
@@ -74,10 +74,10 @@ def oracle_U(down_proj):
     announce("down_proj: oracle factor of the 28672^2 H on the host")
     Hh = H.cpu().numpy().astype(np.float64)
     Hh[np.diag_indices(n)] += lam0
-    print("[oracle] H copied to the host; reversed Cholesky + triangular inverse", flush=True)
+    progress("[oracle] H copied to the host; reversed Cholesky + triangular inverse", flush=True)
     Uref = oracle.inverse_upper_factor(Hh)
     del Hh
-    print("[oracle] U of n = 28672 formed", flush=True)
+    progress("[oracle] U of n = 28672 formed", flush=True)
     return Uref, lam0
 
 
@@ -90,7 +90,7 @@ def test_full_U(down_proj, oracle_U):
     torch.cuda.synchronize()
     assert abs(lam - lam0) <= 1e-12 * lam0
     err = _rel_fro_rows(U, Uref)
-    print(f"[oracle] full U (28672^2): relative Frobenius error {err:.3e}", flush=True)
+    progress(f"[oracle] full U (28672^2): relative Frobenius error {err:.3e}", flush=True)
     assert err <= 1e-4, err
 
 
@@ -104,7 +104,7 @@ def test_hessian_blocks(down_proj):
         H0b, _ = oracle.proxy_hessian(to64(X[:, cols].cpu()), chunk_rows=16384)
         Hb = H[c0:c0 + TRAIL, c0:c0 + TRAIL].cpu().double().numpy()
         assert rel_fro(Hb, H0b) <= 1e-5
-        print(f"[oracle] H block at {c0} checked", flush=True)
+        progress(f"[oracle] H block at {c0} checked", flush=True)
     # an off-diagonal block, error measured against sqrt(H_ii H_jj)
     ci = list(range(1000, 1256))
     cj = list(range(n - 3000, n - 2744))
@@ -149,7 +149,7 @@ def test_gptq_fullsize(down_proj, oracle_U, bits):
     c_ref, s_ref, _ = oracle.gptq_columns(to64(W[rows].cpu()), Uref, bits, 128)
     c_gpu = res["codes"][rows].cpu().numpy()
     assert code_match(c_gpu, c_ref) >= 0.99, code_match(c_gpu, c_ref)
-    print(f"[oracle] loop on {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal",
+    progress(f"[oracle] loop on {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal",
           flush=True)
 
     codes = res["codes"]
@@ -170,7 +170,7 @@ def test_gptq_fullsize(down_proj, oracle_U, bits):
     Hd.diagonal().sub_(lam)
     obj = float(((dW @ Hd) * dW).sum())
     assert abs(res["stats"]["objective"] - obj) <= 2e-3 * obj
-    print("[check] loop identities checked", flush=True)
+    progress("[check] loop identities checked", flush=True)
     # relative output error of the sampled rows within 1% of the oracle's
     gi = torch.arange(n, device=W.device) // 128
     Ws = W[rows].double()
@@ -181,7 +181,7 @@ def test_gptq_fullsize(down_proj, oracle_U, bits):
     e_gpu = float(((dWg @ Hd) * dWg).sum()) / den
     e_ref = float(((dWr @ Hd) * dWr).sum()) / den
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
-    print(f"[oracle] sampled rows: relative output error {e_gpu:.6g} vs oracle {e_ref:.6g}", flush=True)
+    progress(f"[oracle] sampled rows: relative output error {e_gpu:.6g} vs oracle {e_ref:.6g}", flush=True)
     # calibration error below plain RTN's (the loop's purpose)
     Wrtn_codes, Wrtn_scales = oracle.rtn(to64(W.cpu()), bits, 128)
     Wrtn = torch.tensor(oracle.dequantize(Wrtn_codes, Wrtn_scales, np.arange(n) // 128), device=W.device)

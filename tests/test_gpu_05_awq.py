@@ -11,7 +11,7 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, code_match, to64
+from gpu_util import announce, code_match, to64, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def test_awq_llama70b_q_proj(gpu):
     for a in alphas:
         _, _, What = oracle.awq_quantize(W64, m ** a, 4, 128)
         errors.append(oracle.output_error(X64, W64, What))
-        print(f"[oracle] alpha {a:.2f}: error {errors[-1]:.6e}", flush=True)
+        progress(f"[oracle] alpha {a:.2f}: error {errors[-1]:.6e}", flush=True)
     errors = np.array(errors)
     best = int(np.argmin(errors))
     s = m ** alphas[best]

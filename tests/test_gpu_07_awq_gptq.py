@@ -12,7 +12,7 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, code_match, rel_fro, to64, zeros_h
+from gpu_util import announce, code_match, rel_fro, to64, zeros_h, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_awq_gptq_vs_oracle(gpu, out, n, rows, bits, alpha, act_order, dtype):
     # stats[3] is the calibration error in the original basis
     obj = oracle.output_error(X64, W64, What_orig)
     assert abs(res["stats"]["objective"] - obj) <= 2e-3 * obj
-    print(f"[oracle] relative output error {e_gpu:.5g} vs {e_ref:.5g}; codes "
+    progress(f"[oracle] relative output error {e_gpu:.5g} vs {e_ref:.5g}; codes "
           f"{100 * code_match(codes, ref['codes']):.3f}% equal", flush=True)
 
 
@@ -95,5 +95,5 @@ def test_composition_after_awq_search(gpu):
                                np.arange(1024) // 128) / s64[None, :]
     e_c = oracle.output_error(X64, W64, What_c)
     e_a = oracle.output_error(X64, W64, What_a)
-    print(f"[check] calibration error: AWQ {e_a:.5g}, AWQ then GPTQ {e_c:.5g}", flush=True)
+    progress(f"[check] calibration error: AWQ {e_a:.5g}, AWQ then GPTQ {e_c:.5g}", flush=True)
     assert e_c < e_a

@@ -13,7 +13,7 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, code_match, rel_fro, to64, zeros_h
+from gpu_util import announce, code_match, rel_fro, to64, zeros_h, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def test_zero_point_vs_oracle(gpu, out, n, rows, bits, g, act_order, dtype):
     dW = W64 - What
     quad = float(np.sum((dW @ Hd) * dW))
     assert abs(res["stats"]["sum_err2"] - quad) <= 1e-3 * quad
-    print(f"[oracle] relative output error {e_gpu:.5g} vs {e_ref:.5g}; codes "
+    progress(f"[oracle] relative output error {e_gpu:.5g} vs {e_ref:.5g}; codes "
           f"{100 * code_match(codes, ref['codes']):.3f}% equal", flush=True)
 
     if bits <= 4:

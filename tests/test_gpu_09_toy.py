@@ -17,7 +17,7 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, zeros_h
+from gpu_util import announce, zeros_h, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_toy_table_ordering(gpu):
             e_ref = oracle.output_error(X, W64, ref[m]) / (X.shape[0] * out)
             assert abs(e - e_ref) <= 0.01 * e_ref, (sname, m, e, e_ref)
             mse[sname, m] = e
-        print(f"[toy] {sname:12s} RTN {mse[sname, 'RTN']:.4f}  GPTQ {mse[sname, 'GPTQ']:.4f}  "
+        progress(f"[toy] {sname:12s} RTN {mse[sname, 'RTN']:.4f}  GPTQ {mse[sname, 'GPTQ']:.4f}  "
               f"AWQ {mse[sname, 'AWQ']:.4f}", flush=True)
     for sname in ("calibration", "same"):
         assert mse[sname, "AWQ"] < mse[sname, "GPTQ"] < mse[sname, "RTN"], sname

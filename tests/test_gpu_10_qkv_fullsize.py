@@ -28,7 +28,7 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, code_match, rel_fro, to64, zeros_h
+from gpu_util import announce, code_match, rel_fro, to64, zeros_h, progress
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,7 @@ def test_qkv_gptq_fullsize(qkv, qkv_d0):
     for c0 in (0, n - 512):
         H0b, _ = oracle.proxy_hessian(to64(X[:, c0:c0 + 512].cpu()), chunk_rows=16384)
         assert rel_fro(H[c0:c0 + 512, c0:c0 + 512].cpu().double().numpy(), H0b) <= 1e-5
-    print("[oracle] d and H blocks checked", flush=True)
+    progress("[oracle] d and H blocks checked", flush=True)
 
     res = api.gptq_quantize_layer(W, H, d, bits=4, group_size=128, damp=0.01)
     U, _, lam = api.gptq_inverse_factor(H, d, damp=0.01)
@@ -80,7 +80,7 @@ def test_qkv_gptq_fullsize(qkv, qkv_d0):
     Uref = oracle.inverse_upper_factor(Hh)
     del Hh
     assert rel_fro(U.cpu().numpy().astype(np.float64), Uref) <= 1e-4
-    print("[oracle] full U checked", flush=True)
+    progress("[oracle] full U checked", flush=True)
 
     rows = list(range(0, out, out // SAMPLE_ROWS))
     c_ref, s_ref, _ = oracle.gptq_columns(to64(W[rows].cpu()), Uref, 4, 128)
@@ -95,7 +95,7 @@ def test_qkv_gptq_fullsize(qkv, qkv_d0):
     e_gpu = float(((dWg @ Hd) * dWg).sum()) / den
     e_ref = float(((dWr @ Hd) * dWr).sum()) / den
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
-    print(f"[oracle] {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal, relative output "
+    progress(f"[oracle] {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal, relative output "
           f"error {e_gpu:.6g} vs {e_ref:.6g}", flush=True)
 
 
@@ -118,7 +118,7 @@ def test_qkv_gptq_act_order_fullsize(qkv, qkv_d0):
     Uref = oracle.inverse_upper_factor(Hh[np.ix_(p, p)])
     del Hh
     assert rel_fro(U.cpu().numpy().astype(np.float64), Uref) <= 1e-4
-    print("[oracle] act-order permutation and full U checked", flush=True)
+    progress("[oracle] act-order permutation and full U checked", flush=True)
 
     rows = list(range(0, out, out // SAMPLE_ROWS))
     cp_ref, s_ref, _ = oracle.gptq_columns(to64(W[rows].cpu())[:, p], Uref, 4, 128)
@@ -138,7 +138,7 @@ def test_qkv_gptq_act_order_fullsize(qkv, qkv_d0):
     e_gpu = float(((dWg @ Hd) * dWg).sum()) / den
     e_ref = float(((dWr @ Hd) * dWr).sum()) / den
     assert abs(e_gpu - e_ref) <= 0.01 * e_ref, (e_gpu, e_ref)
-    print(f"[oracle] act-order, {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal, "
+    progress(f"[oracle] act-order, {len(rows)} sampled rows: {100 * code_match(c_gpu, c_ref):.3f}% codes equal, "
           f"relative output error {e_gpu:.6g} vs {e_ref:.6g}", flush=True)
 
 
@@ -173,7 +173,7 @@ def test_awq_heldout_report(qkv, gpu):
         for m, Wq in What.items():
             e = _err(Xs, W, Wq)
             table[sname, m] = e
-            print(f"[report] {sname:11s} {m:22s} relative error {e / energy:.6f}  MSE "
+            progress(f"[report] {sname:11s} {m:22s} relative error {e / energy:.6f}  MSE "
                   f"{e / (Xs.shape[0] * cfg.out):.6e}", flush=True)
     awq_key = [k for k in What if k.startswith("AWQ")][0]
     assert table["calibration", awq_key] <= table["calibration", "RTN"] * (1 + 1e-9)

@@ -17,7 +17,7 @@ import torch
 
 import inputs
 import oracle
-from gpu_util import announce, to64, zeros_h
+from gpu_util import announce, to64, zeros_h, progress
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -29,7 +29,7 @@ def _check(res, X64, W64, What):
     e, y = res
     assert abs(e - e_ref) <= TOL * e_ref, (e, e_ref)
     assert abs(y - y_ref) <= TOL * y_ref, (y, y_ref)
-    print(f"[oracle] error {e:.8g} vs {e_ref:.8g}, energy {y:.8g} vs {y_ref:.8g}", flush=True)
+    progress(f"[oracle] error {e:.8g} vs {e_ref:.8g}, energy {y:.8g} vs {y_ref:.8g}", flush=True)
 
 
 @pytest.mark.parametrize("out,n,rows,g,dtype", [
