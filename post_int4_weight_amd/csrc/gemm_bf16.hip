@@ -105,6 +105,14 @@ struct Bf16GemmArgs {
 __host__ __device__ inline bool split3_subblocks(int64_t tiles_m, int64_t tiles_n, int tri, int upper_only) {
     return tiles_m >= 8 && tiles_n >= 8 && tri == TRI_NONE && !upper_only;
 }
+// Products with a triangular B: a tile's depth depends on its column only, so
+// whole tile columns go to the XCDs (zigzag) in order of decreasing depth,
+// and the last tiles to start are the shortest; dealt by rows, every row
+// would run from deep to shallow and deep tiles of the last rows would start
+// near the end of the launch.
+__host__ __device__ inline bool split3_column_deal(int64_t tiles_n, int tri, int upper_only) {
+    return tiles_n >= 8 && (tri == TRI_B_UPPER_NK || tri == TRI_B_UPPER_KN) && !upper_only;
+}
 
 // AWQ error tiles: 4 x 8 sub-blocks of the tile grid dealt round-robin to
 // the XCDs, so the 32 tiles an XCD runs side by side read 12 panels through
@@ -531,7 +539,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         // A panels in its L2): its k-th is row 8k + x for even k and
         // 8k + 7 - x for odd k, a zigzag that balances over the XCDs the
         // triangular products whose row work falls with the row (A upper,
-        // upper_only). Else plain row-major.
+        // upper_only); products with a triangular B deal whole tile columns
+        // the same way (split3_column_deal). Else plain row-major.
         int64_t tm, tn;
         if (split3_subblocks(g.tiles_m, g.tiles_n, g.tri, g.upper_only)) {
             // 4 x 8 sub-blocks of tiles dealt round-robin to the XCDs: the 32
@@ -542,6 +551,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
             tm = 4 * (sbi / sbc) + w / 8;
             tn = 8 * (sbi % sbc) + w % 8;
             if (tm >= g.tiles_m || tn >= g.tiles_n) return;
+        } else if (split3_column_deal(g.tiles_n, g.tri, g.upper_only)) {
+            const int64_t x = bid % NXCD, i = bid / NXCD, k = i / g.tiles_m;
+            tn = NXCD * k + ((k & 1) ? NXCD - 1 - x : x);
+            tm = i % g.tiles_m;
+            if (tn >= g.tiles_n) return;
         } else if (g.tiles_m >= NXCD) {
             const int64_t x = bid % NXCD, i = bid / NXCD, k = i / g.tiles_n;
             tm = NXCD * k + ((k & 1) ? NXCD - 1 - x : x);
@@ -1001,6 +1015,8 @@ Bf16GemmArgs split3_args(const GemmArgs& a, const uint16_t* pa, const uint16_t* 
 unsigned split3_grid(const Bf16GemmArgs& g) {
     if (split3_subblocks(g.tiles_m, g.tiles_n, g.tri, g.upper_only))
         return (unsigned)(cdiv(cdiv(g.tiles_m, 4) * cdiv(g.tiles_n, 8), NXCD) * NXCD * 32);
+    if (split3_column_deal(g.tiles_n, g.tri, g.upper_only))
+        return (unsigned)(NXCD * cdiv(g.tiles_n, NXCD) * g.tiles_m);
     return (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n : g.tiles_m * g.tiles_n);
 }
 // op(B) is A's transpose view: one set of planes serves both operands
