@@ -259,6 +259,18 @@ __device__ __forceinline__ void f32_wait_vmcnt() {
 // BT = 128 (4 waves of 64 x 64 = 2 x 2 MFMA blocks) or 64 (4 waves of one
 // 32 x 32 block each): the small tile quadruples the workgroups of the small
 // products deep in the U recursion, which otherwise run on a few CUs.
+// Products with a triangular B: a tile's depth depends on its column only,
+// so whole tile columns go to the XCDs (the same zigzag) in order of
+// decreasing depth and the last tiles to start are the shortest.
+__host__ __device__ inline bool column_deal(const GemmArgs& g, int64_t tiles_n) {
+    return tiles_n >= XCDS && (g.tri == TRI_B_UPPER_NK || g.tri == TRI_B_UPPER_KN) && !g.upper_only;
+}
+// workgroups of a direct launch over tm x tn tiles
+__host__ __device__ inline unsigned direct_grid(const GemmArgs& g, int64_t tm, int64_t tn) {
+    if (column_deal(g, tn)) return (unsigned)(XCDS * cdiv(tn, XCDS) * tm);
+    return (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
+}
+
 template <bool B_KMAJOR, int DNST, int BT>
 __device__ __forceinline__ void direct_tile(const GemmArgs& g, int64_t tiles_m, int64_t tiles_n, unsigned bid) {
     static_assert(DNST >= 3, "the ring needs three stages");
@@ -271,10 +283,16 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& g, int64_t tiles_m, 
     // for even k and 8k + 7 - x for odd k: the tiles one XCD runs side by
     // side share A panels (and B panels across its rows) in its own L2, and
     // the zigzag keeps the triangular products (A upper, upper_only), whose
-    // work falls with the row, balanced over the XCDs. Fewer rows: plain
-    // row-major order over all XCDs.
+    // work falls with the row, balanced over the XCDs. Products with a
+    // triangular B take whole columns instead (column_deal). Fewer rows:
+    // plain row-major order over all XCDs.
     int64_t tm, tn;
-    if (tiles_m >= XCDS) {
+    if (column_deal(g, tiles_n)) {
+        const int64_t x = bid % XCDS, i = bid / XCDS, k = i / tiles_m;
+        tn = XCDS * k + ((k & 1) ? XCDS - 1 - x : x);
+        tm = i % tiles_m;
+        if (tn >= tiles_n) return;
+    } else if (tiles_m >= XCDS) {
         const int64_t x = bid % XCDS, i = bid / XCDS, k = i / tiles_n;
         tm = XCDS * k + ((k & 1) ? XCDS - 1 - x : x);
         tn = i % tiles_n;
@@ -505,7 +523,7 @@ int launch_direct_ring(const GemmArgs& a, hipStream_t st) {
         ready = true;
     }
     const int64_t tm = cdiv(a.M, BT), tn = cdiv(a.N, BT);
-    const unsigned grid = (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
+    const unsigned grid = direct_grid(a, tm, tn);
     hipLaunchKernelGGL((gemm_f32_direct_kernel<B_KMAJOR, DNST, BT>), dim3(grid), dim3(NT), DNST * DSTAGE_BYTES<BT>,
                        st, a, tm, tn);
     PTQ_LAUNCH_CHECK();
@@ -551,11 +569,8 @@ int launch_direct_pair(const GemmArgs& a0, const GemmArgs& a1, hipStream_t st) {
                                     hipFuncAttributeMaxDynamicSharedMemorySize, DNST * DSTAGE_BYTES<BT>));
         ready = true;
     }
-    auto grid_of = [](int64_t tm, int64_t tn) {
-        return (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
-    };
     const int64_t tm0 = cdiv(a0.M, BT), tn0 = cdiv(a0.N, BT), tm1 = cdiv(a1.M, BT), tn1 = cdiv(a1.N, BT);
-    const unsigned grid0 = (unsigned)cdiv(grid_of(tm0, tn0), XCDS) * XCDS, grid1 = grid_of(tm1, tn1);
+    const unsigned grid0 = (unsigned)cdiv(direct_grid(a0, tm0, tn0), XCDS) * XCDS, grid1 = direct_grid(a1, tm1, tn1);
     hipLaunchKernelGGL((gemm_f32_direct_pair_kernel<DNST, BT>), dim3(grid0 + grid1), dim3(NT),
                        DNST * DSTAGE_BYTES<BT>, st, a0, tm0, tn0, grid0, a1, tm1, tn1);
     PTQ_LAUNCH_CHECK();
