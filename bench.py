@@ -426,7 +426,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the path here is the single-GPU kernel set (--gpus {args.gpus} "
-              "is not supported: this build measures one GPU's share at its real shape)", file=sys.stderr)
+              "is not supported: it measures one GPU's share of the work at its real shape)", file=sys.stderr)
         sys.exit(2)
 
     import torch
