@@ -67,11 +67,14 @@ def test_split3_large_ragged(gpu, beta_one):
     assert rel_fro(C[:, :N].cpu().double().numpy(), want) < 1e-5
 
 
+# n = 2100: nine 256-wide tile columns, the last ragged, so the products
+# with a triangular B take the whole-column deal over the XCDs; C starts as
+# NaN, so a tile left out shows
+@pytest.mark.parametrize("n,m", [(640, 544), (2100, 300)])
 @pytest.mark.parametrize("tri", [1, 2, 3])
-def test_split3_triangles(gpu, tri):
+def test_split3_triangles(gpu, tri, n, m):
     from post_int4_weight_amd import api
-    announce(f"gemm_f32_split3 triangle mode {tri}")
-    n, m = 640, 544
+    announce(f"gemm_f32_split3 triangle mode {tri} n={n} m={m}")
     g = torch.Generator().manual_seed(tri)
     T = torch.triu(torch.randn(n, n, generator=g))
     if tri == 1:      # C[n, m] = T[n, n] X[n, m], A upper
