@@ -98,21 +98,15 @@ struct Bf16GemmArgs {
     float alpha2; int beta_one2; int tri2; int upper_only2;
 };
 
-// EPI_GEMM tile order: 4 x 8 sub-blocks per XCD for dense products of at
-// least 8 x 8 tiles (the GPTQ trailing updates: column stage -0.7 ms); the
-// triangular ones keep whole tile rows in a zigzag over the XCDs, which
-// balances their uneven tile depths (sub-blocks made the factor 10 ms slower)
-__host__ __device__ inline bool split3_subblocks(int64_t tiles_m, int64_t tiles_n, int tri, int upper_only) {
-    return tiles_m >= 8 && tiles_n >= 8 && tri == TRI_NONE && !upper_only;
-}
-// Products with a triangular B: a tile's depth depends on its column only, so
-// whole tile columns go to the XCDs (zigzag) in order of decreasing depth,
-// and the last tiles to start are the shortest; dealt by rows, every row
-// would run from deep to shallow and deep tiles of the last rows would start
-// near the end of the launch.
-__host__ __device__ inline bool split3_column_deal(int64_t tiles_n, int tri, int upper_only) {
-    return tiles_n >= 8 && (tri == TRI_B_UPPER_NK || tri == TRI_B_UPPER_KN) && !upper_only;
-}
+// EPI_GEMM tile order (tile_order::gemm_tile with sub-blocks allowed): 4 x 8
+// sub-blocks per XCD for dense products of at least 8 x 8 tiles (the GPTQ
+// trailing updates: column stage -0.7 ms); the triangular ones take whole
+// tile rows (A upper, upper_only) or columns (B upper) in a zigzag over the
+// XCDs, which balances their uneven tile depths (sub-blocks made the factor
+// 10 ms slower)
+static_assert(tile_order::TRI_NONE_ == TRI_NONE && tile_order::TRI_A_UP == TRI_A_UPPER &&
+                  tile_order::TRI_B_UP_KN == TRI_B_UPPER_KN && tile_order::TRI_B_UP_NK == TRI_B_UPPER_NK,
+              "triangle codes");
 
 // AWQ error tiles: 4 x 8 sub-blocks of the tile grid dealt round-robin to
 // the XCDs, so the 32 tiles an XCD runs side by side read 12 panels through
@@ -535,42 +529,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_bf16_nt_direct_kernel(Bf16Gem
         i0 = (int64_t)ti * BMX;
         j0 = (int64_t)tj * BMX;
     } else if (EPI == EPI_GEMM) {
-        // With at least 8 tile rows, XCD x takes whole rows (its tiles share
-        // A panels in its L2): its k-th is row 8k + x for even k and
-        // 8k + 7 - x for odd k, a zigzag that balances over the XCDs the
-        // triangular products whose row work falls with the row (A upper,
-        // upper_only); products with a triangular B deal whole tile columns
-        // the same way (split3_column_deal). Else plain row-major.
         int64_t tm, tn;
-        if (split3_subblocks(g.tiles_m, g.tiles_n, g.tri, g.upper_only)) {
-            // 4 x 8 sub-blocks of tiles dealt round-robin to the XCDs: the 32
-            // tiles an XCD runs side by side read 12 panels through its L2
-            // (whole tile rows: 33)
-            const int64_t x = bid % NXCD, i = bid / NXCD, sbc = cdiv(g.tiles_n, 8);
-            const int64_t sbi = NXCD * (i / 32) + x, w = i % 32;
-            tm = 4 * (sbi / sbc) + w / 8;
-            tn = 8 * (sbi % sbc) + w % 8;
-            if (tm >= g.tiles_m || tn >= g.tiles_n) return;
-        } else if (split3_column_deal(g.tiles_n, g.tri, g.upper_only)) {
-            const int64_t x = bid % NXCD, i = bid / NXCD, k = i / g.tiles_m;
-            tn = NXCD * k + ((k & 1) ? NXCD - 1 - x : x);
-            tm = i % g.tiles_m;
-            if (tn >= g.tiles_n) return;
-        } else if (g.tiles_m >= NXCD) {
-            const int64_t x = bid % NXCD, i = bid / NXCD, k = i / g.tiles_n;
-            tm = NXCD * k + ((k & 1) ? NXCD - 1 - x : x);
-            tn = i % g.tiles_n;
-            if (tm >= g.tiles_m) return;
-        } else {
-            if ((int64_t)bid >= g.tiles_m * g.tiles_n) return;
-            tm = bid / g.tiles_n;
-            tn = bid % g.tiles_n;
-        }
-        // B upper triangular [K][N]: a tile's depth grows with its column,
-        // so columns go in descending order and the deepest tiles start first
-        // (the last tiles to start are then the shortest)
-        if (g.tri == TRI_B_UPPER_KN) tn = g.tiles_n - 1 - tn;
-        if (g.upper_only && tm > tn) return;
+        if (!tile_order::gemm_tile(bid, g.tiles_m, g.tiles_n, g.tri, g.upper_only, true, tm, tn)) return;
         i0 = tm * BMX;
         j0 = tn * BMX;
     } else {
@@ -1013,11 +973,7 @@ Bf16GemmArgs split3_args(const GemmArgs& a, const uint16_t* pa, const uint16_t* 
     return g;
 }
 unsigned split3_grid(const Bf16GemmArgs& g) {
-    if (split3_subblocks(g.tiles_m, g.tiles_n, g.tri, g.upper_only))
-        return (unsigned)(cdiv(cdiv(g.tiles_m, 4) * cdiv(g.tiles_n, 8), NXCD) * NXCD * 32);
-    if (split3_column_deal(g.tiles_n, g.tri, g.upper_only))
-        return (unsigned)(NXCD * cdiv(g.tiles_n, NXCD) * g.tiles_m);
-    return (unsigned)(g.tiles_m >= NXCD ? NXCD * cdiv(g.tiles_m, NXCD) * g.tiles_n : g.tiles_m * g.tiles_n);
+    return (unsigned)tile_order::gemm_grid(g.tiles_m, g.tiles_n, g.tri, g.upper_only, true);
 }
 // op(B) is A's transpose view: one set of planes serves both operands
 bool same_operand(const GemmArgs& a) {

@@ -23,6 +23,7 @@
 //    LDS row puts the two half-waves in disjoint banks. Interior tiles take
 //    an unguarded load path.
 #include "common.hpp"
+#include "tile_order.hpp"
 
 namespace ptq {
 namespace {
@@ -259,16 +260,10 @@ __device__ __forceinline__ void f32_wait_vmcnt() {
 // BT = 128 (4 waves of 64 x 64 = 2 x 2 MFMA blocks) or 64 (4 waves of one
 // 32 x 32 block each): the small tile quadruples the workgroups of the small
 // products deep in the U recursion, which otherwise run on a few CUs.
-// Products with a triangular B: a tile's depth depends on its column only,
-// so whole tile columns go to the XCDs (the same zigzag) in order of
-// decreasing depth and the last tiles to start are the shortest.
-__host__ __device__ inline bool column_deal(const GemmArgs& g, int64_t tiles_n) {
-    return tiles_n >= XCDS && (g.tri == TRI_B_UPPER_NK || g.tri == TRI_B_UPPER_KN) && !g.upper_only;
-}
-// workgroups of a direct launch over tm x tn tiles
-__host__ __device__ inline unsigned direct_grid(const GemmArgs& g, int64_t tm, int64_t tn) {
-    if (column_deal(g, tn)) return (unsigned)(XCDS * cdiv(tn, XCDS) * tm);
-    return (unsigned)(tm >= XCDS ? XCDS * cdiv(tm, XCDS) * tn : tm * tn);
+// workgroups of a direct launch over tm x tn tiles (tile_order::gemm_tile
+// without sub-blocks)
+inline unsigned direct_grid(const GemmArgs& g, int64_t tm, int64_t tn) {
+    return (unsigned)tile_order::gemm_grid(tm, tn, g.tri, g.upper_only, false);
 }
 
 template <bool B_KMAJOR, int DNST, int BT>
@@ -278,35 +273,16 @@ __device__ __forceinline__ void direct_tile(const GemmArgs& g, int64_t tiles_m, 
     constexpr int WB = BT / 64;                          // 32 x 32 blocks per wave and dimension
     constexpr int DQ = BT * DBK * 4 / 1024 / 4;         // 1 KB copies per wave per operand per stage
     constexpr int SB = DSTAGE_BYTES<BT>;
-    // Tile order. blockIdx b runs on XCD b % 8. With at least 8 tile rows,
-    // XCD x takes whole rows in row-major order, its k-th being row 8k + x
-    // for even k and 8k + 7 - x for odd k: the tiles one XCD runs side by
-    // side share A panels (and B panels across its rows) in its own L2, and
-    // the zigzag keeps the triangular products (A upper, upper_only), whose
-    // work falls with the row, balanced over the XCDs. Products with a
-    // triangular B take whole columns instead (column_deal). Fewer rows:
-    // plain row-major order over all XCDs.
+    // Tile order (tile_order::gemm_tile, no sub-blocks). blockIdx b runs on
+    // XCD b % 8. With at least 8 tile rows, XCD x takes whole rows, its k-th
+    // being row 8k + x for even k and 8k + 7 - x for odd k: the tiles one
+    // XCD runs side by side share A panels (and B panels across its rows) in
+    // its own L2, and the zigzag keeps the triangular products (A upper,
+    // upper_only), whose work falls with the row, balanced over the XCDs.
+    // Products with a triangular B take whole columns the same way, deepest
+    // first. Fewer rows: plain row-major order over all XCDs.
     int64_t tm, tn;
-    if (column_deal(g, tiles_n)) {
-        const int64_t x = bid % XCDS, i = bid / XCDS, k = i / tiles_m;
-        tn = XCDS * k + ((k & 1) ? XCDS - 1 - x : x);
-        tm = i % tiles_m;
-        if (tn >= tiles_n) return;
-    } else if (tiles_m >= XCDS) {
-        const int64_t x = bid % XCDS, i = bid / XCDS, k = i / tiles_n;
-        tm = XCDS * k + ((k & 1) ? XCDS - 1 - x : x);
-        tn = i % tiles_n;
-        if (tm >= tiles_m) return;
-    } else {
-        if ((int64_t)bid >= tiles_m * tiles_n) return;
-        tm = bid / tiles_n;
-        tn = bid % tiles_n;
-    }
-    // B upper triangular [K][N]: a tile's depth grows with its column, so
-    // columns go in descending order and the deepest tiles start first (the
-    // last tiles to start are then the shortest)
-    if (g.tri == TRI_B_UPPER_KN) tn = tiles_n - 1 - tn;
-    if (g.upper_only && tm > tn) return;
+    if (!tile_order::gemm_tile(bid, tiles_m, tiles_n, g.tri, g.upper_only, false, tm, tn)) return;
     const int64_t m0 = tm * BT, n0 = tn * BT;
 
     int64_t kb = 0, ke = g.K;
