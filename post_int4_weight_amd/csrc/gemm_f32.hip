@@ -257,15 +257,15 @@ __device__ __forceinline__ void f32_wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// BT = 128 (4 waves of 64 x 64 = 2 x 2 MFMA blocks) or 64 (4 waves of one
-// 32 x 32 block each): the small tile quadruples the workgroups of the small
-// products deep in the U recursion, which otherwise run on a few CUs.
 // workgroups of a direct launch over tm x tn tiles (tile_order::gemm_tile
 // without sub-blocks)
 inline unsigned direct_grid(const GemmArgs& g, int64_t tm, int64_t tn) {
     return (unsigned)tile_order::gemm_grid(tm, tn, g.tri, g.upper_only, false);
 }
 
+// BT = 128 (4 waves of 64 x 64 = 2 x 2 MFMA blocks) or 64 (4 waves of one
+// 32 x 32 block each): the small tile quadruples the workgroups of the small
+// products deep in the U recursion, which otherwise run on a few CUs.
 template <bool B_KMAJOR, int DNST, int BT>
 __device__ __forceinline__ void direct_tile(const GemmArgs& g, int64_t tiles_m, int64_t tiles_n, unsigned bid) {
     static_assert(DNST >= 3, "the ring needs three stages");
