@@ -1265,20 +1265,32 @@ XtxPlan plan_xtx(int64_t n, int64_t rows) {
     p.bm = (n >= 2048) ? 256 : 128;
     p.T = (int)cdiv(n, p.bm);
     p.chunk = std::min<int64_t>(CHUNK_ROWS_MAX, cdiv(std::max<int64_t>(rows, 1), 64) * 64);
-    // Split the depth of a launch so that its tile jobs fill the CUs evenly:
-    // the busiest XCD runs its jobs in waves of 32 (one per CU) and sets the
-    // launch time. Take the smallest power of two whose jobs keep 90% of the
-    // slots busy (at most 16, each split at least SPLIT_ROWS_MIN rows deep).
-    const int64_t ntiles = (int64_t)p.T * (p.T + 1) / 2;
+    // Split the depth of a launch (s a power of two up to 16, each split at
+    // least SPLIT_ROWS_MIN rows deep) so that its tile jobs fill the CUs: the
+    // busiest XCD runs its jobs in waves of 32 (one per CU) and sets the
+    // launch time. Each job costs its 64-deep stages plus an epilogue that
+    // stores or adds a whole tile, and s > 1 adds a pass over s partial H, so
+    // s is the one with the smallest estimate
+    //   waves(s) * (stages(s) * t_stage + t_epilogue) + s * n^2 * 4 B / 5 TB/s
+    // with the stage and epilogue times measured on 256-wide tiles (1.45 and
+    // 48 us) and scaled by the tile area for 128-wide ones. Deeper jobs waste
+    // less on epilogues, more splits fill more CUs: the 4096-wide q_proj
+    // (32768 rows) takes 4 splits (0.75 ms per call against 0.99 ms with the
+    // 16 that a 90%-occupancy rule gave), the 8192-wide q/k/v 4, down_proj 1.
     const int nb = (int)cdiv(p.T, SB);
     int64_t per_xcd = 0;   // tiles of the busiest XCD in one launch without splitting
     for (int P = 0; P < nb; ++P)
         for (int Q = P; Q < nb; ++Q) per_xcd += cdiv(hessian_round_tiles(P, Q, p.T), NXCD);
-    auto busy = [&](int64_t s) {
-        return (double)(ntiles * s) / (double)(256 * cdiv(per_xcd * s, 256 / NXCD));
+    const double area = (double)p.bm * p.bm / (256.0 * 256.0);
+    auto estimate = [&](int64_t s) {
+        const double waves = (double)cdiv(per_xcd * s, 256 / NXCD);
+        const double stages = (double)p.chunk / (64.0 * (double)s);
+        const double reduce = s > 1 ? (double)s * (double)n * (double)n * 4.0 / 5.0e6 : 0.0;   // us at 5 TB/s
+        return waves * area * (stages * 1.45 + 48.0) + reduce;
     };
     int s = 1;
-    while (busy(s) < 0.9 && p.chunk / (2 * s) >= SPLIT_ROWS_MIN && s < 16) s *= 2;
+    for (int c = 2; c <= 16 && p.chunk / c >= SPLIT_ROWS_MIN; c *= 2)
+        if (estimate(c) < estimate(s)) s = c;
     p.nsplit = s;
     p.slab_rows = std::max<int64_t>(SLAB_ROWS, cdiv(cdiv(rows, MAX_SLABS), 64) * 64);
     p.nslab = (int)std::max<int64_t>(1, cdiv(rows, p.slab_rows));
